@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs for the W4A16 linear layer.
+
+This module only draws random numbers.  It holds none of the layer's
+arithmetic (no packing, no dequantization, no products), so the HIP path and
+the CPU oracle can both be fed from it without sharing any of the method.
+
+Distributions (the quantized LLaMA-7B linears of the PerfXLLM page, §2 and
+§3.1: int4 codes, one scale and one zero per 128 weights):
+
+* q: uniform integer codes in [0, 15], shape [M, K];
+* z: uniform integer codes in [0, 15], shape [M, K / 128];
+* s: uniform in [0.002, 0.02], drawn in float64 and rounded to fp16;
+* X: standard normal, drawn in float32 and rounded to fp16, shape [K, N].
+
+Seeds are numpy PCG64 streams keyed by (workload id, layer, projection,
+stream); weights use stream 0 and activations stream 1 + N, so one weight
+matrix serves a whole sweep over N with fresh activations per N.
+"""
+
+import numpy as np
+
+GROUP = 128
+
+# LLaMA-7B linear shapes (M = output rows, K = reduction length).  The page
+# fuses the three QKV products into one (§3.2), giving M = 3 * 4096.
+LLAMA7B_PROJ = (
+    ("qkv", 12288, 4096),
+    ("o_proj", 4096, 4096),
+    ("gate_up", 22016, 4096),
+    ("down", 4096, 11008),
+)
+
+# Named workloads.  ``wid`` is the seed key of each workload.
+WORKLOADS = {
+    "gemv_4096x4096": {"wid": 1, "shapes": [("w", 4096, 4096)], "N": [1]},
+    "llama7b_decode_linears": {"wid": 2, "shapes": list(LLAMA7B_PROJ), "N": [1]},
+    "small_n_12288x4096": {"wid": 3, "shapes": [("w", 12288, 4096)],
+                           "N": [1, 2, 4, 8, 16, 32]},
+    "large_n_12288x4096": {"wid": 4, "shapes": [("w", 12288, 4096)],
+                           "N": [64, 128, 256, 512, 1024, 2048, 4096]},
+    "llama7b_stack_32x4": {"wid": 5, "shapes": list(LLAMA7B_PROJ), "N": [1, 16],
+                           "layers": 32},
+}
+
+
+def weight_rng(wid, layer, proj):
+    return np.random.default_rng([wid, layer, proj, 0])
+
+
+def act_rng(wid, layer, proj, N):
+    return np.random.default_rng([wid, layer, proj, 1 + N])
+
+
+def weights(M, K, wid=0, layer=0, proj=0):
+    """(q uint8 [M, K], s float16 [M, K/128], z uint8 [M, K/128])."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    rng = weight_rng(wid, layer, proj)
+    G = K // GROUP
+    q = rng.integers(0, 16, (M, K), dtype=np.uint8)
+    z = rng.integers(0, 16, (M, G), dtype=np.uint8)
+    s = rng.uniform(0.002, 0.02, (M, G)).astype(np.float16)
+    return q, s, z
+
+
+def raw_q_words(M, K, wid=0, layer=0, proj=0):
+    """Uniform random uint32 words [M, K/8] for the weight codes.
+
+    Eight independent uniform 4-bit codes per word have the same law as a
+    uniform 32-bit word, so large stacks draw the packed words directly
+    instead of 8x as many bytes of codes.  Scales and zeros come from
+    ``scales_zeros`` with the same seed key.
+    """
+    rng = weight_rng(wid, layer, proj)
+    return rng.integers(0, 1 << 32, (M, K // 8), dtype=np.uint32)
+
+
+def scales_zeros(M, K, wid=0, layer=0, proj=0):
+    """(s float16 [M, K/128], z uint8 [M, K/128]) on their own stream."""
+    rng = np.random.default_rng([wid, layer, proj, 2])
+    G = K // GROUP
+    z = rng.integers(0, 16, (M, G), dtype=np.uint8)
+    s = rng.uniform(0.002, 0.02, (M, G)).astype(np.float16)
+    return s, z
+
+
+def activations(K, N, wid=0, layer=0, proj=0):
+    """X float16 [K, N], standard normal rounded to fp16."""
+    rng = act_rng(wid, layer, proj, N)
+    return rng.standard_normal((K, N), dtype=np.float32).astype(np.float16)
+
+
+def uniform_codes(shape, seed):
+    """Uniform integer codes in [0, 15] (generic helper for tests)."""
+    return np.random.default_rng(seed).integers(0, 16, shape, dtype=np.uint8)
+
+
+def fp16_weights(M, K, seed):
+    """Unquantized fp16 weights ~ N(0, 0.02^2), for the quantizer's tests."""
+    rng = np.random.default_rng([seed, 7])
+    return (0.02 * rng.standard_normal((M, K))).astype(np.float16)

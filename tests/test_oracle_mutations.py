@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in a copy of the oracle, on the CPU, and check
+that the pins in ``oracle_pins`` catch every one of them.
+
+Each mutation is a textual edit of the oracle's source; the mutated source is
+executed as a fresh module, and at least one pin must then fail.
+"""
+
+import inspect
+import types
+
+import pytest
+
+import oracle.w4a16 as ora
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "sign_of_zero": ("((qf - zf) * sf)", "((zf - qf) * sf)"),
+    "zero_not_subtracted": ("((qf - zf) * sf)", "((qf - 0 * zf) * sf)"),
+    "scale_not_applied": ("((qf - zf) * sf)", "((qf - zf) * (sf * 0 + 1))"),
+    "nibble_order_reversed": ("out[:, j::8] = (words >> np.uint32(4 * j))",
+                              "out[:, 7 - j::8] = (words >> np.uint32(4 * j))"),
+    "pack_high_nibble_first": ("words |= padded[:, j::8] << np.uint32(4 * j)",
+                               "words |= padded[:, j::8] << np.uint32(28 - 4 * j)"),
+    "group_of_zero_shifted": ("zf = z.astype(np.float64)[:, :, None]",
+                              "zf = np.roll(z.astype(np.float64), 1, axis=1)[:, :, None]"),
+    "group_of_scale_shifted": ("sf = s.astype(np.float64)[:, :, None]",
+                               "sf = np.roll(s.astype(np.float64), 1, axis=1)[:, :, None]"),
+    "scale_by_k_mod_g": ("qf = q.astype(np.float64).reshape(q.shape[0], G, GROUP)",
+                         "qf = q.astype(np.float64).reshape(q.shape[0], GROUP, G).transpose(0, 2, 1)"),
+    "last_group_dropped": ("return ((qf - zf) * sf).reshape(q.shape[0], K)",
+                           "return np.concatenate([((qf - zf) * sf)[:, :-1], 0 * qf[:, -1:]], 1).reshape(q.shape[0], K)"),
+    "x_reversed": ("        C[rows] = W @ Xf\n", "        C[rows] = W @ Xf[::-1]\n"),
+    "abs_bound_wrong": ("        A[rows] = np.abs(W) @ Xa\n", "        A[rows] = np.abs(W @ Xf)\n"),
+    "block_tail_lost": ("for r0 in range(0, M, step):", "for r0 in range(0, M - 1, step):"),
+    "rows_ignored": ("        qpk, zpk, s = qpk[rows], zpk[rows], s[rows]\n",
+                     "        qpk, zpk, s = qpk[rows], zpk[rows], s[::-1][rows]\n"),
+    "tolerance_loose": ("return 5e-3 * np.asarray(A, dtype=np.float64) + 1e-3",
+                        "return 5e-2 * np.asarray(A, dtype=np.float64) + 1e-3"),
+    "nan_passes": ("n_bad = int(np.count_nonzero(~(ratio <= 1.0)))",
+                   "n_bad = int(np.count_nonzero(ratio > 1.0) - np.count_nonzero(~finite))"),
+    "quantizer_floor": ("q = np.clip(np.rint(w / s32[:, :, None])", "q = np.clip(np.floor(w / s32[:, :, None])"),
+    "quantizer_zero_range": ("lo = np.minimum(w.min(axis=2), np.float32(0.0))", "lo = w.min(axis=2)"),
+    "quantizer_scale_16": ("s16 = (rng / np.float32(15.0))", "s16 = (rng / np.float32(16.0))"),
+    "group_size_64": ("GROUP = 128", "GROUP = 64"),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(ora)
+    assert src.count(old) == 1, "mutation anchor must occur once: %r" % old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_copy_passes():
+    mod = _mutant("GROUP = 128", "GROUP = 128")
+    for pin in ALL_PINS:
+        pin(mod)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, "no pin catches mutation %s" % name
