@@ -6,7 +6,7 @@ is the C-ABI library ``libw4a16.so`` (hand-written HIP kernels); the Python
 names below only marshal torch device tensors into its entry points.
 """
 
-__all__ = ["pack", "gemv", "gemm", "workspace_size", "quantize", "lib"]
+__all__ = ["pack", "gemv", "gemm", "workspace_size", "plan_default", "Plan", "Workspace", "lib"]
 
 
 def __getattr__(name):

@@ -1,0 +1,249 @@
+"""Python binding of ``libw4a16.so``: argument marshalling only.
+
+Every function takes torch tensors on the current HIP device, checks dtype,
+shape, device and contiguity, and forwards raw pointers and the current
+stream to the C ABI declared in ``include/w4a16.h``.  All arithmetic runs in
+the library's HIP kernels; there is no fallback path.  If the shared library
+is missing, loading fails with an error naming the build command.
+"""
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a16.h")
+
+GROUP = 128
+KERNEL_SKINNY = 1
+KERNEL_TILED = 2
+
+_lib = None
+_lock = threading.Lock()
+
+
+class W4A16Error(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status, message):
+        super().__init__("w4a16 status %d: %s" % (status, message))
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("ncol", ctypes.c_int32), ("rb", ctypes.c_int32),
+                ("wm", ctypes.c_int32), ("wk", ctypes.c_int32), ("bm", ctypes.c_int32),
+                ("bn", ctypes.c_int32), ("splitk", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
+
+    @classmethod
+    def make(cls, **kw):
+        p = cls()
+        for k, v in kw.items():
+            setattr(p, k, int(v))
+        return p
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle of libw4a16.so."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise ImportError("%s is not built; run `python -m gemm_w4a16_group_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        lib.w4a16_status_string.restype = ctypes.c_char_p
+        lib.w4a16_status_string.argtypes = [ctypes.c_int]
+        lib.w4a16_last_error.restype = ctypes.c_char_p
+        lib.w4a16_last_error.argtypes = []
+        lib.w4a16_version.restype = ctypes.c_int
+        lib.w4a16_version.argtypes = []
+        lib.w4a16_pack.restype = ctypes.c_int
+        lib.w4a16_pack.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+        lib.w4a16_gemv.restype = ctypes.c_int
+        lib.w4a16_gemv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
+        lib.w4a16_plan_default.restype = ctypes.c_int
+        lib.w4a16_plan_default.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        lib.w4a16_workspace_size_plan.restype = sz
+        lib.w4a16_workspace_size_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        lib.w4a16_gemm_workspace_size.restype = sz
+        lib.w4a16_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.w4a16_gemm.restype = ctypes.c_int
+        lib.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+        lib.w4a16_gemm_plan.restype = ctypes.c_int
+        lib.w4a16_gemm_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32,
+                                        ctypes.POINTER(Plan), vp, sz, vp]
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def lib():
+    return load_library()
+
+
+def header_functions():
+    """Names of the functions declared in include/w4a16.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().w4a16_last_error().decode(errors="replace")
+        raise W4A16Error(status, msg)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def pack(q=None, z=None):
+    """Pack uint8 codes on the GPU: q [M, K] -> uint32 [M, K/8] (as int32),
+    z [M, K/128] -> uint32 [M, ceil(G/8)] (as int32).  Returns (qpk, zpk)."""
+    if q is None and z is None:
+        raise ValueError("nothing to pack")
+    ref = q if q is not None else z
+    M = ref.shape[0]
+    if q is not None:
+        _need(q, "q", torch.uint8)
+        K = q.shape[1]
+    else:
+        _need(z, "z", torch.uint8)
+        K = z.shape[1] * GROUP
+    G = K // GROUP
+    if z is not None:
+        _need(z, "z", torch.uint8, (M, G))
+    qpk = torch.empty((M, K // 8), dtype=torch.int32, device=ref.device) if q is not None else None
+    zpk = torch.empty((M, (G + 7) // 8), dtype=torch.int32, device=ref.device) if z is not None else None
+    _check(lib().w4a16_pack(_p(q), _p(z), M, K, GROUP, _p(qpk), _p(zpk), _stream()))
+    return qpk, zpk
+
+
+def _dims(qpk, s, zpk, x):
+    _need(qpk, "q_packed", torch.int32)
+    M, KW = qpk.shape
+    K = KW * 8
+    G = K // GROUP
+    _need(s, "scales", torch.float16, (M, G))
+    _need(zpk, "z_packed", torch.int32, (M, (G + 7) // 8))
+    if x.dim() == 1:
+        _need(x, "x", torch.float16, (K,))
+        N = 1
+    else:
+        _need(x, "x", torch.float16)
+        if x.shape[0] != K:
+            raise ValueError("x must be [K=%d, N], got %s" % (K, tuple(x.shape)))
+        N = x.shape[1]
+    return M, N, K
+
+
+def plan_default(M, N, K):
+    p = Plan()
+    _check(lib().w4a16_plan_default(M, N, K, GROUP, ctypes.byref(p)))
+    return p
+
+
+def workspace_size(M, N, K, plan=None):
+    if plan is None:
+        return int(lib().w4a16_gemm_workspace_size(M, N, K, GROUP))
+    return int(lib().w4a16_workspace_size_plan(M, N, K, GROUP, ctypes.byref(plan)))
+
+
+class Workspace:
+    """A zero-filled device buffer for split reductions (kept zeroed by the
+    kernels between calls).  One per stream."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace_for(device):
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device)
+    return ws
+
+
+def gemv(qpk, s, zpk, x, out=None):
+    """c[M] = Wdeq . x[K] (N = 1, no workspace)."""
+    M, N, K = _dims(qpk, s, zpk, x)
+    if N != 1:
+        raise ValueError("gemv wants one activation column")
+    if out is None:
+        out = torch.empty((M,), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", torch.float16)
+        if out.numel() != M:
+            raise ValueError("out must hold M=%d values" % M)
+    _check(lib().w4a16_gemv(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, K, GROUP, _stream()))
+    return out
+
+
+def gemm(qpk, s, zpk, x, out=None, plan=None, workspace=None):
+    """c[M, N] = Wdeq[M, K] . x[K, N] with the library's dispatch (or a plan)."""
+    M, N, K = _dims(qpk, s, zpk, x)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", torch.float16)
+        if out.numel() != M * N:
+            raise ValueError("out must hold M*N=%d values" % (M * N))
+    need = workspace_size(M, N, K, plan)
+    if plan is not None and need == 0:
+        # invalid plans report size 0; let the library say why
+        need = 0
+    ws = None
+    if need:
+        if workspace is None:
+            ws = _workspace_for(x.device).get(need)
+        else:
+            ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if plan is None:
+        _check(lib().w4a16_gemm(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP,
+                                _p(ws), ws_bytes, _stream()))
+    else:
+        _check(lib().w4a16_gemm_plan(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP,
+                                     ctypes.byref(plan), _p(ws), ws_bytes, _stream()))
+    return out

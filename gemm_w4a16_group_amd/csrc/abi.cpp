@@ -1,0 +1,343 @@
+// C ABI of the W4A16 linear layer: argument checks, plan choice, dispatch.
+//
+// Every check happens on the host before any HIP call.  The two regimes of
+// PerfXLLM §3.3 item 1 (few tokens: bandwidth-bound; many tokens:
+// compute-bound, each with its own tiling) map to the skinny and the tiled
+// kernel; w4a16_plan_default() picks one from the shape.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/w4a16.h"
+#include "launch.hpp"
+
+using namespace w4a16;
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int kGroupSize = 128;
+constexpr size_t kMaxDynLds = 65536;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
+// Split reductions keep one arrival counter per output tile at a fixed place,
+// the first 64 KB of the workspace, so partial sums of one call can never
+// land on the counters of another call with a different shape.
+constexpr int64_t kCounterSlots = 16384;
+constexpr size_t kCounterBytes = kCounterSlots * 4;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int ok() {
+    g_err.clear();
+    return W4A16_OK;
+}
+
+bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_dims(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+    if (group_size != kGroupSize)
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size must be 128, got %d", (int)group_size);
+    if (M < 1 || N < 1 || K < kGroupSize)
+        return fail(W4A16_ERR_INVALID_ARG, "need M >= 1, N >= 1, K >= 128 (M=%lld N=%lld K=%lld)",
+                    (long long)M, (long long)N, (long long)K);
+    if (K % kGroupSize)
+        return fail(W4A16_ERR_INVALID_ARG, "K=%lld is not a multiple of 128", (long long)K);
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return fail(W4A16_ERR_INVALID_ARG, "M, N and K must each be below 2^31");
+    // byte sizes used below: M*K/2, M*N*4*splitk; keep them far from overflow
+    if ((double)M * (double)K > 9.0e18 || (double)M * (double)N * 4.0 * 64.0 > 9.0e18)
+        return fail(W4A16_ERR_INVALID_ARG, "problem too large");
+    return W4A16_OK;
+}
+
+int64_t groups_of(int64_t K) { return K / kGroupSize; }
+int64_t zwords_of(int64_t K) { return (groups_of(K) + 7) / 8; }
+
+int next_pow2_ncol(int64_t N) {
+    int c = 1;
+    while (c < N) c *= 2;
+    return c;
+}
+
+GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.G = (int32_t)groups_of(K);
+    a.ZW = (int32_t)zwords_of(K);
+    return a;
+}
+
+SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
+TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk}; }
+
+// Default plan (tuned on MI355X for the LLaMA-7B shapes; any valid plan is
+// correct, this one only decides speed).
+w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
+    w4a16_plan p;
+    memset(&p, 0, sizeof(p));
+    const int64_t G = groups_of(K);
+    if (N <= 64) {
+        p.kernel = W4A16_KERNEL_SKINNY;
+        p.ncol = next_pow2_ncol(N);
+        p.rb = p.ncol >= 8 ? 2 : 1;
+        p.wm = p.ncol <= 2 ? 1 : (p.ncol <= 8 ? 2 : 4);
+        // activations staged per workgroup: at most 32 KB (64 KB for N = 1)
+        const int64_t lds_cap = p.ncol == 1 ? 65536 - 64 : 32768;
+        const int64_t bmw0 = 16LL * p.rb * p.wm;
+        int64_t gmax = lds_cap / (256 * (int64_t)p.ncol + 3 * bmw0);
+        if (gmax < 1) gmax = 1;
+        int64_t splitk = (G + gmax - 1) / gmax;
+        if (splitk < 1) splitk = 1;
+        p.splitk = (int32_t)splitk;
+        const int64_t bmw = 16LL * p.rb * p.wm;
+        const int64_t tiles = (M + bmw - 1) / bmw;
+        // aim for about 3072 waves in flight, 1..8 waves per workgroup
+        int wk = 1;
+        const int64_t ngs = (G + splitk - 1) / splitk;
+        while (wk * 2 * p.wm <= 8 && tiles * splitk * p.wm * wk < 3072 && ngs >= 2 * wk * 2) wk *= 2;
+        p.wk = wk;
+        p.bm = p.bn = 0;
+        // a split needs one counter per row tile; past that, the tiled
+        // kernel (no split) takes the shape
+        if (p.splitk == 1 || tiles <= kCounterSlots) return p;
+    }
+    {
+        p.kernel = W4A16_KERNEL_TILED;
+        const int cand[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
+        int pick = 3;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = ((M + cand[i][0] - 1) / cand[i][0]) * ((N + cand[i][1] - 1) / cand[i][1]);
+            if (t >= 512) {
+                pick = i;
+                break;
+            }
+        }
+        p.bm = cand[pick][0];
+        p.bn = cand[pick][1];
+        const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+        int64_t splitk = 1;
+        const int64_t nst = K / 64;
+        while (t * splitk < 512 && splitk * 2 <= nst / 4 && t <= kCounterSlots) splitk *= 2;
+        p.splitk = (int32_t)splitk;
+        p.ncol = 0;
+        p.rb = p.wm = p.wk = 0;
+    }
+    return p;
+}
+
+int64_t tiles_of(const GemmArgs& a, const w4a16_plan& p) {
+    return p.kernel == W4A16_KERNEL_SKINNY ? skinny_row_tiles(a, skinny_of(p))
+                                           : tiled_tiles(a, tiled_of(p));
+}
+
+// Workspace layout: [counters: 64 KB][fp32 partials: splitk * M * N].
+size_t workspace_bytes_for(const GemmArgs& a, const w4a16_plan& p) {
+    if (p.splitk <= 1) return 0;
+    return kCounterBytes + (size_t)p.splitk * (size_t)a.M * (size_t)a.N * 4;
+}
+
+int check_plan(const GemmArgs& a, const w4a16_plan& p) {
+    if (p.splitk > 65535)
+        return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d above the grid limit 65535", p.splitk);
+    if (p.kernel == W4A16_KERNEL_SKINNY) {
+        const SkinnyShape s = skinny_of(p);
+        if (!skinny_supported(s))
+            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan invalid (ncol=%d rb=%d wm=%d wk=%d splitk=%d)",
+                        p.ncol, p.rb, p.wm, p.wk, p.splitk);
+        if (p.ncol < a.N)
+            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan stages %d columns but N=%lld", p.ncol,
+                        (long long)a.N);
+        if (p.splitk > a.G)
+            return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d exceeds the %d groups of a row", p.splitk, a.G);
+        if (p.splitk > 1 && tiles_of(a, p) > kCounterSlots)
+            return fail(W4A16_ERR_UNSUPPORTED, "split plans support at most %lld row tiles",
+                        (long long)kCounterSlots);
+        const size_t lds = skinny_lds_bytes(a, s);
+        if (lds == 0 || lds > kMaxDynLds)
+            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan needs %zu bytes of LDS (max %zu)", lds,
+                        kMaxDynLds);
+        return W4A16_OK;
+    }
+    if (p.kernel == W4A16_KERNEL_TILED) {
+        const TiledShape t = tiled_of(p);
+        if (!tiled_supported(t))
+            return fail(W4A16_ERR_UNSUPPORTED, "tiled plan invalid (bm=%d bn=%d splitk=%d)", p.bm, p.bn,
+                        p.splitk);
+        if (p.splitk > 1 && tiles_of(a, p) > kCounterSlots)
+            return fail(W4A16_ERR_UNSUPPORTED, "split plans support at most %lld tiles",
+                        (long long)kCounterSlots);
+        if (p.splitk > a.K / 64)
+            return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d exceeds the %lld k-stages", p.splitk,
+                        (long long)(a.K / 64));
+        return W4A16_OK;
+    }
+    return fail(W4A16_ERR_UNSUPPORTED, "unknown kernel id %d", p.kernel);
+}
+
+int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, void* c,
+             int64_t M, int64_t N, int64_t K, int32_t group_size, const w4a16_plan* plan_in,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    if (!qpk || !scales || !zpk || !x || !c)
+        return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(qpk) || !aligned16(scales) || !aligned16(zpk) || !aligned16(x) || !aligned16(c))
+        return fail(W4A16_ERR_MISALIGNED, "every data pointer must be 16-byte aligned");
+    const int64_t G = groups_of(K);
+    const size_t nq = (size_t)M * (size_t)(K / 8) * 4, ns = (size_t)M * G * 2,
+                 nz = (size_t)M * zwords_of(K) * 4, nx = (size_t)K * N * 2, nc = (size_t)M * N * 2;
+    if (overlaps(c, nc, qpk, nq) || overlaps(c, nc, scales, ns) || overlaps(c, nc, zpk, nz) ||
+        overlaps(c, nc, x, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "output overlaps an input");
+
+    GemmArgs a = make_args(M, N, K);
+    const w4a16_plan p = plan_in ? *plan_in : default_plan(M, N, K);
+    st = check_plan(a, p);
+    if (st) return st;
+    const size_t need = workspace_bytes_for(a, p);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+        if (overlaps(workspace, need, c, nc) || overlaps(workspace, need, qpk, nq) ||
+            overlaps(workspace, need, scales, ns) || overlaps(workspace, need, zpk, nz) ||
+            overlaps(workspace, need, x, nx))
+            return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
+        a.counters = static_cast<uint32_t*>(workspace);
+        a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    }
+    a.qpk = qpk;
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.zpk = zpk;
+    a.x = static_cast<const uint16_t*>(x);
+    a.c = static_cast<uint16_t*>(c);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = p.kernel == W4A16_KERNEL_SKINNY ? launch_skinny(a, skinny_of(p), s)
+                                                   : launch_tiled(a, tiled_of(p), s);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument";
+        case W4A16_ERR_UNSUPPORTED: return "unsupported";
+        case W4A16_ERR_MISALIGNED: return "misaligned pointer";
+        case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4A16_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* w4a16_last_error(void) { return g_err.c_str(); }
+
+int w4a16_version(void) { return 100; }
+
+int w4a16_pack(const uint8_t* q, const uint8_t* z, int64_t M, int64_t K, int32_t group_size,
+               uint32_t* q_packed, uint32_t* z_packed, void* stream) {
+    int st = check_dims(M, 1, K, group_size);
+    if (st) return st;
+    if (!q && !z) return fail(W4A16_ERR_INVALID_ARG, "nothing to pack: q and z are both NULL");
+    if ((q && !q_packed) || (z && !z_packed))
+        return fail(W4A16_ERR_INVALID_ARG, "a code array is given without its packed output");
+    if ((q && !aligned16(q)) || (z && !aligned16(z)) || (q_packed && !aligned16(q_packed)) ||
+        (z_packed && !aligned16(z_packed)))
+        return fail(W4A16_ERR_MISALIGNED, "every pointer must be 16-byte aligned");
+    const int64_t G = groups_of(K);
+    const size_t nq = (size_t)M * K, nqp = (size_t)M * (K / 8) * 4, nzc = (size_t)M * G,
+                 nzp = (size_t)M * zwords_of(K) * 4;
+    if (q && (overlaps(q_packed, nqp, q, nq) || (z && overlaps(q_packed, nqp, z, nzc)) ||
+              (z && overlaps(q_packed, nqp, z_packed, nzp))))
+        return fail(W4A16_ERR_INVALID_ARG, "packed weights overlap another buffer");
+    if (z && (overlaps(z_packed, nzp, z, nzc) || (q && overlaps(z_packed, nzp, q, nq))))
+        return fail(W4A16_ERR_INVALID_ARG, "packed zeros overlap another buffer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (q) {
+        hipError_t e = launch_pack_rows(q, q_packed, M, K, s);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+    }
+    if (z) {
+        hipError_t e = launch_pack_rows(z, z_packed, M, G, s);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size, w4a16_plan* plan) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    if (!plan) return fail(W4A16_ERR_INVALID_ARG, "plan is NULL");
+    *plan = default_plan(M, N, K);
+    return ok();
+}
+
+size_t w4a16_workspace_size_plan(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                 const w4a16_plan* plan) {
+    if (check_dims(M, N, K, group_size) || !plan) return 0;
+    GemmArgs a = make_args(M, N, K);
+    if (check_plan(a, *plan)) return 0;
+    return workspace_bytes_for(a, *plan);
+}
+
+size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+    if (check_dims(M, N, K, group_size)) return 0;
+    GemmArgs a = make_args(M, N, K);
+    return workspace_bytes_for(a, default_plan(M, N, K));
+}
+
+int w4a16_gemv(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x,
+               void* c, int64_t M, int64_t K, int32_t group_size, void* stream) {
+    int st = check_dims(M, 1, K, group_size);
+    if (st) return st;
+    w4a16_plan p = default_plan(M, 1, K);
+    GemmArgs a = make_args(M, 1, K);
+    if (workspace_bytes_for(a, p) != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld needs a split reduction; use w4a16_gemm", (long long)K);
+    return run_gemm(q_packed, scales, z_packed, x, c, M, 1, K, group_size, &p, nullptr, 0, stream);
+}
+
+int w4a16_gemm(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x,
+               void* c, int64_t M, int64_t N, int64_t K, int32_t group_size, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, nullptr, workspace,
+                    workspace_bytes, stream);
+}
+
+int w4a16_gemm_plan(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed,
+                    const void* x, void* c, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                    const w4a16_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan) return fail(W4A16_ERR_INVALID_ARG, "plan is NULL");
+    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, plan, workspace,
+                    workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal launchers of the W4A16 kernels (called by the C ABI in abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+struct GemmArgs {
+    const uint32_t* qpk;      // [M, K/8]
+    const uint16_t* scales;   // fp16 bits [M, G]
+    const uint32_t* zpk;      // [M, ZW]
+    const uint16_t* x;        // fp16 bits [K, N]
+    uint16_t* c;              // fp16 bits [M, N]
+    float* part;              // fp32 [splitk, M, N] partial sums (splitk > 1)
+    uint32_t* counters;       // one arrival counter per output tile (splitk > 1)
+    int64_t M, N, K;
+    int32_t G, ZW;
+};
+
+struct SkinnyShape {
+    int ncol, rb, wm, wk, splitk;
+};
+
+struct TiledShape {
+    int bm, bn, splitk;
+};
+
+// Bytes of dynamic LDS the skinny kernel needs (0 if the shape is invalid).
+size_t skinny_lds_bytes(const GemmArgs& a, const SkinnyShape& s);
+bool skinny_supported(const SkinnyShape& s);
+int64_t skinny_row_tiles(const GemmArgs& a, const SkinnyShape& s);
+hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream);
+
+bool tiled_supported(const TiledShape& t);
+int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t);
+hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream);
+
+hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,
+                            hipStream_t stream);
+
+}  // namespace w4a16

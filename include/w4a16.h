@@ -1,0 +1,157 @@
+/*
+ * w4a16.h - C ABI of the W4A16 group-quantized linear layer for MI355X (gfx950).
+ *
+ * The operation (PerfXLLM page on Snapdragon 8 Gen2, 3532n.com/d/2322131):
+ *   - §3.3 item 1 defines the product C[m, n] = A[m, k] . B[k, n]; here A is the
+ *     dequantized weight matrix Wdeq[M, K] and B the activations X[K, N];
+ *   - §3.3 item 2 is the same product with n = 1 (the decode-time GEMV);
+ *   - §3.1 stores the weights as int4 codes with one scale and one zero per
+ *     group of 128 weights.
+ * Read here as
+ *   C[m, n] = sum_k (q[m, k] - z[m, k / 128]) * s[m, k / 128] * X[k, n]
+ * with fp16 s, X and C, 4-bit q and z, and fp32 accumulation.
+ *
+ * Layouts (all row-major, all device memory unless stated):
+ *   q_packed  uint32 [M, K / 8]          nibble j (bits 4j..4j+3) of word w of
+ *                                        row m holds q[m, 8w + j]
+ *   scales    fp16   [M, G], G = K / 128
+ *   z_packed  uint32 [M, ceil(G / 8)]    nibble j of word w of row m holds
+ *                                        z[m, 8w + j]; padding nibbles are 0
+ *   x         fp16   [K, N]              (N contiguous)
+ *   c         fp16   [M, N]              (N contiguous), written, never read
+ *
+ * Conventions shared by every entry point:
+ *   - functions never throw, abort or allocate device memory, and never
+ *     synchronize; work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and its results are valid once that stream has reached it;
+ *   - every argument is checked on the host before any HIP call; on failure
+ *     the function returns a non-zero w4a16_status, writes nothing and
+ *     records a message readable with w4a16_last_error();
+ *   - the caller owns every buffer; no pointer is kept after the call.
+ *   - base pointers must be 16-byte aligned (W4A16_ERR_MISALIGNED otherwise).
+ *   - the output must not overlap any input (W4A16_ERR_INVALID_ARG).
+ *   - NaN and Inf in scales or x propagate and are not checked.
+ *   - results are bitwise repeatable for a given plan and shape: split
+ *     reductions are summed in a fixed order, no float atomics are used.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = 1,   /* bad size, null pointer, overlap, overflow  */
+    W4A16_ERR_UNSUPPORTED = 2,   /* group_size other than 128, or a bad plan   */
+    W4A16_ERR_MISALIGNED = 3,    /* a base pointer not 16-byte aligned         */
+    W4A16_ERR_WORKSPACE = 4,     /* workspace missing or too small             */
+    W4A16_ERR_HIP = 5            /* a HIP call failed (no device, launch error) */
+} w4a16_status;
+
+/* Static text for a status code ("unknown status" for other values). */
+const char *w4a16_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char *w4a16_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int w4a16_version(void);
+
+/*
+ * Pack 4-bit codes into the storage format above (PerfXLLM §3.1 storage).
+ *   q : uint8 [M, K] weight codes, or NULL to pack zeros only
+ *   z : uint8 [M, K / group_size] zero codes, or NULL to pack weights only
+ * Only the low nibble of each code is used.  q_packed / z_packed receive
+ * [M, K / 8] and [M, ceil(G / 8)] words; a NULL output is allowed only with
+ * a NULL input.  Requires M >= 1, K >= 128, K % 128 == 0, group_size == 128.
+ * Bit-exact: the result is a pure function of the inputs.
+ */
+int w4a16_pack(const uint8_t *q, const uint8_t *z, int64_t M, int64_t K,
+               int32_t group_size, uint32_t *q_packed, uint32_t *z_packed,
+               void *stream);
+
+/*
+ * The GEMV of PerfXLLM §3.3 item 2: N = 1, c[M] = Wdeq . x[K].
+ * Needs no workspace.  Same layouts and checks as w4a16_gemm with N = 1.
+ */
+int w4a16_gemv(const uint32_t *q_packed, const void *scales,
+               const uint32_t *z_packed, const void *x, void *c, int64_t M,
+               int64_t K, int32_t group_size, void *stream);
+
+/*
+ * Execution plan: which kernel runs and how the work is split.  Filled by
+ * w4a16_plan_default(); tests and tuning may pass their own.
+ *   kernel : W4A16_KERNEL_SKINNY (N <= 64: weights streamed once, products on
+ *            16x16x32 fp16 MFMA, activations staged in LDS) or
+ *            W4A16_KERNEL_TILED (tiles of BM x BN outputs, 32x32x16 fp16 MFMA).
+ *   skinny : ncol = staged activation columns (1, 2, 4, 8, 16, 32 or 64,
+ *            >= N); rb = 16-row blocks per wave (1 or 2); wm / wk = waves per
+ *            workgroup along rows / along K (wm * wk <= 8); splitk = number of
+ *            workgroups sharing one row tile along K (>= 1).
+ *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256});
+ *            splitk as above.
+ * splitk > 1 needs a workspace (w4a16_workspace_size).
+ */
+enum { W4A16_KERNEL_SKINNY = 1, W4A16_KERNEL_TILED = 2 };
+
+typedef struct {
+    int32_t kernel;
+    int32_t ncol;
+    int32_t rb;
+    int32_t wm;
+    int32_t wk;
+    int32_t bm;
+    int32_t bn;
+    int32_t splitk;
+} w4a16_plan;
+
+/* The plan w4a16_gemm uses for this shape.  Returns a status. */
+int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                       w4a16_plan *plan);
+
+/* Workspace bytes a plan needs (0 when splitk == 1); 0 on invalid input. */
+size_t w4a16_workspace_size_plan(int64_t M, int64_t N, int64_t K,
+                                 int32_t group_size, const w4a16_plan *plan);
+
+/* Workspace bytes w4a16_gemm needs with its default plan. */
+size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
+                                 int32_t group_size);
+
+/*
+ * The GEMM of PerfXLLM §3.3 item 1: c[M, N] = Wdeq[M, K] . x[K, N], with the
+ * two regimes of that item (few tokens: bandwidth-bound skinny kernel; many
+ * tokens: compute-bound tiled kernel) chosen by w4a16_plan_default().
+ * Requires M >= 1, N >= 1, K >= 128, K % 128 == 0, group_size == 128.
+ *
+ * workspace: device memory of at least w4a16_gemm_workspace_size() bytes,
+ * 16-byte aligned, or NULL when that size is 0.  Its first 64 KB hold one
+ * arrival counter per output tile (split plans allow at most 16384 tiles);
+ * fp32 partial sums follow.  Before its first use the caller must fill at
+ * least the first 64 KB with zeros; every call leaves the counters at zero
+ * again, so one zero-fill serves all later calls of any shape.  Calls that
+ * share a workspace must not run concurrently (one workspace per stream).
+ */
+int w4a16_gemm(const uint32_t *q_packed, const void *scales,
+               const uint32_t *z_packed, const void *x, void *c, int64_t M,
+               int64_t N, int64_t K, int32_t group_size, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* w4a16_gemm with an explicit plan (W4A16_ERR_UNSUPPORTED for a plan the
+ * shape cannot use). */
+int w4a16_gemm_plan(const uint32_t *q_packed, const void *scales,
+                    const uint32_t *z_packed, const void *x, void *c,
+                    int64_t M, int64_t N, int64_t K, int32_t group_size,
+                    const w4a16_plan *plan, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

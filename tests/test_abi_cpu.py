@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects every bad argument with the documented status before
+any HIP call.  Pointers here are fake and never dereferenced: each call
+fails validation first.  The one test that lets a valid call reach HIP runs
+only where no GPU is visible, so that the launch itself fails."""
+
+import ctypes
+
+import pytest
+
+from gemm_w4a16_group_amd import binding as B
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4, 5
+
+# fake, distinct, 16-byte aligned addresses (never dereferenced)
+Q, S, Z, X, C, WS = (ctypes.c_void_p(0x100000 * (i + 1)) for i in range(6))
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def _gpu_count():
+    try:
+        import torch
+        return torch.cuda.device_count()
+    except Exception:
+        return 0
+
+
+def test_exports_every_header_function(lib):
+    names = B.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.w4a16_status_string(OK) == b"ok"
+    for st in (INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIPERR):
+        assert lib.w4a16_status_string(st) not in (b"ok", b"unknown status")
+    assert lib.w4a16_status_string(99) == b"unknown status"
+    assert lib.w4a16_version() >= 100
+
+
+def _gemm(lib, M=64, N=1, K=256, g=128, q=Q, s=S, z=Z, x=X, c=C, ws=NULL, wsb=0):
+    return lib.w4a16_gemm(q, s, z, x, c, M, N, K, g, ws, wsb, NULL)
+
+
+def test_gemm_dimension_checks(lib):
+    assert _gemm(lib, g=64) == UNSUPPORTED
+    assert b"group_size" in lib.w4a16_last_error()
+    assert _gemm(lib, M=0) == INVALID
+    assert _gemm(lib, N=0) == INVALID
+    assert _gemm(lib, K=0) == INVALID
+    assert _gemm(lib, K=200) == INVALID
+    assert _gemm(lib, K=64) == INVALID
+    assert _gemm(lib, M=1 << 31) == INVALID
+    assert _gemm(lib, N=-3) == INVALID
+
+
+def test_gemm_pointer_checks(lib):
+    assert _gemm(lib, q=NULL) == INVALID
+    assert _gemm(lib, c=NULL) == INVALID
+    assert _gemm(lib, x=ctypes.c_void_p(0x300008)) == MISALIGNED
+    assert _gemm(lib, s=ctypes.c_void_p(0x200002)) == MISALIGNED
+    # output overlapping an input
+    assert _gemm(lib, c=ctypes.c_void_p(0x100000 + 64)) == INVALID
+    assert b"overlap" in lib.w4a16_last_error()
+
+
+def test_workspace_checks(lib):
+    M, N, K = 4096, 16, 4096
+    need = lib.w4a16_gemm_workspace_size(M, N, K, 128)
+    assert need > 0
+    big = 0x10000000
+    q, s, z, x, c = (ctypes.c_void_p(big * (i + 1)) for i in range(5))
+    ws = ctypes.c_void_p(big * 7)
+    assert _gemm(lib, M=M, N=N, K=K, q=q, s=s, z=z, x=x, c=c) == WORKSPACE
+    assert _gemm(lib, M=M, N=N, K=K, q=q, s=s, z=z, x=x, c=c, ws=ws, wsb=need - 1) == WORKSPACE
+    assert _gemm(lib, M=M, N=N, K=K, q=q, s=s, z=z, x=x, c=c,
+                 ws=ctypes.c_void_p(big * 7 + 4), wsb=need) == MISALIGNED
+    assert _gemm(lib, M=M, N=N, K=K, q=q, s=s, z=z, x=x, c=c, ws=c, wsb=need) == INVALID
+
+
+def test_plan_checks(lib):
+    p = B.Plan()
+    assert lib.w4a16_plan_default(12288, 1, 4096, 128, ctypes.byref(p)) == OK
+    assert p.kernel == B.KERNEL_SKINNY and p.ncol == 1 and p.splitk == 1
+    assert lib.w4a16_plan_default(12288, 4096, 4096, 128, ctypes.byref(p)) == OK
+    assert p.kernel == B.KERNEL_TILED
+    assert lib.w4a16_plan_default(12288, 1, 4096, 128, None) == INVALID
+
+    def gp(**kw):
+        pl = B.Plan.make(**kw)
+        return lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, kw.pop("N", 4), 1024, 128,
+                                   ctypes.byref(pl), NULL, 0, NULL)
+    assert gp(kernel=7, splitk=1) == UNSUPPORTED
+    assert gp(kernel=1, ncol=2, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol < N
+    assert gp(kernel=1, ncol=3, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol not a power of 2
+    assert gp(kernel=1, ncol=4, rb=3, wm=1, wk=1, splitk=1) == UNSUPPORTED
+    assert gp(kernel=1, ncol=4, rb=1, wm=4, wk=4, splitk=1) == UNSUPPORTED   # 16 waves
+    assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=9) == UNSUPPORTED   # > 8 groups
+    assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=2) == WORKSPACE
+    assert gp(kernel=2, bm=64, bn=64, splitk=1) == UNSUPPORTED
+    assert gp(kernel=2, bm=128, bn=64, splitk=17) == UNSUPPORTED            # > 16 stages
+    assert lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, 4, 1024, 128, None, NULL, 0, NULL) == INVALID
+    bad = B.Plan.make(kernel=2, bm=64, bn=64, splitk=1)
+    assert lib.w4a16_workspace_size_plan(64, 4, 1024, 128, ctypes.byref(bad)) == 0
+
+
+def test_default_plans_are_valid(lib):
+    shapes = [(4096, 4096), (12288, 4096), (22016, 4096), (4096, 11008), (1, 128), (17, 384),
+              (5, 32768)]
+    for (M, K) in shapes:
+        for N in (1, 2, 3, 4, 8, 16, 17, 32, 33, 64, 65, 128, 256, 1000, 4096):
+            p = B.Plan()
+            assert lib.w4a16_plan_default(M, N, K, 128, ctypes.byref(p)) == OK
+            ws = lib.w4a16_workspace_size_plan(M, N, K, 128, ctypes.byref(p))
+            assert ws == lib.w4a16_gemm_workspace_size(M, N, K, 128)
+            assert (ws == 0) == (p.splitk == 1), (M, N, K, p.as_dict())
+            # a valid plan passes every check: with fake pointers the call
+            # then fails only on the workspace (if any), never on the plan
+            far = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]
+            st = lib.w4a16_gemm_plan(*far, M, N, K, 128, ctypes.byref(p), NULL, 0, NULL) \
+                if ws else None
+            if ws:
+                assert st == WORKSPACE, (M, N, K, p.as_dict(), lib.w4a16_last_error())
+
+
+def test_gemv_checks(lib):
+    assert lib.w4a16_gemv(Q, S, Z, X, C, 64, 256, 32, NULL) == UNSUPPORTED
+    assert lib.w4a16_gemv(Q, S, Z, NULL, C, 64, 256, 128, NULL) == INVALID
+    assert lib.w4a16_gemv(Q, S, Z, X, ctypes.c_void_p(0x500004), 64, 256, 128, NULL) == MISALIGNED
+
+
+def test_pack_checks(lib):
+    P1, P2 = ctypes.c_void_p(0x700000), ctypes.c_void_p(0x800000)
+    assert lib.w4a16_pack(NULL, NULL, 4, 256, 128, P1, P2, NULL) == INVALID
+    assert lib.w4a16_pack(Q, NULL, 4, 256, 128, NULL, NULL, NULL) == INVALID
+    assert lib.w4a16_pack(Q, Z, 4, 256, 64, P1, P2, NULL) == UNSUPPORTED
+    assert lib.w4a16_pack(Q, Z, 4, 200, 128, P1, P2, NULL) == INVALID
+    assert lib.w4a16_pack(ctypes.c_void_p(0x100001), NULL, 4, 256, 128, P1, NULL, NULL) == MISALIGNED
+    assert lib.w4a16_pack(Q, NULL, 4, 256, 128, Q, NULL, NULL) == INVALID   # output overlaps input
+
+
+@pytest.mark.skipif(_gpu_count() != 0, reason="needs a machine with no GPU: the launch must fail")
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    st = _gemm(lib)
+    assert st == HIPERR
+    assert len(lib.w4a16_last_error()) > 0

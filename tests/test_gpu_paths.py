@@ -1,0 +1,128 @@
+"""Every kernel variant against the oracle on small, ragged shapes: several
+tiles, tails in M and N, every activation staging width, every split.
+Element-by-element, with the rule |C - C_ref| <= 5e-3 * sum|W X| + 1e-3."""
+
+import numpy as np
+import pytest
+
+from gemm_w4a16_group_amd import binding as B
+from gemm_w4a16_group_amd import inputs
+from gpu_util import Problem, assert_parity, log, run
+
+pytestmark = pytest.mark.gpu
+
+_probs = {}
+
+
+def prob(M, K):
+    key = (M, K)
+    if key not in _probs:
+        _probs[key] = Problem(M, K, seed=len(_probs))
+    return _probs[key]
+
+
+def X_for(K, N, seed=0):
+    return inputs.activations(K, N, wid=200 + seed, layer=K, proj=N)
+
+
+SKINNY = [
+    # (M, K, N, ncol, rb, wm, wk, splitk)
+    (1, 128, 1, 1, 1, 1, 1, 1),
+    (17, 384, 1, 1, 1, 1, 2, 1),
+    (63, 1152, 1, 1, 2, 1, 4, 1),
+    (200, 1152, 1, 1, 1, 2, 4, 1),
+    (200, 1152, 1, 1, 2, 2, 2, 3),
+    (130, 4096, 1, 1, 1, 1, 8, 2),
+    (33, 11008, 1, 1, 1, 1, 8, 1),
+    (40, 384, 2, 2, 1, 1, 1, 1),
+    (40, 384, 3, 4, 1, 1, 2, 1),
+    (77, 1152, 4, 4, 2, 2, 1, 2),
+    (77, 1152, 5, 8, 1, 2, 2, 1),
+    (96, 1152, 8, 8, 2, 2, 2, 3),
+    (96, 1152, 13, 16, 1, 4, 2, 1),
+    (130, 1152, 16, 16, 2, 4, 1, 2),
+    (130, 1152, 17, 32, 1, 2, 2, 2),
+    (64, 1152, 31, 32, 2, 4, 2, 2),
+    (64, 1152, 32, 32, 2, 1, 8, 3),
+    (50, 640, 33, 64, 1, 2, 2, 2),
+    (50, 640, 64, 64, 2, 2, 1, 5),
+    (300, 384, 1, 2, 1, 1, 1, 1),      # ncol wider than N
+    (300, 384, 2, 16, 1, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", SKINNY, ids=lambda c: "M%d_K%d_N%d_c%d_rb%d_wm%d_wk%d_s%d" % c)
+def test_skinny_plan(case):
+    M, K, N, ncol, rb, wm, wk, splitk = case
+    log("skinny %s" % (case,))
+    p = prob(M, K)
+    X = X_for(K, N)
+    plan = B.Plan.make(kernel=B.KERNEL_SKINNY, ncol=ncol, rb=rb, wm=wm, wk=wk, splitk=splitk)
+    C = run(p, X, plan=plan)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, str(case))
+
+
+TILED = [
+    # (M, K, N, bm, bn, splitk)
+    (1, 128, 65, 128, 64, 1),
+    (100, 384, 65, 128, 64, 1),
+    (300, 384, 100, 128, 128, 1),
+    (300, 1152, 128, 128, 64, 2),
+    (300, 1152, 200, 256, 64, 3),
+    (257, 384, 264, 256, 128, 1),
+    (257, 1152, 264, 128, 256, 2),
+    (520, 640, 520, 256, 256, 1),
+    (520, 640, 256, 256, 256, 4),
+    (64, 256, 77, 128, 128, 1),       # N not a multiple of 8
+    (129, 384, 130, 256, 128, 2),
+    (40, 128, 3, 128, 64, 1),         # small N on the tiled kernel
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d" % c)
+def test_tiled_plan(case):
+    M, K, N, bm, bn, splitk = case
+    log("tiled %s" % (case,))
+    p = prob(M, K)
+    X = X_for(K, N)
+    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk)
+    C = run(p, X, plan=plan)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, str(case))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 16, 17, 33, 64, 65, 100, 128, 256])
+def test_default_dispatch(N):
+    M, K = 333, 1152
+    log("default N=%d" % N)
+    p = prob(M, K)
+    X = X_for(K, N, seed=1)
+    C = run(p, X)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, "default N=%d" % N)
+
+
+def test_gemv_entry_point():
+    import torch
+    from gpu_util import dev
+    M, K = 515, 4096
+    p = prob(M, K)
+    X = X_for(K, 1, seed=2)
+    out = B.gemv(p.qpk, p.s_d, p.zpk, dev(X[:, 0]))
+    torch.cuda.synchronize()
+    C_ref, A_ref = p.reference(X)
+    assert_parity(out.cpu().numpy()[:, None], C_ref, A_ref, "gemv")
+
+
+def test_repeatable_bitwise():
+    """Same plan and inputs give identical bits, split reductions included."""
+    M, K = 300, 1152
+    p = prob(M, K)
+    for N, plan in [(1, None), (16, None), (200, None),
+                    (8, B.Plan.make(kernel=1, ncol=8, rb=2, wm=2, wk=2, splitk=3)),
+                    (264, B.Plan.make(kernel=2, bm=128, bn=256, splitk=2))]:
+        X = X_for(K, N, seed=3)
+        a = run(p, X, plan=plan)
+        b = run(p, X, plan=plan)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), N
