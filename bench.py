@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 group-quantized linear layer on one MI355X.
+
+Default workload (the headline): the decode GEMV C[12288] = Wdeq[12288, 4096]
+. x[4096] with int4 weights, fp16 scales, 4-bit zeros, g = 128.  One step is
+one call of the layer on one batch (here one activation column), reading
+the whole packed matrix once.  The weights are replicated into R device
+copies (R * 26 MB > 1 GB, four times the 256 MB last-level cache) and the
+steps cycle through them, so every call streams its weights from HBM.  The
+R calls are captured once in a HIP graph and replayed; HIP events on the
+launch stream bracket the timed steps.
+
+Printed (one JSON line): GB/s of algorithmic bytes (packed weights, scales,
+zeros, x and C, each counted once) per call, the roofline fraction against
+8 TB/s, the large-N GEMM figure at N = 4096 (TFLOP/s against the 2.5 PF/s
+fp16 dense peak) as a second measurement, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+GROUP = 128
+
+
+def alg_bytes(M, K, N):
+    """Algorithmic bytes of one call: each array moved once."""
+    G = K // GROUP
+    return M * K // 2 + 2 * M * G + M * G // 2 + 2 * K * N + 2 * M * N
+
+
+def alg_flops(M, K, N):
+    return 2 * M * K * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--copies", type=int, default=40, help="weight copies cycled through (cold cache)")
+    ap.add_argument("--workload", default="gemv_12288x4096",
+                    choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
+                             "large_n", "stack"])
+    ap.add_argument("--gemm-iters", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
+    return ap.parse_args()
+
+
+class Layer:
+    """One weight matrix packed on the device, replicated ``copies`` times."""
+
+    def __init__(self, M, K, wid, proj=0, layer=0, copies=1):
+        import torch
+        from gemm_w4a16_group_amd import binding as B
+        from gemm_w4a16_group_amd import inputs
+        self.M, self.K = M, K
+        q, s, z = inputs.weights(M, K, wid=wid, layer=layer, proj=proj)
+        self.host = (q, s, z)
+        qpk, zpk = B.pack(torch.from_numpy(q).cuda(), torch.from_numpy(z).cuda())
+        sd = torch.from_numpy(s).cuda()
+        self.copies = [(qpk, sd, zpk)]
+        for _ in range(copies - 1):
+            self.copies.append((qpk.clone(), sd.clone(), zpk.clone()))
+        torch.cuda.synchronize()
+
+
+def capture(calls, stream):
+    """Capture a list of zero-argument launch closures into one HIP graph."""
+    import torch
+    with torch.cuda.stream(stream):
+        for c in calls:          # eager run first: allocations, lazy loading
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, replays, stream):
+    """Milliseconds of ``replays`` graph replays, HIP events on ``stream``."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(replays):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def gemv_rotation(M, K, wid, copies, steps, warmup, plan=None):
+    """Time `steps` calls cycling over `copies` weight copies.  Returns
+    (ms per call, plan dict, graph calls per replay)."""
+    import torch
+    from gemm_w4a16_group_amd import binding as B
+    from gemm_w4a16_group_amd import inputs
+    lay = Layer(M, K, wid, copies=copies)
+    x = torch.from_numpy(inputs.activations(K, 1, wid=wid)).cuda()
+    outs = [torch.empty((M, 1), dtype=torch.float16, device="cuda") for _ in range(copies)]
+    calls = [(lambda c=c, o=o: B.gemm(c[0], c[1], c[2], x, out=o, plan=plan))
+             for c, o in zip(lay.copies, outs)]
+    stream = torch.cuda.Stream()
+    g = capture(calls, stream)
+    reps_w = max(1, warmup // copies)
+    reps = max(1, steps // copies)
+    time_graph(g, reps_w, stream)
+    ms = time_graph(g, reps, stream)
+    return ms / (reps * copies), B.plan_default(M, 1, K).as_dict(), reps * copies, lay, x, outs[0]
+
+
+def gemm_large(M, K, N, wid, iters):
+    """Eager timing of the large-N GEMM (each call is hundreds of us)."""
+    import torch
+    from gemm_w4a16_group_amd import binding as B
+    from gemm_w4a16_group_amd import inputs
+    lay = Layer(M, K, wid)
+    qpk, sd, zpk = lay.copies[0]
+    x = torch.from_numpy(inputs.activations(K, N, wid=wid)).cuda()
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            B.gemm(qpk, sd, zpk, x, out=out)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(iters):
+            B.gemm(qpk, sd, zpk, x, out=out)
+        end.record(stream)
+    end.synchronize()
+    ms = start.elapsed_time(end) / iters
+    return ms, B.plan_default(M, N, K).as_dict()
+
+
+def cpu_baseline(M, K, seconds, wid):
+    """The oracle on the same workload, repeated for about ``seconds``."""
+    import numpy as np
+    import oracle.w4a16 as ora
+    from gemm_w4a16_group_amd import inputs
+    q, s, z = inputs.weights(M, K, wid=wid)
+    X = inputs.activations(K, 1, wid=wid)
+    qpk, zpk = ora.pack(q, z)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(d.get("internal_api"), d.get("num_threads")) for d in threadpool_info()
+                if d.get("user_api") == "blas"]
+    except Exception:
+        blas = []
+    threads = max([t for _, t in blas] or [1])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        ora.reference(qpk, s, zpk, X)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= 2) or n >= 200:
+            break
+    per = el / n
+    return {
+        "value": alg_bytes(M, K, 1) / per / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "%d full calls of the fp64 numpy oracle on %dx%d, N=1 (%.2f s each; dequant "
+                  "single-threaded numpy, product %s with %d threads, %d host cores visible)"
+                  % (n, M, K, per, "/".join(str(b[0]) for b in blas) or "BLAS", threads,
+                     len(os.sched_getaffinity(0))),
+    }
+
+
+def headline(args):
+    import torch
+    M, K, N = 12288, 4096, 1
+    wid = 3
+    ms, plan, steps, *_ = gemv_rotation(M, K, wid, args.copies, args.steps, args.warmup)
+    b = alg_bytes(M, K, N)
+    gbs = b / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "W4A16 GEMV HBM GB/s (12288x4096,N=1) + GEMM TFLOPS at N=4096; % roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "gemv_12288x4096_n1", "M": M, "K": K, "N": N, "group_size": GROUP,
+                   "weights": "int4 packed, fp16 scale + 4-bit zero per 128",
+                   "cold_cache_copies": args.copies, "timing": "HIP graph of %d calls, HIP events"
+                   % args.copies, "plan": plan},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "skinny_kernel<1,1>", "bytes_per_launch": b,
+                     "us_per_launch": round(ms * 1e3, 3)},
+    }
+    if not args.no_gemm:
+        Ng = 4096
+        gms, gplan = gemm_large(12288, 4096, Ng, 4, args.gemm_iters)
+        tf = alg_flops(12288, 4096, Ng) / (gms * 1e-3) / 1e12
+        line["secondary"] = {
+            "metric": "W4A16 GEMM TFLOP/s (12288x4096, N=4096)", "value": round(tf, 2),
+            "unit": "TFLOP/s", "ms_per_call": round(gms, 4), "plan": gplan,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "tiled_kernel<256,256>", "flops_per_launch": alg_flops(12288, 4096, Ng)}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(M, K, args.cpu_seconds, wid)
+    print(json.dumps(line), flush=True)
+
+
+def extra(args):
+    """Other workloads, one JSON line each (for tuning and the design notes)."""
+    import torch
+    from gemm_w4a16_group_amd import binding as B
+    from gemm_w4a16_group_amd import inputs
+    rows = []
+    if args.workload == "gemv_4096x4096":
+        ms, plan, steps, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup)
+        rows.append(("gemv_4096x4096", 4096, 4096, 1, ms, plan))
+    elif args.workload == "decode_linears":
+        for proj, (name, M, K) in enumerate(inputs.LLAMA7B_PROJ):
+            cps = max(8, int(1.1e9 // alg_bytes(M, K, 1)))
+            ms, plan, *_ = gemv_rotation(M, K, 2, cps, args.steps, args.warmup)
+            rows.append((name, M, K, 1, ms, plan))
+    elif args.workload in ("small_n", "large_n"):
+        Ns = [1, 2, 4, 8, 16, 32] if args.workload == "small_n" else [64, 128, 256, 512, 1024, 2048, 4096]
+        wid = 3 if args.workload == "small_n" else 4
+        M, K = 12288, 4096
+        cps = 40
+        lay = Layer(M, K, wid, copies=cps)
+        for N in Ns:
+            x = torch.from_numpy(inputs.activations(K, N, wid=wid)).cuda()
+            outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(cps)]
+            ncalls = cps if N <= 256 else 4
+            calls = [(lambda c=c, o=o: B.gemm(c[0], c[1], c[2], x, out=o))
+                     for c, o in zip(lay.copies[:ncalls], outs[:ncalls])]
+            stream = torch.cuda.Stream()
+            g = capture(calls, stream)
+            reps = max(2, (args.steps // ncalls) if N <= 256 else 5)
+            time_graph(g, 2, stream)
+            ms = time_graph(g, reps, stream) / (reps * ncalls)
+            rows.append(("12288x4096", M, K, N, ms, B.plan_default(M, N, K).as_dict()))
+    elif args.workload == "stack":
+        for N in (1, 16):
+            mats = []
+            for layer in range(32):
+                for proj, (name, M, K) in enumerate(inputs.LLAMA7B_PROJ):
+                    w = torch.from_numpy(inputs.raw_q_words(M, K, wid=5, layer=layer, proj=proj).view("int32")).cuda()
+                    s, z = inputs.scales_zeros(M, K, wid=5, layer=layer, proj=proj)
+                    _, zd = B.pack(None, torch.from_numpy(z).cuda())
+                    x = torch.from_numpy(inputs.activations(K, N, wid=5, layer=layer, proj=proj)).cuda()
+                    o = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                    mats.append((w, torch.from_numpy(s).cuda(), zd, x, o))
+            calls = [(lambda m=m: B.gemm(m[0], m[1], m[2], m[3], out=m[4])) for m in mats]
+            stream = torch.cuda.Stream()
+            g = capture(calls, stream)
+            time_graph(g, 3, stream)
+            reps = 20
+            ms = time_graph(g, reps, stream) / reps
+            wbytes = sum(alg_bytes(M, K, N) for (_, M, K) in inputs.LLAMA7B_PROJ) * 32
+            print(json.dumps({"workload": "llama7b_stack_32x4", "N": N, "ms_per_step": round(ms, 4),
+                              "steps_per_s": round(1e3 / ms, 1),
+                              "GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+            del mats, calls, g
+            torch.cuda.empty_cache()
+        return
+    for (name, M, K, N, ms, plan) in rows:
+        b = alg_bytes(M, K, N)
+        f = alg_flops(M, K, N)
+        print(json.dumps({"workload": name, "M": M, "K": K, "N": N, "us": round(ms * 1e3, 3),
+                          "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2),
+                          "frac_mfma": round(f / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                          "plan": plan}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from gemm_w4a16_group_amd import binding
+    binding.load_library()
+    if args.workload == "gemv_12288x4096":
+        headline(args)
+    else:
+        extra(args)
+
+
+if __name__ == "__main__":
+    main()
