@@ -22,7 +22,6 @@ namespace {
 thread_local std::string g_err;
 
 constexpr int kGroupSize = 128;
-constexpr size_t kMaxDynLds = 65536;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
 // Split reductions keep one arrival counter per output tile at a fixed place,
 // the first 64 KB of the workspace, so partial sums of one call can never
@@ -72,11 +71,7 @@ int check_dims(int64_t M, int64_t N, int64_t K, int32_t group_size) {
 int64_t groups_of(int64_t K) { return K / kGroupSize; }
 int64_t zwords_of(int64_t K) { return (groups_of(K) + 7) / 8; }
 
-int next_pow2_ncol(int64_t N) {
-    int c = 1;
-    while (c < N) c *= 2;
-    return c;
-}
+bool skinny_columns(int64_t N) { return (N >= 1 && N <= 8) || N == 16 || N == 32; }
 
 GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
     GemmArgs a;
@@ -92,36 +87,44 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
 TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk}; }
 
+int check_plan(const GemmArgs& a, const w4a16_plan& p);
+
 // Default plan (tuned on MI355X for the LLaMA-7B shapes; any valid plan is
 // correct, this one only decides speed).
+//
+// Skinny kernel (N <= 8, or N in {16, 32, 64}): one 16-row block per wave
+// (several waves along M share the staged activations when N grows), about
+// eight groups per wave along K so that all of a wave's weight loads are in
+// flight at once, and a split across workgroups only when the staged
+// activations would not fit in LDS.
 w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
     w4a16_plan p;
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
-    if (N <= 64) {
+    const GemmArgs a = make_args(M, N, K);
+    if (skinny_columns(N)) {
         p.kernel = W4A16_KERNEL_SKINNY;
-        p.ncol = next_pow2_ncol(N);
-        p.rb = p.ncol >= 8 ? 2 : 1;
-        p.wm = p.ncol <= 2 ? 1 : (p.ncol <= 8 ? 2 : 4);
-        // activations staged per workgroup: at most 32 KB (64 KB for N = 1)
-        const int64_t lds_cap = p.ncol == 1 ? 65536 - 64 : 32768;
-        const int64_t bmw0 = 16LL * p.rb * p.wm;
-        int64_t gmax = lds_cap / (256 * (int64_t)p.ncol + 3 * bmw0);
-        if (gmax < 1) gmax = 1;
-        int64_t splitk = (G + gmax - 1) / gmax;
-        if (splitk < 1) splitk = 1;
-        p.splitk = (int32_t)splitk;
-        const int64_t bmw = 16LL * p.rb * p.wm;
-        const int64_t tiles = (M + bmw - 1) / bmw;
-        // aim for about 3072 waves in flight, 1..8 waves per workgroup
-        int wk = 1;
-        const int64_t ngs = (G + splitk - 1) / splitk;
-        while (wk * 2 * p.wm <= 8 && tiles * splitk * p.wm * wk < 3072 && ngs >= 2 * wk * 2) wk *= 2;
-        p.wk = wk;
-        p.bm = p.bn = 0;
-        // a split needs one counter per row tile; past that, the tiled
-        // kernel (no split) takes the shape
-        if (p.splitk == 1 || tiles <= kCounterSlots) return p;
+        p.ncol = (int32_t)N;
+        p.rb = 1;
+        p.wm = N <= 8 ? 1 : 4;
+        const int64_t rows = 16LL * p.rb * p.wm;
+        const int64_t tiles = (M + rows - 1) / rows;
+        for (int64_t splitk = 1; splitk <= G; ++splitk) {
+            const int64_t ngs = (G + splitk - 1) / splitk;
+            int64_t wk = (ngs + 4) / 8;
+            if (wk < 1) wk = 1;
+            while (wk * p.wm > 16) wk /= 2;
+            // small grids: more waves along K (at least two groups each)
+            while (wk * 2 * p.wm <= 16 && tiles * splitk * p.wm * wk < 2048 && ngs >= 4 * wk) wk *= 2;
+            p.wk = (int32_t)wk;
+            p.splitk = (int32_t)splitk;
+            if (splitk > 1 && tiles > kCounterSlots) break;
+            const std::string saved = g_err;
+            const int st = check_plan(a, p);
+            g_err = saved;
+            if (st == W4A16_OK) return p;
+        }
+        memset(&p, 0, sizeof(p));
     }
     {
         p.kernel = W4A16_KERNEL_TILED;
@@ -166,18 +169,16 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p) {
         if (!skinny_supported(s))
             return fail(W4A16_ERR_UNSUPPORTED, "skinny plan invalid (ncol=%d rb=%d wm=%d wk=%d splitk=%d)",
                         p.ncol, p.rb, p.wm, p.wk, p.splitk);
-        if (p.ncol < a.N)
-            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan stages %d columns but N=%lld", p.ncol,
+        if (p.ncol != a.N)
+            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan is built for %d columns but N=%lld", p.ncol,
                         (long long)a.N);
         if (p.splitk > a.G)
             return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d exceeds the %d groups of a row", p.splitk, a.G);
         if (p.splitk > 1 && tiles_of(a, p) > kCounterSlots)
             return fail(W4A16_ERR_UNSUPPORTED, "split plans support at most %lld row tiles",
                         (long long)kCounterSlots);
-        const size_t lds = skinny_lds_bytes(a, s);
-        if (lds == 0 || lds > kMaxDynLds)
-            return fail(W4A16_ERR_UNSUPPORTED, "skinny plan needs %zu bytes of LDS (max %zu)", lds,
-                        kMaxDynLds);
+        const char* why = skinny_check(a, s);
+        if (why) return fail(W4A16_ERR_UNSUPPORTED, "skinny plan: %s", why);
         return W4A16_OK;
     }
     if (p.kernel == W4A16_KERNEL_TILED) {

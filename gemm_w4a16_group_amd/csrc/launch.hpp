@@ -26,9 +26,9 @@ struct TiledShape {
     int bm, bn, splitk;
 };
 
-// Bytes of dynamic LDS the skinny kernel needs (0 if the shape is invalid).
-size_t skinny_lds_bytes(const GemmArgs& a, const SkinnyShape& s);
 bool skinny_supported(const SkinnyShape& s);
+// nullptr if the skinny kernel can run this shape and plan, else the reason.
+const char* skinny_check(const GemmArgs& a, const SkinnyShape& s);
 int64_t skinny_row_tiles(const GemmArgs& a, const SkinnyShape& s);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream);
 

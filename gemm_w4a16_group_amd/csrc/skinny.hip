@@ -1,21 +1,33 @@
 // Skinny W4A16 kernel: few activation columns (N <= 64), the bandwidth-bound
-// regime of PerfXLLM §3.3 (item 1 for few tokens, item 2 for one token).
+// regime of the PerfXLLM page on Snapdragon 8 Gen2, §3.3 (item 1 for few
+// tokens, item 2 for one token).
 //
-// Every packed weight word is read from HBM exactly once, with 16-byte loads:
-// lane (r, kb) of a wave reads words 4kb .. 4kb+3 of one 128-weight group of
-// row r, so one load per lane brings in a whole group of 16 rows.  Each word
-// is dequantized in registers to eight exact fp16 (q - z) values, which form
-// the A operand of a 16x16x32 fp16 MFMA; the activations, staged once per
-// workgroup in LDS in the matching order, form the B operand.  The four MFMAs
-// of a group accumulate in fp32 and the group's scale is applied once to that
-// fp32 partial (PerfXLLM §3.3 item 2 keeps scale and zero in shared memory:
-// both are staged in LDS per workgroup).
+// Every packed weight word is read from HBM exactly once, with 16-byte
+// loads: lane (r, kb) of a wave reads words 4kb .. 4kb+3 of one 128-weight
+// group of row r, so one load per lane brings in a whole group of 16 rows.
+// The B operand of a 16x16x32 fp16 MFMA is made from each word with two
+// masks and a shift and nothing else: a nibble q at bits 0-3 of a half is
+// the fp16 subnormal q * 2^-24, a nibble at bits 4-7 is 16 q * 2^-24 (the
+// matrix cores take subnormal inputs exactly).  The A operand is a 16-token
+// block of the activations (tokens x k), staged per wave in LDS in the
+// matching k order, with the k positions of the bits-4-7 nibbles divided by
+// 16.  So one group's MFMAs give T = 2^-24 * sum_k q x exactly rounded in
+// fp32, the group sums S = sum_k x come from the same staged activations
+// (an MFMA with a constant operand), and the group adds
+//     s * (q - z) . x = (s * 2^24) * T - (s * z) * S
+// to the fp32 accumulator.  The product is C^T, so a lane's four
+// accumulators are four tokens of the very row it loaded, and its scale and
+// zero are per lane.  Scale and zero are staged in LDS, as §3.3 item 2 does.
 //
-// Work split (PerfXLLM §3.3 item 2 tiles both dimensions of the weight
-// matrix): a workgroup owns 16 * rb * wm rows; its wk waves along K each take
-// a contiguous run of groups and are summed through LDS; `splitk`
-// workgroups may share one row tile, their fp32 partials summed in a fixed
-// order by the last one to arrive.
+// Work split (§3.3 item 2 tiles both dimensions of the weight matrix): a
+// workgroup owns 16 * rb * wm rows and a run of groups; its wk waves along K
+// each take a contiguous part of that run and are summed through LDS;
+// `splitk` workgroups may share one row tile, their fp32 partials summed in
+// a fixed order by the last one to arrive.
+//
+// Latency: all small loads (scales, zeros, activations) are issued before
+// the weight loads, so that staging them never waits for the weight stream;
+// up to PF groups of weights per wave are in flight at any time.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -23,333 +35,549 @@ namespace w4a16 {
 
 namespace {
 
-struct SkinnyLds {
-    int ngs_max;    // groups per workgroup (upper bound)
-    int bmw;        // rows per workgroup
-    size_t x_off, s_off, z_off, flag_off, red_bytes, total;
-};
+constexpr int kMaxThreads = 1024;
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+// One group pair of one wave's 16 rows (16 x 128 B), rows 8..15 placed one
+// half bank-row later so that both the load-order writes and the MFMA-order
+// reads touch all 64 banks.
+constexpr int kPairBytes = 2304;
 
-template <int NCOL>
-__host__ __device__ inline SkinnyLds skinny_layout(int G, int splitk, int rb, int wm, int wk) {
-    constexpr int NB = NCOL >= 16 ? NCOL / 16 : 1;
-    SkinnyLds L;
-    L.ngs_max = (G + splitk - 1) / splitk;
-    L.bmw = 16 * rb * wm;
-    L.x_off = 0;
-    size_t xb = (size_t)L.ngs_max * 16 * NCOL * 16;
-    L.s_off = xb;
-    size_t sb = (size_t)L.ngs_max * L.bmw * 2;
-    L.z_off = L.s_off + ((sb + 15) & ~(size_t)15);
-    size_t zb = (size_t)L.ngs_max * L.bmw;
-    L.flag_off = L.z_off + ((zb + 15) & ~(size_t)15);
-    size_t main_bytes = L.flag_off + 16;
-    L.red_bytes = (size_t)(wk > 1 ? wk - 1 : 0) * wm * rb * NB * 4 * 64 * 4;
-    L.total = main_bytes > L.red_bytes + 16 ? main_bytes : L.red_bytes + 16;
-    // the arrival flag must not alias the reduction buffer
-    if (L.flag_off < L.red_bytes) {
-        L.flag_off = (L.red_bytes + 15) & ~(size_t)15;
-        L.total = L.flag_off + 16;
-        if (L.total < main_bytes) L.total = main_bytes;
-    }
-    return L;
+// Activation columns the kernel is built for: any N <= 8, or 16 or 32.
+__host__ __device__ constexpr bool ncol_ok(int n) {
+    return (n >= 1 && n <= 8) || n == 16 || n == 32;
 }
 
-template <int NCOL, int RB>
-__global__ void __launch_bounds__(512) skinny_kernel(GemmArgs a, int wm, int wk, int splitk) {
-    constexpr int NB = NCOL >= 16 ? NCOL / 16 : 1;
-    constexpr int PF = 8 / RB;                 // groups prefetched per wave
+// Activation blocks (and scale slots) a lane stages per load: a wave of 64
+// lanes stages PF groups = 16 PF octets of NB8 column-octets each, and four
+// groups of scales per load.
+__host__ __device__ constexpr int skinny_staging_loads(int NT, int PF) {
+    const int v = (PF * (NT <= 8 ? 1 : NT / 8) + 3) / 4;
+    return v > 0 ? v : 1;
+}
+// Largest PF per column count: staged activation registers F * min(NT, 8) * 4
+// stay within 64 VGPRs and weight buffers within 64.
+__host__ __device__ constexpr int skinny_max_pf(int NT) {
+    return NT <= 4 ? 16 : NT <= 8 ? 8 : NT == 16 ? 4 : 2;
+}
+
+// Everything the kernel needs about a plan, computed on the host so that the
+// kernel's prologue has no integer divisions ahead of its first loads.
+struct SkinnyParams {
+    int wm;                   // waves along M per workgroup
+    int wk;                   // waves along K per workgroup
+    int splitk;               // workgroups along K
+    int rows;                 // rows per workgroup
+    int sg_base, sg_rem;      // groups of split s: sg_base + (s < sg_rem)
+    int wq0, wr0, wq1, wr1;   // per-wave share of sg_base / sg_base + 1 groups
+    int ngw_max;              // groups per wave (upper bound)
+    int zwt_max;              // zero words per row a wave stages (upper bound)
+    int PF;                   // weight loads per lane = groups per wave (upper bound)
+    int F;                    // staging loads per lane (scales, activations)
+    uint32_t wave_bytes;      // one wave's LDS region
+    uint32_t s_off, z_off;    // scale / zero-word offsets inside it
+    uint32_t t_off;           // group-sum table offset inside it
+    uint32_t q_off;           // two weight-transpose buffers inside it
+    uint32_t flag_off, total; // arrival flag, total dynamic LDS
+};
+
+// Every wave stages, in its own LDS region, what its groups need: the
+// activations (NT columns; a 16-byte chunk holds eight k of one column,
+// chunks ordered [k-octet][column]), the scales ([group][row] halves) and
+// the zero words ([row][word]).  No wave waits for another before its main
+// loop.  Returns false for a shape the kernel cannot run.
+inline bool skinny_params(int NT, int G, int splitk, int rb, int wm, int wk, SkinnyParams& P) {
+    if (wm < 1 || wk < 1 || splitk < 1 || splitk > G) return false;
+    const int TB = (NT + 15) / 16;
+    P.wm = wm;
+    P.wk = wk;
+    P.splitk = splitk;
+    P.rows = 16 * rb * wm;
+    P.sg_base = G / splitk;
+    P.sg_rem = G % splitk;
+    P.wq0 = P.sg_base / wk;
+    P.wr0 = P.sg_base % wk;
+    P.wq1 = (P.sg_base + 1) / wk;
+    P.wr1 = (P.sg_base + 1) % wk;
+    const int ngs_max = P.sg_base + (P.sg_rem > 0);
+    P.ngw_max = (ngs_max + wk - 1) / wk;
+    P.zwt_max = (P.ngw_max + 7) / 8 + 1;
+    if (rb != 1 || P.zwt_max > 4) return false;
+    // PF = groups of weights a wave keeps in flight = all of its groups
+    P.PF = 2;
+    while (P.PF < P.ngw_max) P.PF *= 2;
+    P.F = skinny_staging_loads(NT, P.PF);
+    if (P.PF > skinny_max_pf(NT)) return false;
+    const size_t xb = (size_t)P.ngw_max * 16 * NT * 16;
+    const size_t sb = (size_t)P.PF * 16 * 2;
+    const size_t zb = (size_t)16 * 4 * 4;
+    const size_t tb = (size_t)P.PF * NT * 4;
+    P.s_off = (uint32_t)xb;
+    P.z_off = (uint32_t)(P.s_off + ((sb + 15) & ~(size_t)15));
+    P.t_off = (uint32_t)(P.z_off + ((zb + 15) & ~(size_t)15));
+    P.q_off = (uint32_t)(P.t_off + ((tb + 15) & ~(size_t)15));
+    const size_t wave_bytes = P.q_off + 2 * (size_t)kPairBytes;
+    size_t main_bytes = wave_bytes * wm * wk;
+    // partial sums of waves 1 .. wk-1, written after the staged data is dead
+    const size_t red = (size_t)(wk - 1) * wm * rb * TB * 4 * 64 * 4;
+    if (red > main_bytes) main_bytes = red;
+    if (main_bytes + 16 > kMaxLds) return false;
+    P.wave_bytes = (uint32_t)wave_bytes;
+    P.flag_off = (uint32_t)main_bytes;
+    P.total = (uint32_t)(main_bytes + 16);
+    return true;
+}
+
+__device__ __forceinline__ uint32_t load_u16(const uint16_t* p) { return (uint32_t)*p; }
+
+// The eight codes of one packed word as fp16 subnormals, in the k order
+// 0, 4, 1, 5, 2, 6, 3, 7: k 0, 4, 2, 6 carry q * 2^-24, k 1, 5, 3, 7 carry
+// 16 q * 2^-24 (the staged activations at those k are divided by 16).
+__device__ __forceinline__ half8 codes8(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    return __builtin_bit_cast(half8, u32x4{w & 0x000F000Fu, w & 0x00F000F0u,
+                                           w8 & 0x000F000Fu, w8 & 0x00F000F0u});
+}
+
+// Constant B operand that sums the staged activations of each A row over a
+// 32-k step: 1 at the k that were kept, 16 at the k that were divided by 16.
+__device__ __forceinline__ half8 unscale_ones() {
+    return __builtin_bit_cast(half8, u32x4{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u});
+}
+
+// Activation block: eight consecutive k (one octet) of T8 = min(NT, 8)
+// columns, loaded with 16-byte loads.  With N == NT every block is 16-byte
+// aligned: for NT <= 8 the block is 16 * NT contiguous bytes, otherwise
+// eight rows of 16 bytes.  It becomes T8 LDS chunks, one per column, each
+// holding the octet in the order 0, 4, 1, 5, 2, 6, 3, 7, with k 1, 5, 3, 7
+// divided by 16 (exact unless the quotient is subnormal: then rounded once).
+template <int NT>
+struct XStage {
+    static constexpr int T8 = NT < 8 ? NT : 8;
+    static constexpr int NB8 = NT <= 8 ? 1 : NT / 8;   // column octets
+    u32x4 v[T8];
+
+    __device__ __forceinline__ void load(const uint16_t* x, int64_t k0, int nb8) {
+        if (NT <= 8) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(x + k0 * NT);
+#pragma unroll
+            for (int t = 0; t < T8; ++t) v[t] = p[t];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                v[r] = *reinterpret_cast<const u32x4*>(x + (k0 + r) * NT + nb8 * 8);
+        }
+    }
+
+    // 32-bit word e2 of the block image, row-major [8 rows][T8 columns] halves
+    __device__ __forceinline__ uint32_t word(int e2) const {
+        const int t = e2 >> 2, j = e2 & 3;
+        return j == 0 ? v[t].x : j == 1 ? v[t].y : j == 2 ? v[t].z : v[t].w;
+    }
+
+    __device__ __forceinline__ void store(unsigned char* xs, int o, int nb8) const {
+        const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        if (T8 == 1) {
+            u32x4 r = permute_k8(v[0]);
+            r.y = as_u32(as_h2(r.y) * sixteenth);
+            r.w = as_u32(as_h2(r.w) * sixteenth);
+            *reinterpret_cast<u32x4*>(xs + (size_t)o * 16) = r;
+            return;
+        }
+#pragma unroll
+        for (int c = 0; c < T8; ++c) {
+            // pair (k r, k r+4) of column c: halves r*T8 + c and (r+4)*T8 + c
+            uint32_t pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e_lo = r * T8 + c, e_hi = (r + 4) * T8 + c;
+                const uint32_t wl = word(e_lo >> 1), wh = word(e_hi >> 1);
+                const uint32_t sel = ((e_lo & 1) ? 0x0302u : 0x0100u) | ((e_hi & 1) ? 0x07060000u : 0x05040000u);
+                pr[r] = __builtin_amdgcn_perm(wh, wl, sel);
+            }
+            pr[1] = as_u32(as_h2(pr[1]) * sixteenth);
+            pr[3] = as_u32(as_h2(pr[3]) * sixteenth);
+            const int col = nb8 * 8 + c;
+            *reinterpret_cast<u32x4*>(xs + ((size_t)o * NT + col) * 16) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+        }
+    }
+};
+
+// Group sums of the staged activations for one column (NT == 1): lane b
+// holds octet b of the wave's run; the sixteen octets of a group are sixteen
+// consecutive lanes.  Sums in fp32, written to stab[group].
+__device__ __forceinline__ void group_sums_one_column(const u32x4& v, int b, int nxb, float* stab) {
+    // k 1, 5, 3, 7 of the staged chunk are divided by 16; sum the raw values
+    const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
+    float t = 0.f;
+    t = __builtin_amdgcn_fdot2(as_h2(v.x), one, t, false);
+    t = __builtin_amdgcn_fdot2(as_h2(v.y), one, t, false);
+    t = __builtin_amdgcn_fdot2(as_h2(v.z), one, t, false);
+    t = __builtin_amdgcn_fdot2(as_h2(v.w), one, t, false);
+    if (b >= nxb) t = 0.f;
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 4);
+    t += __shfl_xor(t, 8);
+    if ((b & 15) == 0 && b < nxb) stab[b >> 4] = t;
+}
+
+template <int NT, int PF>
+__global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyParams P) {
+    constexpr int F = skinny_staging_loads(NT, PF); // activation loads per lane
+    constexpr int TB = (NT + 15) / 16;              // 16-column MFMA blocks
+    constexpr int NB8 = XStage<NT>::NB8;
+    // only the first min(NT, 4) accumulators of a block can hold a real
+    // column when NT < 4 (columns 4 kb + r with kb > 0 are past NT)
+    constexpr int RMAX = NT < 4 ? NT : 4;
+    constexpr int SZL = (PF + 3) / 4;               // scale loads per lane
+    constexpr int NP = PF / 2;                      // group pairs per wave
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-    const int M = (int)a.M, N = (int)a.N, G = a.G;
+    const int M = (int)a.M, G = a.G;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wave_m = wave % wm;
-    const int wave_k = wave / wm;
+    // wave-uniform (scalar) index, so that every per-wave loop bound and
+    // branch below is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_k = wave / P.wm;               // scalar division, once
+    const int wave_m = wave - wave_k * P.wm;
     const int nthreads = blockDim.x;
-    const int li = lane & 15;     // MFMA row (A) / column (B) within a 16-block
+    const int li = lane & 15;     // weight row (B column) / column of x (A row)
     const int kb = lane >> 4;     // which quarter of the 32-k MFMA step
 
-    const SkinnyLds L = skinny_layout<NCOL>(G, splitk, RB, wm, wk);
-    unsigned char* xs = smem + L.x_off;
-    uint16_t* ss = reinterpret_cast<uint16_t*>(smem + L.s_off);
-    uint8_t* zs = smem + L.z_off;
+    unsigned char* wbase = smem + (size_t)wave * P.wave_bytes;
+    unsigned char* xs = wbase;
+    uint16_t* ss = reinterpret_cast<uint16_t*>(wbase + P.s_off);
+    uint32_t* zsw = reinterpret_cast<uint32_t*>(wbase + P.z_off);
+    float* stab = reinterpret_cast<float*>(wbase + P.t_off);
+    unsigned char* qbuf = wbase + P.q_off;
 
-    const int bmw = L.bmw;
-    const int64_t tile_row0 = (int64_t)blockIdx.x * bmw;
+    const int64_t row0 = (int64_t)blockIdx.x * P.rows + wave_m * 16;
     const int sidx = blockIdx.y;
-    const int gs0 = (int)((int64_t)G * sidx / splitk);
-    const int gs1 = (int)((int64_t)G * (sidx + 1) / splitk);
-    const int ngs = gs1 - gs0;
-    const int gw0 = gs0 + ngs * wave_k / wk;
-    const int gw1 = gs0 + ngs * (wave_k + 1) / wk;
-    const int ng = gw1 - gw0;
+    const int gs0 = sidx * P.sg_base + (sidx < P.sg_rem ? sidx : P.sg_rem);
+    const bool big = sidx < P.sg_rem;
+    const int wq = big ? P.wq1 : P.wq0, wr = big ? P.wr1 : P.wr0;
+    const int gw0 = gs0 + wave_k * wq + (wave_k < wr ? wave_k : wr);
+    const int ng = wq + (wave_k < wr ? 1 : 0);
+    const int gw1 = gw0 + ng;
+    const int glast = ng > 0 ? gw1 - 1 : (gw0 < G ? gw0 : G - 1);   // clamp target
+    const int zw0 = gw0 >> 3;                     // first zero word of the wave
+    const int zwt = ng > 0 ? ((gw1 - 1) >> 3) - zw0 + 1 : 1;
+    int64_t lrow = row0 + li;                     // weight row of this lane (MFMA layout)
+    lrow = lrow < M ? lrow : M - 1;
 
-    // ---- issue the first weight loads before anything else
-    const int64_t KW = a.K / 8;
-    const uint32_t* wrow[RB];
+    // Loads are issued in the order their data is needed, and return in that
+    // order: activations, scales and zeros first, then every group's
+    // weights.  All loads are unconditional (indices clamped into range) so
+    // that they issue back to back; stores to LDS are masked.
+    // ---- 1. activations of the wave's groups: block b = lane + 64 j
+    const int nxb = ng * 16 * NB8;
+    XStage<NT> xst[F];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        int64_t row = tile_row0 + wave_m * 16 * RB + rb * 16 + li;
-        if (row > M - 1) row = M - 1;
-        wrow[rb] = a.qpk + row * KW + kb * 4;
+    for (int j = 0; j < F; ++j) {
+        int b = lane + j * 64;
+        b = b < nxb ? b : (nxb > 0 ? nxb - 1 : 0);
+        const int o = b / NB8, nb8 = b % NB8;     // NB8 is a power of two
+        int64_t k0 = (int64_t)gw0 * kGroup + (int64_t)o * 8;
+        k0 = k0 < a.K - 8 ? k0 : a.K - 8;
+        xst[j].load(a.x, k0, nb8);
     }
-    u32x4 buf[PF][RB];
+    // ---- 2. scales: lane (row li, group 4 j + kb); zero words: lane (row
+    // li, word kb)
+    uint32_t sreg[SZL];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        if (p < ng) {
+    for (int j = 0; j < SZL; ++j) {
+        const int gl = 4 * j + kb;
+        const int g = gw0 + gl < glast ? gw0 + gl : glast;
+        sreg[j] = load_u16(a.scales + lrow * G + g);
+    }
+    uint32_t zreg;
+    {
+        const int w = zw0 + kb < a.ZW ? zw0 + kb : a.ZW - 1;
+        zreg = a.zpk[lrow * a.ZW + w];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- 3. weights, two groups (128 bytes of a row) per load: lane
+    // (r = lane / 8, c = lane % 8) of half h reads 16 bytes c of the pair's
+    // 128 bytes of row 8 h + r.  Eight lanes cover a whole 128-byte line.
+    // Groups past the wave's run read a line every lane shares instead.
+    const int lr = lane >> 3, lc = lane & 7;
+    const u32x4* spare = reinterpret_cast<const u32x4*>(a.x);
+    u32x4 buf[NP][2];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                buf[p][rb] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(wrow[rb] + (int64_t)(gw0 + p) * 16));
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int64_t row = row0 + 8 * h + lr;
+            row = row < M ? row : M - 1;
+            const int gl = 2 * pp + (lc >> 2);
+            const u32x4* src = gl < ng ? reinterpret_cast<const u32x4*>(a.qpk + row * (a.K / 8) + (int64_t)(gw0 + gl) * 16 + (lc & 3) * 4)
+                                       : spare;
+            buf[pp][h] = __builtin_nontemporal_load(src);
         }
-    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage activations (in dequant order), scales and zeros in LDS
-    if (NCOL == 1) {
-        for (int f = threadIdx.x; f < ngs * 16; f += nthreads) {
-            const int gl = f >> 4, i = (f >> 2) & 3, q = f & 3;
-            const int64_t k0 = (int64_t)(gs0 + gl) * kGroup + q * 32 + i * 8;
-            u32x4 v = *reinterpret_cast<const u32x4*>(a.x + k0);
-            *reinterpret_cast<u32x4*>(xs + (size_t)f * 16) = permute_k8(v);
-        }
-    } else {
-        for (int u = threadIdx.x; u < ngs * 16 * NCOL; u += nthreads) {
-            const int f = u / NCOL, j = u - f * NCOL;
-            const int gl = f >> 4, i = (f >> 2) & 3, q = f & 3;
-            const int64_t k0 = (int64_t)(gs0 + gl) * kGroup + q * 32 + i * 8;
-            u32x4 r = {0u, 0u, 0u, 0u};
-            if (j < N) {
-                const uint16_t* col = a.x + k0 * N + j;
-                uint32_t h[8];
+    // ---- 4. stage activations, scales and zeros; group sums
+    // S[g][t] = sum of the group's 128 activations of column t
 #pragma unroll
-                for (int e = 0; e < 8; ++e) h[e] = col[(int64_t)e * N];
-                r.x = h[0] | (h[4] << 16);
-                r.y = h[1] | (h[5] << 16);
-                r.z = h[2] | (h[6] << 16);
-                r.w = h[3] | (h[7] << 16);
+    for (int j = 0; j < F; ++j) {
+        const int b = lane + j * 64;
+        if (b < nxb) xst[j].store(xs, b / NB8, b % NB8);
+    }
+#pragma unroll
+    for (int j = 0; j < SZL; ++j) {
+        const int gl = 4 * j + kb;
+        if (gl < ng) ss[gl * 16 + li] = (uint16_t)sreg[j];
+    }
+    if (kb < zwt) zsw[li * 4 + kb] = zreg;
+    if (NT == 1) {
+#pragma unroll
+        for (int j = 0; j < F; ++j) group_sums_one_column(xst[j].v[0], lane + j * 64, nxb, stab);
+    }
+    // LDS accesses of one wave complete in order; the fences keep the
+    // compiler from moving later reads above these writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (NT > 1) {
+        // rows of A are (group, column) pairs q = g * NT + t, sixteen per
+        // MFMA, times a constant operand
+        const half8 ones = unscale_ones();
+        const int nq = ng * NT;
+        for (int q0 = 0; q0 < nq; q0 += 16) {
+            int q = q0 + li;
+            q = q < nq ? q : nq - 1;
+            const int gq = q / NT, tq = q - gq * NT;
+            floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half8 xa = *reinterpret_cast<const half8*>(xs + ((size_t)(gq * 16 + kb * 4 + i) * NT + tq) * 16);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ones, d, 0, 0, 0);
             }
-            *reinterpret_cast<u32x4*>(xs + (size_t)u * 16) = r;
+            if (li == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (q0 + kb * 4 + r < nq) stab[q0 + kb * 4 + r] = d[r];
+            }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    for (int e = threadIdx.x; e < ngs * bmw; e += nthreads) {
-        const int gl = e / bmw, r = e - gl * bmw;
-        int64_t row = tile_row0 + r;
-        if (row > M - 1) row = M - 1;
-        const int g = gs0 + gl;
-        ss[e] = a.scales[row * G + g];
-        zs[e] = (uint8_t)((a.zpk[row * a.ZW + (g >> 3)] >> (4 * (g & 7))) & 0xFu);
+
+    // ---- 5. per group pair, as its weights arrive: through LDS into the
+    // MFMA layout (lane (j = row, kb) takes 16 bytes kb of the group), then
+    // per group T = 2^-24 sum_k q x on the matrix cores and
+    //   acc += s * (q - z) . x = (s * 2^24) * T - (s * z) * S
+    int tok[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = tb * 16 + li;
+        tok[tb] = t < NT ? t : NT - 1;          // rows of A past NT repeat a staged one
     }
-    __syncthreads();
-
-    // ---- main loop over this wave's groups
-    floatx4 acc[RB][NB];
+    floatx4 acc[TB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // slot of 16-byte chunk c of pair row r: (r + r / 8) * 128 + (c ^ (r % 8)) * 16
+    const int wslot0 = (lr + 0) * 128 + ((lc ^ lr) * 16);          // half 0: rows 0..7
+    const int wslot1 = (8 + lr + 1) * 128 + ((lc ^ lr) * 16);      // half 1: rows 8..15
+    const int rbase = (li + (li >> 3)) * 128;
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    const int rowoff_a = wave_m * 16 * RB + li;        // A-operand row of this lane
-    const int rowoff_c = wave_m * 16 * RB + 4 * kb;    // first C row of this lane
-
-    for (int gb = 0; gb < ng; gb += PF) {
+    for (int pp = 0; pp < NP; ++pp) {
+        if (2 * pp < ng) {
+            unsigned char* qb = qbuf + (pp & 1) * kPairBytes;
+            *reinterpret_cast<u32x4*>(qb + wslot0) = buf[pp][0];
+            *reinterpret_cast<u32x4*>(qb + wslot1) = buf[pp][1];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int gi = gb + p;
-            if (gi < ng) {
-                u32x4 w[RB];
+            for (int e = 0; e < 2; ++e) {
+                const int p = 2 * pp + e;
+                if (p < ng) {
+                    const u32x4 wv = *reinterpret_cast<const u32x4*>(qb + rbase + (((4 * e + kb) ^ (li & 7)) * 16));
+                    const int g = gw0 + p;
+                    const uint32_t zw = zsw[li * 4 + (g >> 3) - zw0];
+                    const float z = (float)((zw >> (4 * (g & 7))) & 0xFu);
+                    const float sc = (float)__builtin_bit_cast(_Float16, ss[p * 16 + li]);
+                    const float sa = sc * 16777216.0f;   // undoes the 2^-24 of the subnormal codes
+                    const float sz = sc * z;
+                    floatx4 part[TB];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) w[rb] = buf[p][rb];
-                if (gi + PF < ng) {
+                    for (int tb = 0; tb < TB; ++tb) part[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        buf[p][rb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                            wrow[rb] + (int64_t)(gw0 + gi + PF) * 16));
-                }
-                const int gl = gw0 + gi - gs0;
-                uint32_t zb[RB];
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t word = i == 0 ? wv.x : i == 1 ? wv.y : i == 2 ? wv.z : wv.w;
+                        const half8 wb = codes8(word);
+                        const size_t obase = (size_t)(p * 16 + kb * 4 + i) * NT;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) zb[rb] = zero_bias(zs[gl * bmw + rowoff_a + rb * 16]);
-                floatx4 part[RB][NB];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int cb = 0; cb < NB; ++cb) part[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    half8 b[NB];
-                    const size_t fbase = ((size_t)(gl * 16 + i * 4 + kb)) * NCOL;
-#pragma unroll
-                    for (int cb = 0; cb < NB; ++cb) {
-                        const int j = cb * 16 + li;
-                        if (NCOL >= 16 || j < NCOL) {
-                            b[cb] = *reinterpret_cast<const half8*>(xs + (fbase + j) * 16);
-                        } else {
-                            b[cb] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+                        for (int tb = 0; tb < TB; ++tb) {
+                            const half8 xa = *reinterpret_cast<const half8*>(xs + (obase + tok[tb]) * 16);
+                            part[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, wb, part[tb], 0, 0, 0);
                         }
                     }
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        const uint32_t word = i == 0 ? w[rb].x : i == 1 ? w[rb].y : i == 2 ? w[rb].z : w[rb].w;
-                        const half8 av = dequant_word(word, zb[rb]);
+                    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                        for (int cb = 0; cb < NB; ++cb)
-                            part[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[cb], part[rb][cb], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const uint2 sv = *reinterpret_cast<const uint2*>(ss + gl * bmw + rowoff_c + rb * 16);
-                    const float s0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv.x & 0xFFFF));
-                    const float s1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv.x >> 16));
-                    const float s2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv.y & 0xFFFF));
-                    const float s3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv.y >> 16));
-#pragma unroll
-                    for (int cb = 0; cb < NB; ++cb) {
-                        acc[rb][cb][0] = __builtin_fmaf(s0, part[rb][cb][0], acc[rb][cb][0]);
-                        acc[rb][cb][1] = __builtin_fmaf(s1, part[rb][cb][1], acc[rb][cb][1]);
-                        acc[rb][cb][2] = __builtin_fmaf(s2, part[rb][cb][2], acc[rb][cb][2]);
-                        acc[rb][cb][3] = __builtin_fmaf(s3, part[rb][cb][3], acc[rb][cb][3]);
-                    }
+                        for (int r = 0; r < RMAX; ++r) {
+                            int t = tb * 16 + kb * 4 + r;
+                            t = t < NT ? t : NT - 1;
+                            const float v = __builtin_fmaf(sa, part[tb][r], acc[tb][r]);
+                            acc[tb][r] = __builtin_fmaf(-sz, stab[p * NT + t], v);
+                        }
                 }
             }
         }
     }
 
-    // ---- sum the wk waves of a row block through LDS
+    // ---- 6. sum the wk waves of a row block through LDS
+    const int wm = P.wm, wk = P.wk, splitk = P.splitk;
     if (wk > 1) {
-        __syncthreads();   // everyone is done with the staged activations
+        __syncthreads();   // every wave is done with its staged data
         float* red = reinterpret_cast<float*>(smem);
         if (wave_k > 0) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+            for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const size_t idx = (((((size_t)(wave_k - 1) * wm + wave_m) * RB + rb) * NB + cb) * 4 + r) * 64 + lane;
-                        red[idx] = acc[rb][cb][r];
-                    }
+                for (int r = 0; r < RMAX; ++r) {
+                    const size_t idx = (((((size_t)(wave_k - 1) * wm + wave_m) * TB + tb) * 4 + r) * 64) + lane;
+                    red[idx] = acc[tb][r];
+                }
         }
         __syncthreads();
         if (wave_k == 0) {
             for (int kk = 1; kk < wk; ++kk) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                    for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const size_t idx = (((((size_t)(kk - 1) * wm + wave_m) * RB + rb) * NB + cb) * 4 + r) * 64 + lane;
-                            acc[rb][cb][r] += red[idx];
-                        }
+                    for (int r = 0; r < RMAX; ++r) {
+                        const size_t idx = (((((size_t)(kk - 1) * wm + wave_m) * TB + tb) * 4 + r) * 64) + lane;
+                        acc[tb][r] += red[idx];
+                    }
             }
         }
     }
 
-    // ---- epilogue
-    if (wave_k == 0) {
+    // ---- 7. epilogue: lane holds columns 16 tb + 4 kb + r of row row0 + li
+    const int N = NT;
+    const int64_t row = row0 + li;
+    if (wave_k == 0 && row < M) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t0 = tb * 16 + kb * 4;
+            if (splitk == 1) {
+                if ((N & 3) == 0 && t0 + 3 < N) {
+                    const uint32_t lo = f32_to_h16_bits(acc[tb][0]) | (f32_to_h16_bits(acc[tb][1]) << 16);
+                    const uint32_t hi = f32_to_h16_bits(acc[tb][2]) | (f32_to_h16_bits(acc[tb][3]) << 16);
+                    *reinterpret_cast<uint2*>(a.c + row * N + t0) = uint2{lo, hi};
+                } else {
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                const int col = cb * 16 + li;
-                if (col < N) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int64_t row = tile_row0 + rowoff_c + rb * 16 + r;
-                        if (row < M) {
-                            if (splitk == 1)
-                                a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rb][cb][r]);
-                            else
-                                a.part[((int64_t)sidx * M + row) * N + col] = acc[rb][cb][r];
-                        }
-                    }
+                    for (int r = 0; r < RMAX; ++r)
+                        if (t0 + r < N) a.c[row * N + t0 + r] = (uint16_t)f32_to_h16_bits(acc[tb][r]);
                 }
+            } else {
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (t0 + r < N)
+                        __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + t0 + r, acc[tb][r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+        }
     }
     if (splitk == 1) return;
 
-    // ---- split-K: the last workgroup of a row tile sums the partials in order
-    int* flag = reinterpret_cast<int*>(smem + L.flag_off);
-    __threadfence();
+    // ---- 8. split-K: the last workgroup of a row tile sums the partials in
+    // order.  Partials are written and read with agent-coherent accesses
+    // (they bypass the per-XCD L2), and every store has completed before the
+    // arrival counter moves, so no cache flush is needed.
+    int* flag = reinterpret_cast<int*>(smem + P.flag_off);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(a.counters + blockIdx.x, 1u);
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
-        if (last) atomicExch(a.counters + blockIdx.x, 0u);
+        if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *flag = last;
     }
     __syncthreads();
     if (!*flag) return;
-    __threadfence();
-    const int64_t rows_here = (M - tile_row0) < bmw ? (M - tile_row0) : bmw;
+    const int64_t tile0 = (int64_t)blockIdx.x * P.rows;
+    const int64_t rows_here = (M - tile0) < P.rows ? (M - tile0) : P.rows;
     const int64_t total = rows_here * N;
     for (int64_t e = threadIdx.x; e < total; e += nthreads) {
-        const int64_t row = tile_row0 + e / N;
+        const int64_t rr = tile0 + e / N;
         const int64_t col = e - (e / N) * N;
         float v = 0.f;
         for (int s = 0; s < splitk; ++s)
-            v += __builtin_nontemporal_load(a.part + ((int64_t)s * M + row) * N + col);
-        a.c[row * N + col] = (uint16_t)f32_to_h16_bits(v);
+            v += __hip_atomic_load(a.part + ((int64_t)s * M + rr) * N + col, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        a.c[rr * N + col] = (uint16_t)f32_to_h16_bits(v);
     }
 }
 
-template <int NCOL>
-size_t lds_for(const GemmArgs& a, const SkinnyShape& s) {
-    return skinny_layout<NCOL>(a.G, s.splitk, s.rb, s.wm, s.wk).total;
-}
-
-template <int NCOL, int RB>
-hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream) {
-    const size_t lds = lds_for<NCOL>(a, s);
-    const int64_t bmw = 16 * RB * s.wm;
-    dim3 grid((unsigned)((a.M + bmw - 1) / bmw), (unsigned)s.splitk);
+template <int NT, int PF>
+hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
+    dim3 grid((unsigned)((a.M + P.rows - 1) / P.rows), (unsigned)s.splitk);
     dim3 block((unsigned)(64 * s.wm * s.wk));
-    hipLaunchKernelGGL((skinny_kernel<NCOL, RB>), grid, block, lds, stream, a, s.wm, s.wk, s.splitk);
+    // dynamic LDS above 64 KB must be allowed per kernel, once
+    static const hipError_t lds_ok = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&skinny_kernel<NT, PF>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kMaxLds);
+    if (lds_ok != hipSuccess && P.total > 65536) return lds_ok;
+    hipLaunchKernelGGL((skinny_kernel<NT, PF>), grid, block, P.total, stream, a, P);
     return hipGetLastError();
 }
 
-template <int NCOL>
-hipError_t launch_rb(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream) {
-    return s.rb == 1 ? launch_one<NCOL, 1>(a, s, stream) : launch_one<NCOL, 2>(a, s, stream);
+template <int NT>
+hipError_t launch_nt(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream) {
+    SkinnyParams P;
+    if (!skinny_params(NT, a.G, s.splitk, s.rb, s.wm, s.wk, P)) return hipErrorInvalidValue;
+    constexpr int cap = skinny_max_pf(NT);
+    switch (P.PF) {
+        case 2: return launch_one<NT, 2>(a, s, P, stream);
+        case 4: return launch_one<NT, (cap >= 4 ? 4 : 2)>(a, s, P, stream);
+        case 8: return launch_one<NT, (cap >= 8 ? 8 : 2)>(a, s, P, stream);
+        case 16: return launch_one<NT, (cap >= 16 ? 16 : 2)>(a, s, P, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 bool skinny_supported(const SkinnyShape& s) {
-    const bool ncol_ok = s.ncol == 1 || s.ncol == 2 || s.ncol == 4 || s.ncol == 8 ||
-                         s.ncol == 16 || s.ncol == 32 || s.ncol == 64;
-    return ncol_ok && (s.rb == 1 || s.rb == 2) && s.wm >= 1 && s.wk >= 1 &&
-           s.wm * s.wk <= 8 && s.splitk >= 1;
+    return ncol_ok(s.ncol) && s.rb == 1 && s.wm >= 1 &&
+           s.wk >= 1 && s.wm * s.wk <= kMaxThreads / 64 && s.splitk >= 1;
 }
 
 int64_t skinny_row_tiles(const GemmArgs& a, const SkinnyShape& s) {
-    const int64_t bmw = 16LL * s.rb * s.wm;
-    return (a.M + bmw - 1) / bmw;
+    const int64_t rows = 16LL * s.rb * s.wm;
+    return (a.M + rows - 1) / rows;
 }
 
-size_t skinny_lds_bytes(const GemmArgs& a, const SkinnyShape& s) {
-    switch (s.ncol) {
-        case 1: return lds_for<1>(a, s);
-        case 2: return lds_for<2>(a, s);
-        case 4: return lds_for<4>(a, s);
-        case 8: return lds_for<8>(a, s);
-        case 16: return lds_for<16>(a, s);
-        case 32: return lds_for<32>(a, s);
-        case 64: return lds_for<64>(a, s);
-        default: return 0;
-    }
+const char* skinny_check(const GemmArgs& a, const SkinnyShape& s) {
+    if (!skinny_supported(s))
+        return "ncol must be 1..8, 16, 32 or 64, rb 1, wm * wk <= 16";
+    if (s.splitk > a.G) return "splitk exceeds the number of groups";
+    SkinnyParams P;
+    if (!skinny_params(s.ncol, a.G, s.splitk, s.rb, s.wm, s.wk, P))
+        return "a wave's groups exceed its load registers, or the staged data the workgroup's LDS; "
+               "add waves along K or splits";
+    return nullptr;
 }
 
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream) {
+    if (a.N != s.ncol) return hipErrorInvalidValue;
     switch (s.ncol) {
-        case 1: return launch_rb<1>(a, s, stream);
-        case 2: return launch_rb<2>(a, s, stream);
-        case 4: return launch_rb<4>(a, s, stream);
-        case 8: return launch_rb<8>(a, s, stream);
-        case 16: return launch_rb<16>(a, s, stream);
-        case 32: return launch_rb<32>(a, s, stream);
-        case 64: return launch_rb<64>(a, s, stream);
+        case 1: return launch_nt<1>(a, s, stream);
+        case 2: return launch_nt<2>(a, s, stream);
+        case 3: return launch_nt<3>(a, s, stream);
+        case 4: return launch_nt<4>(a, s, stream);
+        case 5: return launch_nt<5>(a, s, stream);
+        case 6: return launch_nt<6>(a, s, stream);
+        case 7: return launch_nt<7>(a, s, stream);
+        case 8: return launch_nt<8>(a, s, stream);
+        case 16: return launch_nt<16>(a, s, stream);
+        case 32: return launch_nt<32>(a, s, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -87,16 +87,19 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
 /*
  * Execution plan: which kernel runs and how the work is split.  Filled by
  * w4a16_plan_default(); tests and tuning may pass their own.
- *   kernel : W4A16_KERNEL_SKINNY (N <= 64: weights streamed once, products on
- *            16x16x32 fp16 MFMA, activations staged in LDS) or
- *            W4A16_KERNEL_TILED (tiles of BM x BN outputs, 32x32x16 fp16 MFMA).
- *   skinny : ncol = staged activation columns (1, 2, 4, 8, 16, 32 or 64,
- *            >= N); rb = 16-row blocks per wave (1 or 2); wm / wk = waves per
- *            workgroup along rows / along K (wm * wk <= 8); splitk = number of
- *            workgroups sharing one row tile along K (>= 1).
+ *   kernel : W4A16_KERNEL_SKINNY (N <= 8, 16 or 32: weights streamed once,
+ *            products on 16x16x32 fp16 MFMA, activations staged per wave in
+ *            LDS) or W4A16_KERNEL_TILED (tiles of BM x BN outputs, 32x32x16
+ *            fp16 MFMA; any N).
+ *   skinny : ncol = N exactly (1..8, 16 or 32); rb = 1 (16 rows per wave);
+ *            wm / wk = waves per workgroup along rows / along K
+ *            (wm * wk <= 16); splitk = number of workgroups sharing one row
+ *            tile along K (>= 1).  A wave takes at most 16 groups (8 for
+ *            N > 4, 4 for N = 16, 2 for N = 32); plans beyond that, or whose
+ *            staged activations exceed 160 KB of LDS, are rejected.
  *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256});
  *            splitk as above.
- * splitk > 1 needs a workspace (w4a16_workspace_size).
+ * splitk > 1 needs a workspace (w4a16_workspace_size_plan).
  */
 enum { W4A16_KERNEL_SKINNY = 1, W4A16_KERNEL_TILED = 2 };
 

@@ -98,10 +98,12 @@ def test_plan_checks(lib):
         return lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, kw.pop("N", 4), 1024, 128,
                                    ctypes.byref(pl), NULL, 0, NULL)
     assert gp(kernel=7, splitk=1) == UNSUPPORTED
-    assert gp(kernel=1, ncol=2, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol < N
-    assert gp(kernel=1, ncol=3, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol not a power of 2
+    assert gp(kernel=1, ncol=2, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol != N
+    assert gp(kernel=1, ncol=8, rb=1, wm=1, wk=1, splitk=1) == UNSUPPORTED   # ncol != N
+    assert gp(kernel=1, ncol=12, rb=1, wm=1, wk=1, splitk=1, N=12) == UNSUPPORTED  # no 12-column kernel
     assert gp(kernel=1, ncol=4, rb=3, wm=1, wk=1, splitk=1) == UNSUPPORTED
-    assert gp(kernel=1, ncol=4, rb=1, wm=4, wk=4, splitk=1) == UNSUPPORTED   # 16 waves
+    assert gp(kernel=1, ncol=4, rb=1, wm=4, wk=8, splitk=1) == UNSUPPORTED   # 32 waves
+    assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=1, N=4) != UNSUPPORTED  # valid plan
     assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=9) == UNSUPPORTED   # > 8 groups
     assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=2) == WORKSPACE
     assert gp(kernel=2, bm=64, bn=64, splitk=1) == UNSUPPORTED

@@ -26,28 +26,34 @@ def X_for(K, N, seed=0):
 
 
 SKINNY = [
-    # (M, K, N, ncol, rb, wm, wk, splitk)
+    # (M, K, N, ncol, rb, wm, wk, splitk); ncol == N (the kernel is built
+    # per column count: 1..8, 16, 32) and rb == 1
     (1, 128, 1, 1, 1, 1, 1, 1),
     (17, 384, 1, 1, 1, 1, 2, 1),
-    (63, 1152, 1, 1, 2, 1, 4, 1),
+    (63, 1152, 1, 1, 1, 1, 4, 1),
     (200, 1152, 1, 1, 1, 2, 4, 1),
-    (200, 1152, 1, 1, 2, 2, 2, 3),
+    (200, 1152, 1, 1, 1, 2, 2, 3),
     (130, 4096, 1, 1, 1, 1, 8, 2),
+    (130, 4096, 1, 1, 1, 1, 2, 1),
     (33, 11008, 1, 1, 1, 1, 8, 1),
+    (33, 11008, 1, 1, 1, 1, 16, 1),
+    (33, 11008, 1, 1, 1, 2, 8, 3),
     (40, 384, 2, 2, 1, 1, 1, 1),
-    (40, 384, 3, 4, 1, 1, 2, 1),
-    (77, 1152, 4, 4, 2, 2, 1, 2),
-    (77, 1152, 5, 8, 1, 2, 2, 1),
-    (96, 1152, 8, 8, 2, 2, 2, 3),
-    (96, 1152, 13, 16, 1, 4, 2, 1),
-    (130, 1152, 16, 16, 2, 4, 1, 2),
-    (130, 1152, 17, 32, 1, 2, 2, 2),
-    (64, 1152, 31, 32, 2, 4, 2, 2),
-    (64, 1152, 32, 32, 2, 1, 8, 3),
-    (50, 640, 33, 64, 1, 2, 2, 2),
-    (50, 640, 64, 64, 2, 2, 1, 5),
-    (300, 384, 1, 2, 1, 1, 1, 1),      # ncol wider than N
-    (300, 384, 2, 16, 1, 1, 1, 1),
+    (40, 384, 3, 3, 1, 1, 2, 1),
+    (77, 1152, 4, 4, 1, 2, 1, 2),
+    (77, 1152, 5, 5, 1, 2, 2, 1),
+    (77, 1152, 6, 6, 1, 1, 4, 1),
+    (77, 1152, 7, 7, 1, 1, 2, 2),
+    (96, 1152, 8, 8, 1, 2, 2, 3),
+    (96, 1152, 8, 8, 1, 2, 4, 1),
+    (130, 1152, 16, 16, 1, 1, 4, 2),
+    (130, 1152, 16, 16, 1, 1, 4, 1),
+    (64, 1152, 32, 32, 1, 1, 4, 3),
+    (64, 1152, 32, 32, 1, 2, 2, 5),
+    (50, 640, 32, 32, 1, 1, 2, 3),
+    (50, 640, 32, 32, 1, 2, 1, 5),
+    (300, 384, 2, 2, 1, 1, 1, 1),
+    (300, 384, 3, 3, 1, 1, 1, 1),
 ]
 
 
@@ -120,7 +126,7 @@ def test_repeatable_bitwise():
     M, K = 300, 1152
     p = prob(M, K)
     for N, plan in [(1, None), (16, None), (200, None),
-                    (8, B.Plan.make(kernel=1, ncol=8, rb=2, wm=2, wk=2, splitk=3)),
+                    (8, B.Plan.make(kernel=1, ncol=8, rb=1, wm=2, wk=2, splitk=3)),
                     (264, B.Plan.make(kernel=2, bm=128, bn=256, splitk=2))]:
         X = X_for(K, N, seed=3)
         a = run(p, X, plan=plan)

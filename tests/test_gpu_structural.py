@@ -15,25 +15,24 @@ pytestmark = pytest.mark.gpu
 PLANS = [
     ("default", None),
     ("skinny_c1_wk4", B.Plan.make(kernel=1, ncol=1, rb=1, wm=1, wk=4, splitk=1)),
-    ("skinny_c16_split", B.Plan.make(kernel=1, ncol=16, rb=2, wm=2, wk=2, splitk=3)),
-    ("skinny_c64", "c64"),
+    ("skinny_c16_split", B.Plan.make(kernel=1, ncol=16, rb=1, wm=2, wk=4, splitk=4)),
+    ("skinny_c32", "c32"),
     ("tiled_256", B.Plan.make(kernel=2, bm=256, bn=256, splitk=1)),
     ("tiled_128x64_split", B.Plan.make(kernel=2, bm=128, bn=64, splitk=2)),
 ]
 
 
 def _plan(plan, K):
-    if plan == "c64":   # 64 staged columns: at most 3 groups (48 KB) per workgroup
+    if plan == "c32":   # 32 staged columns: at most two groups (16 KB of LDS) per wave
         G = K // 128
-        return B.Plan.make(kernel=1, ncol=64, rb=1, wm=2, wk=1, splitk=max(4, (G + 2) // 3))
+        return B.Plan.make(kernel=1, ncol=32, rb=1, wm=1, wk=2, splitk=(G + 3) // 4)
     return plan
 
 
 def _ncols(plan, want):
-    if plan is None:
-        return want
-    if plan.kernel == B.KERNEL_SKINNY:
-        return min(want, plan.ncol)
+    # a skinny plan is built for exactly plan.ncol activation columns
+    if plan is not None and plan.kernel == B.KERNEL_SKINNY:
+        return plan.ncol
     return want
 
 
@@ -61,7 +60,7 @@ def test_identity_columns(name, plan):
     p = Problem(M, K, seed=9)
     ks = [0, 7, 8, 127, 128, 129, 255, 640, K - 1, 1000, 31, 32, 33, 64, 96, 1151 - 8]
     N = _ncols(plan, len(ks))
-    ks = ks[:N]
+    ks = (ks + [int(k) for k in np.random.default_rng(11).integers(0, K, N)])[:N]
     X = np.zeros((K, N), dtype=np.float16)
     for n, k in enumerate(ks):
         X[k, n] = 1.0
