@@ -85,7 +85,7 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
 }
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
-TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk}; }
+TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm}; }
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p);
 
@@ -141,11 +141,12 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
         p.bn = cand[pick][1];
         const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
         int64_t splitk = 1;
-        const int64_t nst = K / 64;
-        while (t * splitk < 512 && splitk * 2 <= nst / 4 && t <= kCounterSlots) splitk *= 2;
+        const int64_t ng = K / 128;
+        while (t * splitk < 512 && splitk * 2 <= ng / 2 && t <= kCounterSlots) splitk *= 2;
         p.splitk = (int32_t)splitk;
         p.ncol = 0;
-        p.rb = p.wm = p.wk = 0;
+        p.rb = p.wk = 0;
+        p.wm = 4;
     }
     return p;
 }
@@ -155,10 +156,18 @@ int64_t tiles_of(const GemmArgs& a, const w4a16_plan& p) {
                                            : tiled_tiles(a, tiled_of(p));
 }
 
-// Workspace layout: [counters: 64 KB][fp32 partials: splitk * M * N].
+// Workspace layout: [counters: 64 KB][fp32 partials: splitk * M * N]
+// [tiled kernel only: activation chunks, K * N fp16, at a 256-byte boundary].
+size_t partial_bytes(const GemmArgs& a, const w4a16_plan& p) {
+    return p.splitk <= 1 ? 0 : (size_t)p.splitk * (size_t)a.M * (size_t)a.N * 4;
+}
+size_t chunks_offset(const GemmArgs& a, const w4a16_plan& p) {
+    return (kCounterBytes + partial_bytes(a, p) + 255) & ~(size_t)255;
+}
 size_t workspace_bytes_for(const GemmArgs& a, const w4a16_plan& p) {
+    if (p.kernel == W4A16_KERNEL_TILED) return chunks_offset(a, p) + xpack_bytes(a);
     if (p.splitk <= 1) return 0;
-    return kCounterBytes + (size_t)p.splitk * (size_t)a.M * (size_t)a.N * 4;
+    return kCounterBytes + partial_bytes(a, p);
 }
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p) {
@@ -189,9 +198,10 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p) {
         if (p.splitk > 1 && tiles_of(a, p) > kCounterSlots)
             return fail(W4A16_ERR_UNSUPPORTED, "split plans support at most %lld tiles",
                         (long long)kCounterSlots);
-        if (p.splitk > a.K / 64)
-            return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d exceeds the %lld k-stages", p.splitk,
-                        (long long)(a.K / 64));
+        if (p.splitk > a.G)
+            return fail(W4A16_ERR_UNSUPPORTED, "splitk=%d exceeds the %d groups of a row", p.splitk, a.G);
+        const char* why = tiled_check(a, t);
+        if (why) return fail(W4A16_ERR_UNSUPPORTED, "tiled plan: %s", why);
         return W4A16_OK;
     }
     return fail(W4A16_ERR_UNSUPPORTED, "unknown kernel id %d", p.kernel);
@@ -229,6 +239,8 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
             return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
         a.counters = static_cast<uint32_t*>(workspace);
         a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+        if (p.kernel == W4A16_KERNEL_TILED)
+            a.xp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + chunks_offset(a, p));
     }
     a.qpk = qpk;
     a.scales = static_cast<const uint16_t*>(scales);

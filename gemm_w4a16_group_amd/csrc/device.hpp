@@ -77,4 +77,42 @@ __device__ __forceinline__ uint32_t f32_to_h16_bits(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+// Raw buffer resource over [base, base + bytes): loads through it take a
+// 32-bit per-lane byte offset plus a scalar offset, and read 0 past the end.
+// bytes is clamped to the 32-bit record count.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at
+// lds + 16 i (lds must be the same for the whole wave).  Written as inline
+// assembly on purpose: the compiler then does not track the LDS write, so it
+// does not drain the load counter before every later LDS read (it cannot
+// tell which LDS bytes the load writes); the caller orders the write with
+// its own s_waitcnt vmcnt and barrier before any wave reads those bytes.
+// The resource is a raw buffer descriptor {base, base_hi, bytes, flags}.
+// m0 carries the LDS address; no other instruction of the kernels that use
+// this helper reads m0.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int64_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFF), n, 0x00020000};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, void* lds, int voffset, int soffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(la), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
 }  // namespace w4a16

@@ -11,6 +11,7 @@ struct GemmArgs {
     const uint16_t* scales;   // fp16 bits [M, G]
     const uint32_t* zpk;      // [M, ZW]
     const uint16_t* x;        // fp16 bits [K, N]
+    uint16_t* xp;             // tiled kernel: X as 16-byte chunks [K/8][N] (workspace)
     uint16_t* c;              // fp16 bits [M, N]
     float* part;              // fp32 [splitk, M, N] partial sums (splitk > 1)
     uint32_t* counters;       // one arrival counter per output tile (splitk > 1)
@@ -24,6 +25,7 @@ struct SkinnyShape {
 
 struct TiledShape {
     int bm, bn, splitk;
+    int wm;   // waves along M: 4 (4 x 1) or 2 (2 x 2)
 };
 
 bool skinny_supported(const SkinnyShape& s);
@@ -33,7 +35,10 @@ int64_t skinny_row_tiles(const GemmArgs& a, const SkinnyShape& s);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream);
 
 bool tiled_supported(const TiledShape& t);
+// nullptr if the tiled kernel can run this shape, else the reason.
+const char* tiled_check(const GemmArgs& a, const TiledShape& t);
 int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t);
+size_t xpack_bytes(const GemmArgs& a);   // workspace the tiled kernel's activation chunks take
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream);
 
 hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,

@@ -1,17 +1,22 @@
 // Tiled W4A16 kernel for many activation columns: the compute-bound regime
-// of PerfXLLM §3.3 item 1 (many tokens), which blocks the product into tiles
-// held in shared memory.
+// of the PerfXLLM page on Snapdragon 8 Gen2, §3.3 item 1 (many tokens),
+// which blocks the product into tiles held in shared memory.
 //
-// A workgroup of four waves owns a BM x BN tile of C and walks K in stages of
-// 64.  Each stage copies the packed weights (BM rows x 32 bytes) and the
-// activations (64 x BN fp16, transposed so that each 16-byte LDS word holds
-// eight k of one column, in the dequant order) from global memory into a
-// double-buffered LDS tile.  Each wave owns a (BM/2) x (BN/2) sub-tile made
-// of 32x32 MFMA blocks: per 16-k step, a lane reads one packed weight word
-// (eight k of one row), dequantizes it in registers to fp16 (q - z) * s and
-// feeds it as the A operand of v_mfma_f32_32x32x16_f16, with fp32
-// accumulation.  The scale is folded into the fp16 operand here (one fp16
-// rounding per weight), since one accumulator spans all groups.
+// Two launches.  xpack_kernel rewrites the activations X [K, N] (N
+// contiguous) once into 16-byte chunks, chunk (ko, n) holding the eight k of
+// octet ko of column n in the order 0, 4, 1, 5, 2, 6, 3, 7 that the
+// dequantized weight words use.  The chunks are exactly the B operand of
+// v_mfma_f32_32x32x16_f16, so the GEMM stages them into LDS with
+// buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
+// reads them back conflict-free.
+//
+// tiled_kernel: a workgroup of four waves owns a BM x BN tile of C and walks
+// K one group (128 k) per stage.  The waves form a WGM x (4 / WGM) grid.
+// Each wave loads the packed weight words of its rows straight into
+// registers (32 bytes per lane per 32-row block and stage, one stage ahead)
+// and dequantizes them there, one MFMA step ahead, to fp16 (q - z) * s: one
+// fp16 rounding per weight, q - z being exact before the scale is applied.
+// fp32 accumulation throughout.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -19,38 +24,115 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int kStageRows = kGroup / 8;   // k-octets per stage
 
-// 16-byte slot of activation column n inside one k-octet row of the LDS
-// tile; the XOR spreads the eight columns a thread writes over all banks.
-__device__ __forceinline__ int xslot(int n) { return n ^ ((n >> 3) & 7); }
+// (w & mask) | bias in one instruction (the bias lives in a vector register
+// so that the instruction needs only one scalar operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bias) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(mask), "v"(bias));
+    return d;
+}
 
-template <int BM, int BN, bool VECX>
+// Eight fp16 weights (q - z) * s of one packed word, in the k order
+// 0, 4, 1, 5, 2, 6, 3, 7.  Nibbles at bits 0-3 of a half are OR-ed into
+// fp16 1024 (ulp 1), nibbles at bits 4-7 into fp16 64 (ulp 1/16); the
+// differences with 1024 + z and 64 + z are the exact integers q - z.
+struct Dequant {
+    uint32_t b1024, b64;     // fp16 1024 / 64 in both halves (vector registers)
+    half2v z1024, z64, s2;   // per row and group
+    __device__ __forceinline__ half8 operator()(uint32_t w) const {
+        const uint32_t w8 = w >> 8;
+        const half2v p0 = (as_h2(and_or(w, 0x000F000Fu, b1024)) - z1024) * s2;
+        const half2v p1 = (as_h2(and_or(w, 0x00F000F0u, b64)) - z64) * s2;
+        const half2v p2 = (as_h2(and_or(w8, 0x000F000Fu, b1024)) - z1024) * s2;
+        const half2v p3 = (as_h2(and_or(w8, 0x00F000F0u, b64)) - z64) * s2;
+        half8 r;
+        r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+        r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+        return r;
+    }
+    __device__ __forceinline__ void set(uint32_t z, uint32_t sbits) {
+        z1024 = as_h2(0x64006400u | z | (z << 16));
+        z64 = as_h2(0x54005400u | (z << 4) | (z << 20));
+        s2 = as_h2(sbits | (sbits << 16));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// X [K, N] -> chunks [K/8][N] of 16 bytes.  One thread per (k-octet, column
+// octet): eight 16-byte row loads (or element loads when N % 8 != 0),
+// transposed in registers, eight 16-byte chunk stores (128 contiguous bytes).
+template <bool VEC>
+__global__ void __launch_bounds__(256) xpack_kernel(const uint16_t* __restrict__ x, u32x4* __restrict__ xp,
+                                                    int64_t K, int64_t N) {
+    const int64_t nocts = (N + 7) / 8;
+    const int64_t total = (K / 8) * nocts;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int64_t ko = t / nocts, n0 = (t % nocts) * 8;
+    u32x4 rows[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint16_t* src = x + (ko * 8 + r) * N + n0;
+        if (VEC) {
+            rows[r] = *reinterpret_cast<const u32x4*>(src);
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = n0 + e < N ? (uint32_t)src[e] : 0u;
+            rows[r] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+    }
+    u32x4* dst = xp + ko * N + n0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+        const int d = cc >> 1;
+        u32x4 o;
+        if ((cc & 1) == 0) {
+            o.x = pair_lo(rows[0][d], rows[4][d]);
+            o.y = pair_lo(rows[1][d], rows[5][d]);
+            o.z = pair_lo(rows[2][d], rows[6][d]);
+            o.w = pair_lo(rows[3][d], rows[7][d]);
+        } else {
+            o.x = pair_hi(rows[0][d], rows[4][d]);
+            o.y = pair_hi(rows[1][d], rows[5][d]);
+            o.z = pair_hi(rows[2][d], rows[6][d]);
+            o.w = pair_hi(rows[3][d], rows[7][d]);
+        }
+        if (VEC || n0 + cc < N) dst[cc] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM>
 __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
-    constexpr int WR = BM / 2, WC = BN / 2;       // wave sub-tile
-    constexpr int TR = WR / 32, TC = WC / 32;     // 32x32 MFMA blocks per wave
-    constexpr int XBYTES = 8 * BN * 16;           // one stage of activations
-    constexpr int WBYTES = BM * 32;               // one stage of packed weights
-    constexpr int XBLK = BN;                      // 8x8 activation blocks per stage
+    constexpr int WGN = 4 / WGM;            // waves along N
+    constexpr int WM = BM / WGM;            // rows per wave
+    constexpr int WN = BN / WGN;            // columns per wave
+    constexpr int RBW = WM / 32;            // 32-row MFMA blocks per wave
+    constexpr int CBW = WN / 32;            // 32-column MFMA blocks per wave
+    constexpr int XBYTES = kStageRows * BN * 16;        // one stage of activation chunks
+    constexpr int XLOADS = kStageRows * BN / 64 / 4;    // 1 KB buffer-to-LDS loads per wave and stage
+    static_assert(BN % 64 == 0 && XLOADS % (BN / 64) == 0, "tile");
     __shared__ __attribute__((aligned(16))) unsigned char xs[2][XBYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char ws[2][WBYTES];
     __shared__ int flag;
 
     const int64_t M = a.M, N = a.N, K = a.K;
     const int G = a.G;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wave_r = wave >> 1, wave_c = wave & 1;
-    const int li = lane & 31;      // A row / B column / C column inside a 32-block
-    const int h = lane >> 5;       // which half of the 16-k step
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WGN, wave_n = wave % WGN;
+    const int l32 = lane & 31;     // A row / B column / C column inside a 32-block
+    const int hh = lane >> 5;      // which half of the 16-k MFMA step
 
     // ---- tile of this workgroup: XCD-contiguous, then grouped along M
     const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
     const int64_t T = ntm * ntn;
     int64_t L = blockIdx.x;
     if (T % 8 == 0) L = (L % 8) * (T / 8) + L / 8;
-    constexpr int64_t GM = 4;
+    constexpr int64_t GM = 8;
     const int64_t group = L / (GM * ntn);
     const int64_t first_m = group * GM;
     const int64_t gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
@@ -59,213 +141,189 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
     const int64_t row0 = tm * BM, col0 = tn * BN;
     const int64_t tile_id = tm * ntn + tn;
 
+    // stages are groups of 128 k
     const int sidx = blockIdx.y;
-    const int nst = (int)(K / BK);
-    const int st0 = (int)((int64_t)nst * sidx / splitk);
-    const int st1 = (int)((int64_t)nst * (sidx + 1) / splitk);
-
+    const int st0 = (int)((int64_t)G * sidx / splitk);
+    const int st1 = (int)((int64_t)G * (sidx + 1) / splitk);
     const int64_t KW = K / 8;
 
-    // ---- copy assignment
-    // weights: chunk c = tid + 256 t -> (half = c / BM, row = c % BM)
-    constexpr int WCH = (BM * 2) / 256;
-    const uint32_t* wsrc[WCH];
-    int wdst[WCH];
+    // ---- weights of this lane: row row0 + WM wave_m + 32 rb + l32, words
+    // 8 hh .. 8 hh + 7 of each group's sixteen.  Buffer resources start at the
+    // tile's first row so that per-lane offsets stay small; the stage moves
+    // the scalar offset only.
+    const int64_t rows_left = M - row0;
+    const int64_t tile_rows = rows_left < BM ? rows_left : BM;
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(a.qpk + row0 * KW, tile_rows * KW * 4);
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(a.scales + row0 * G, tile_rows * G * 2);
+    const __amdgpu_buffer_rsrc_t zres = buffer_rsrc(a.zpk + row0 * a.ZW, tile_rows * a.ZW * 4);
+    int woff[RBW], soff[RBW], zoff[RBW];
 #pragma unroll
-    for (int t = 0; t < WCH; ++t) {
-        const int c = tid + 256 * t;
-        const int hh = c / BM, r = c % BM;
-        int64_t row = row0 + r;
-        if (row > M - 1) row = M - 1;
-        wsrc[t] = a.qpk + row * KW + hh * 4;
-        wdst[t] = hh * (BM * 16) + r * 16;
-    }
-    // activations: block b = tid (if < XBLK) -> (k-octet ko, column octet nb)
-    const bool xcopy = tid < XBLK;
-    const int xko = tid / (BN / 8), xnb = tid % (BN / 8);
-    const int64_t xcol = col0 + xnb * 8;
-
-    // scale / zero rows of this lane (A-operand rows)
-    const uint16_t* srow[TR];
-    const uint32_t* zrow[TR];
-#pragma unroll
-    for (int rt = 0; rt < TR; ++rt) {
-        int64_t row = row0 + wave_r * WR + rt * 32 + li;
-        if (row > M - 1) row = M - 1;
-        srow[rt] = a.scales + row * G;
-        zrow[rt] = a.zpk + row * a.ZW;
+    for (int rb = 0; rb < RBW; ++rb) {
+        int r = WM * wave_m + 32 * rb + l32;
+        r = r < tile_rows ? r : (int)tile_rows - 1;
+        woff[rb] = (int)((r * KW + 8 * hh) * 4);
+        soff[rb] = (int)(r * G * 2);
+        zoff[rb] = (int)(r * a.ZW * 4);
     }
 
-    u32x4 wreg[WCH];
-    u32x4 xreg[8];
+    // ---- activation chunks: load i of wave w fills LDS chunks
+    // [64 (w XLOADS + i), +64) of the stage, i.e. chunk row
+    // (64 (w XLOADS + i)) / BN, columns (64 (w XLOADS + i)) % BN + lane.
+    // Columns past N re-read column N - 1 (they reach only output columns
+    // that are never stored).
+    constexpr int NCB = BN / 64;    // distinct column bases
+    int xcoff[NCB];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+        int64_t n = col0 + 64 * c + lane;
+        n = n < N ? n : N - 1;
+        xcoff[c] = (int)(n * 16);
+    }
+    const int xrow = (int)(N * 16);   // bytes per chunk row
 
-    auto load_stage = [&](int st) {
-        const int64_t kw0 = (int64_t)st * (BK / 8);
+    // weight words, zero word and scale of a stage, in two register sets
+    // used alternately (stage pairs are unrolled, so no copies between them)
+    u32x4 wA[RBW][2], wB[RBW][2];
+    uint32_t zA[RBW], sA[RBW], zB[RBW], sB[RBW];
+
+    auto load_w = [&](int g, u32x4 (*wr)[2], uint32_t* zr, uint32_t* sr) {
 #pragma unroll
-        for (int t = 0; t < WCH; ++t)
-            wreg[t] = *reinterpret_cast<const u32x4*>(wsrc[t] + kw0);
-        if (xcopy) {
-            const int64_t k = (int64_t)st * BK + xko * 8;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (VECX) {
-                    if (xcol < N)
-                        xreg[r] = *reinterpret_cast<const u32x4*>(a.x + (k + r) * N + xcol);
-                    else
-                        xreg[r] = u32x4{0u, 0u, 0u, 0u};
-                } else {
-                    uint32_t hv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        hv[e] = (xcol + e < N) ? (uint32_t)a.x[(k + r) * N + xcol + e] : 0u;
-                    xreg[r] = u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
-                                    hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
-                }
-            }
+        for (int rb = 0; rb < RBW; ++rb) {
+            wr[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, 0);
+            wr[rb][1] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb] + 16, g * 64, 0);
+            zr[rb] = __builtin_amdgcn_raw_buffer_load_b32(zres, zoff[rb], (g >> 3) * 4, 0);
+            sr[rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
         }
     };
-    auto store_stage = [&](int buf) {
+    auto load_x = [&](int g, int buf) {
+        const i32x4 xres = raw_rsrc(a.xp + (int64_t)g * kStageRows * N * 8, (int64_t)kStageRows * N * 16);
 #pragma unroll
-        for (int t = 0; t < WCH; ++t)
-            *reinterpret_cast<u32x4*>(&ws[buf][wdst[t]]) = wreg[t];
-        if (xcopy) {
-            // transpose the 8 (k) x 8 (n) block: column c gets the pairs
-            // (k0, k4), (k1, k5), (k2, k6), (k3, k7)
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int d = cc >> 1;
-                u32x4 o;
-                if ((cc & 1) == 0) {
-                    o.x = pair_lo(xreg[0][d], xreg[4][d]);
-                    o.y = pair_lo(xreg[1][d], xreg[5][d]);
-                    o.z = pair_lo(xreg[2][d], xreg[6][d]);
-                    o.w = pair_lo(xreg[3][d], xreg[7][d]);
-                } else {
-                    o.x = pair_hi(xreg[0][d], xreg[4][d]);
-                    o.y = pair_hi(xreg[1][d], xreg[5][d]);
-                    o.z = pair_hi(xreg[2][d], xreg[6][d]);
-                    o.w = pair_hi(xreg[3][d], xreg[7][d]);
-                }
-                const int n = xnb * 8 + cc;
-                *reinterpret_cast<u32x4*>(&xs[buf][(xko * BN + xslot(n)) * 16]) = o;
-            }
+        for (int i = 0; i < XLOADS; ++i) {
+            // XLOADS is a multiple of NCB, so the column base depends on i only
+            const int chunk = 64 * (wave * XLOADS + i);
+            const int row = chunk / BN, cb = i % NCB;
+            buffer_load_lds16(xres, &xs[buf][chunk * 16], xcoff[cb], row * xrow);
         }
     };
 
-    floatx16 acc[TR][TC];
+    floatx16 acc[RBW][CBW];
 #pragma unroll
-    for (int rt = 0; rt < TR; ++rt)
+    for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int ct = 0; ct < TC; ++ct)
+        for (int cb = 0; cb < CBW; ++cb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[rt][ct][e] = 0.f;
+            for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0.f;
 
-    // raw scale / zero words of a stage's group, loaded one stage ahead so
-    // that waiting for them never waits for the next stage's tile loads
-    uint32_t zraw[TR], sraw[TR];
-    auto load_sz = [&](int st, uint32_t* zr, uint32_t* sr) {
-        const int g = (st * BK) / kGroup;
+    Dequant dq[RBW];
 #pragma unroll
-        for (int rt = 0; rt < TR; ++rt) {
-            zr[rt] = zrow[rt][g >> 3];
-            sr[rt] = srow[rt][g];
-        }
-    };
-
-    if (st0 < st1) {
-        load_sz(st0, zraw, sraw);
-        load_stage(st0);
-        store_stage(0);
+    for (int rb = 0; rb < RBW; ++rb) {
+        dq[rb].b1024 = 0x64006400u;
+        dq[rb].b64 = 0x54005400u;
     }
-    __syncthreads();
+    // B fragment of lane (l32, hh), block cb, MFMA step t: chunk row 8 hh + t,
+    // column WN wave_n + 32 cb + l32 -> one base plus an immediate offset
+    const int bbase = ((8 * hh) * BN + WN * wave_n + l32) * 16;
 
-    for (int st = st0; st < st1; ++st) {
-        const int cur = (st - st0) & 1;
-        const bool more = st + 1 < st1;
-        uint32_t znext[TR], snext[TR];
-        if (more) {
-            load_sz(st + 1, znext, snext);
-            load_stage(st + 1);
-        }
+    // One stage: prefetch stage nx (weights into the other register set,
+    // activation chunks into the other LDS buffer), then 8 MFMA steps on
+    // stage st from buffer cur, then wait for the prefetch and meet.
+    auto stage = [&](int st, int nx, int cur, u32x4 (*wc)[2], const uint32_t* zc, const uint32_t* sc,
+                     u32x4 (*wn)[2], uint32_t* zn, uint32_t* sn) {
+        load_w(nx, wn, zn, sn);
+        load_x(nx, cur ^ 1);
+        // keep every load of the next stage at the top of this one
+        __builtin_amdgcn_sched_barrier(0);
+        // scale and zero of this group
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zc[rb] >> (4 * (st & 7))) & 0xFu, sc[rb]);
 
-        // scale and zero of this stage's group for each A row of the lane
-        const int g = (st * BK) / kGroup;
-        uint32_t zb[TR];
-        half2v s2[TR];
+        const unsigned char* xb = &xs[cur][bbase];
+        // A operand of MFMA step t: word t of the lane's eight (k-octet
+        // 8 hh + t), dequantized one step ahead; B fragments likewise
+        half8 afrag[2][RBW], bfrag[2][CBW];
+        auto read_b = [&](int t, half8* bf) {
 #pragma unroll
-        for (int rt = 0; rt < TR; ++rt) {
-            zb[rt] = zero_bias((zraw[rt] >> (4 * (g & 7))) & 0xFu);
-            s2[rt] = as_h2(sraw[rt] | (sraw[rt] << 16));
-        }
-
-        u32x4 wv[TR];
+            for (int cb = 0; cb < CBW; ++cb)
+                bf[cb] = *reinterpret_cast<const half8*>(xb + (t * BN + cb * 32) * 16);
+        };
+        auto make_a = [&](int t, half8* af) {
 #pragma unroll
-        for (int rt = 0; rt < TR; ++rt)
-            wv[rt] = *reinterpret_cast<const u32x4*>(
-                &ws[cur][h * (BM * 16) + (wave_r * WR + rt * 32 + li) * 16]);
-
+            for (int rb = 0; rb < RBW; ++rb) af[rb] = dq[rb](wc[rb][t >> 2][t & 3]);
+        };
+        read_b(0, bfrag[0]);
+        make_a(0, afrag[0]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            half8 b[TC];
-            const int ko = 4 * h + kk;
-#pragma unroll
-            for (int ct = 0; ct < TC; ++ct) {
-                const int n = wave_c * WC + ct * 32 + li;
-                b[ct] = *reinterpret_cast<const half8*>(&xs[cur][(ko * BN + xslot(n)) * 16]);
+        for (int t = 0; t < 8; ++t) {
+            if (t < 7) {
+                read_b(t + 1, bfrag[(t + 1) & 1]);
+                make_a(t + 1, afrag[(t + 1) & 1]);
             }
 #pragma unroll
-            for (int rt = 0; rt < TR; ++rt) {
-                const uint32_t word = kk == 0 ? wv[rt].x : kk == 1 ? wv[rt].y : kk == 2 ? wv[rt].z : wv[rt].w;
-                const half8 av = dequant_word_scaled(word, zb[rt], s2[rt]);
+            for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-                for (int ct = 0; ct < TC; ++ct)
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b[ct], acc[rt][ct], 0, 0, 0);
-            }
+                for (int cb = 0; cb < CBW; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[t & 1][rb], bfrag[t & 1][cb],
+                                                                         acc[rb][cb], 0, 0, 0);
         }
-
-        if (more) {
-            store_stage(cur ^ 1);
-#pragma unroll
-            for (int rt = 0; rt < TR; ++rt) {
-                zraw[rt] = znext[rt];
-                sraw[rt] = snext[rt];
-            }
-        }
+        // the prefetched chunks have landed in LDS and every wave is done
+        // with buffer cur
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    // every split has at least one group (splitk <= G); the last stage
+    // prefetches itself again (no branch around the loads; the buffer it
+    // fills was last read before the previous barrier)
+    load_w(st0, wA, zA, sA);
+    load_x(st0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = st0; st < st1; st += 2) {
+        const int n1 = st + 1 < st1 ? st + 1 : st;
+        stage(st, n1, 0, wA, zA, sA, wB, zB, sB);
+        if (st + 1 < st1) {
+            const int n2 = st + 2 < st1 ? st + 2 : st + 1;
+            stage(st + 1, n2, 1, wB, zB, sB, wA, zA, sA);
+        }
     }
 
-    // ---- epilogue: lane holds rows (e / 4) * 8 + 4 h + e % 4, column li
+    // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
 #pragma unroll
-    for (int rt = 0; rt < TR; ++rt)
+    for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int ct = 0; ct < TC; ++ct) {
-            const int64_t col = col0 + wave_c * WC + ct * 32 + li;
+        for (int cb = 0; cb < CBW; ++cb) {
+            const int64_t col = col0 + WN * wave_n + cb * 32 + l32;
             if (col < N) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int64_t row = row0 + wave_r * WR + rt * 32 + (e >> 2) * 8 + 4 * h + (e & 3);
+                    const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
                     if (row < M) {
                         if (splitk == 1)
-                            a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rt][ct][e]);
+                            a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rb][cb][e]);
                         else
-                            a.part[((int64_t)sidx * M + row) * N + col] = acc[rt][ct][e];
+                            __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col, acc[rb][cb][e],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
         }
     if (splitk == 1) return;
 
-    __threadfence();
+    // ---- split-K: the last workgroup of a tile sums the partials in order.
+    // Partials are written and read with agent-coherent accesses (they
+    // bypass the per-XCD L2), and every store has completed before the
+    // arrival counter moves, so no cache flush is needed.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = atomicAdd(a.counters + tile_id, 1u);
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
-        if (last) atomicExch(a.counters + tile_id, 0u);
+        if (last) __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         flag = last;
     }
     __syncthreads();
     if (!flag) return;
-    __threadfence();
     const int64_t rows_here = (M - row0) < BM ? (M - row0) : BM;
     const int64_t cols_here = (N - col0) < BN ? (N - col0) : BN;
     const int64_t total = rows_here * cols_here;
@@ -274,20 +332,17 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
         const int64_t col = col0 + e % cols_here;
         float v = 0.f;
         for (int s = 0; s < splitk; ++s)
-            v += __builtin_nontemporal_load(a.part + ((int64_t)s * M + row) * N + col);
+            v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         a.c[row * N + col] = (uint16_t)f32_to_h16_bits(v);
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM = 4>
 hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles, (unsigned)t.splitk);
-    const bool vecx = (a.N % 8) == 0;
-    if (vecx)
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, true>), grid, dim3(256), 0, stream, a, t.splitk);
-    else
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, false>), grid, dim3(256), 0, stream, a, t.splitk);
+    hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM>), grid, dim3(256), 0, stream, a, t.splitk);
     return hipGetLastError();
 }
 
@@ -296,14 +351,45 @@ hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t strea
 bool tiled_supported(const TiledShape& t) {
     const bool bm_ok = t.bm == 128 || t.bm == 256;
     const bool bn_ok = t.bn == 64 || t.bn == 128 || t.bn == 256;
-    return bm_ok && bn_ok && t.splitk >= 1;
+    const bool wm_ok = t.wm == 4 || (t.wm == 2 && t.bn >= 128);
+    return bm_ok && bn_ok && wm_ok && t.splitk >= 1;
+}
+
+const char* tiled_check(const GemmArgs& a, const TiledShape& t) {
+    (void)t;
+    // 32-bit buffer offsets: a 256-row weight tile and a 16-row chunk slab
+    if (a.K > ((int64_t)1 << 24)) return "K above 2^24";
+    if (a.N > ((int64_t)1 << 23)) return "N above 2^23";
+    return nullptr;
 }
 
 int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t) {
     return ((a.M + t.bm - 1) / t.bm) * ((a.N + t.bn - 1) / t.bn);
 }
 
+size_t xpack_bytes(const GemmArgs& a) { return (size_t)a.K * (size_t)a.N * 2; }
+
+hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
+    const int64_t total = (a.K / 8) * ((a.N + 7) / 8);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    u32x4* xp = reinterpret_cast<u32x4*>(a.xp);
+    if (a.N % 8 == 0)
+        hipLaunchKernelGGL((xpack_kernel<true>), dim3(blocks), dim3(256), 0, stream, a.x, xp, a.K, a.N);
+    else
+        hipLaunchKernelGGL((xpack_kernel<false>), dim3(blocks), dim3(256), 0, stream, a.x, xp, a.K, a.N);
+    return hipGetLastError();
+}
+
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
+    hipError_t e = launch_xpack(a, stream);
+    if (e != hipSuccess) return e;
+    if (t.wm == 2) {
+        if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256, 2>(a, t, stream);
+        if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128, 2>(a, t, stream);
+        if (t.bm == 128 && t.bn == 256) return launch_bmbn<128, 256, 2>(a, t, stream);
+        if (t.bm == 128 && t.bn == 128) return launch_bmbn<128, 128, 2>(a, t, stream);
+        return hipErrorInvalidValue;
+    }
     if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256>(a, t, stream);
     if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128>(a, t, stream);
     if (t.bm == 256 && t.bn == 64) return launch_bmbn<256, 64>(a, t, stream);

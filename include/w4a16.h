@@ -98,8 +98,11 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            N > 4, 4 for N = 16, 2 for N = 32); plans beyond that, or whose
  *            staged activations exceed 160 KB of LDS, are rejected.
  *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256});
- *            splitk as above.
- * splitk > 1 needs a workspace (w4a16_workspace_size_plan).
+ *            wm = waves along rows: 4 (each wave owns bm/4 rows and all
+ *            bn columns) or 2 (2 x 2 waves, bn >= 128); 0 means 4;
+ *            splitk as above; K <= 2^24 and N <= 2^23.
+ * Skinny plans with splitk > 1 and every tiled plan need a workspace
+ * (w4a16_workspace_size_plan).
  */
 enum { W4A16_KERNEL_SKINNY = 1, W4A16_KERNEL_TILED = 2 };
 
@@ -118,7 +121,8 @@ typedef struct {
 int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
                        w4a16_plan *plan);
 
-/* Workspace bytes a plan needs (0 when splitk == 1); 0 on invalid input. */
+/* Workspace bytes a plan needs (0 for a skinny plan with splitk == 1); 0 on
+ * invalid input. */
 size_t w4a16_workspace_size_plan(int64_t M, int64_t N, int64_t K,
                                  int32_t group_size, const w4a16_plan *plan);
 
@@ -135,7 +139,8 @@ size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
  * workspace: device memory of at least w4a16_gemm_workspace_size() bytes,
  * 16-byte aligned, or NULL when that size is 0.  Its first 64 KB hold one
  * arrival counter per output tile (split plans allow at most 16384 tiles);
- * fp32 partial sums follow.  Before its first use the caller must fill at
+ * fp32 partial sums follow, then (tiled kernel) x rewritten as 16-byte
+ * chunks of eight k of one column.  Before its first use the caller must fill at
  * least the first 64 KB with zeros; every call leaves the counters at zero
  * again, so one zero-fill serves all later calls of any shape.  Calls that
  * share a workspace must not run concurrently (one workspace per stream).

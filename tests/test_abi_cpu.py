@@ -107,7 +107,9 @@ def test_plan_checks(lib):
     assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=9) == UNSUPPORTED   # > 8 groups
     assert gp(kernel=1, ncol=4, rb=1, wm=1, wk=1, splitk=2) == WORKSPACE
     assert gp(kernel=2, bm=64, bn=64, splitk=1) == UNSUPPORTED
-    assert gp(kernel=2, bm=128, bn=64, splitk=17) == UNSUPPORTED            # > 16 stages
+    assert gp(kernel=2, bm=128, bn=64, splitk=9) == UNSUPPORTED             # > 8 groups
+    assert gp(kernel=2, bm=128, bn=64, splitk=1, wm=2) == UNSUPPORTED       # 2 x 2 needs bn >= 128
+    assert gp(kernel=2, bm=128, bn=128, splitk=1, wm=3) == UNSUPPORTED
     assert lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, 4, 1024, 128, None, NULL, 0, NULL) == INVALID
     bad = B.Plan.make(kernel=2, bm=64, bn=64, splitk=1)
     assert lib.w4a16_workspace_size_plan(64, 4, 1024, 128, ctypes.byref(bad)) == 0
@@ -122,7 +124,10 @@ def test_default_plans_are_valid(lib):
             assert lib.w4a16_plan_default(M, N, K, 128, ctypes.byref(p)) == OK
             ws = lib.w4a16_workspace_size_plan(M, N, K, 128, ctypes.byref(p))
             assert ws == lib.w4a16_gemm_workspace_size(M, N, K, 128)
-            assert (ws == 0) == (p.splitk == 1), (M, N, K, p.as_dict())
+            needs = p.kernel == 2 or p.splitk > 1
+            assert (ws == 0) == (not needs), (M, N, K, p.as_dict())
+            if p.kernel == 2:
+                assert ws >= 65536 + K * N * 2
             # a valid plan passes every check: with fake pointers the call
             # then fails only on the workspace (if any), never on the plan
             far = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]

@@ -70,29 +70,34 @@ def test_skinny_plan(case):
 
 
 TILED = [
-    # (M, K, N, bm, bn, splitk)
-    (1, 128, 65, 128, 64, 1),
-    (100, 384, 65, 128, 64, 1),
-    (300, 384, 100, 128, 128, 1),
-    (300, 1152, 128, 128, 64, 2),
-    (300, 1152, 200, 256, 64, 3),
-    (257, 384, 264, 256, 128, 1),
-    (257, 1152, 264, 128, 256, 2),
-    (520, 640, 520, 256, 256, 1),
-    (520, 640, 256, 256, 256, 4),
-    (64, 256, 77, 128, 128, 1),       # N not a multiple of 8
-    (129, 384, 130, 256, 128, 2),
-    (40, 128, 3, 128, 64, 1),         # small N on the tiled kernel
+    # (M, K, N, bm, bn, splitk, wm)
+    (1, 128, 65, 128, 64, 1, 4),
+    (100, 384, 65, 128, 64, 1, 4),
+    (300, 384, 100, 128, 128, 1, 4),
+    (300, 1152, 128, 128, 64, 2, 4),
+    (300, 1152, 200, 256, 64, 3, 4),
+    (257, 384, 264, 256, 128, 1, 4),
+    (257, 1152, 264, 128, 256, 2, 4),
+    (520, 640, 520, 256, 256, 1, 4),
+    (520, 640, 256, 256, 256, 4, 4),
+    (64, 256, 77, 128, 128, 1, 4),       # N not a multiple of 8
+    (129, 384, 130, 256, 128, 2, 4),
+    (40, 128, 3, 128, 64, 1, 4),         # small N on the tiled kernel
+    # 2 x 2 wave grid
+    (300, 384, 100, 128, 128, 1, 2),
+    (257, 1152, 264, 128, 256, 2, 2),
+    (520, 640, 520, 256, 256, 1, 2),
+    (129, 384, 130, 256, 128, 2, 2),
 ]
 
 
-@pytest.mark.parametrize("case", TILED, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d" % c)
+@pytest.mark.parametrize("case", TILED, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d_wm%d" % c)
 def test_tiled_plan(case):
-    M, K, N, bm, bn, splitk = case
+    M, K, N, bm, bn, splitk, wm = case
     log("tiled %s" % (case,))
     p = prob(M, K)
     X = X_for(K, N)
-    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk)
+    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk, wm=wm)
     C = run(p, X, plan=plan)
     C_ref, A_ref = p.reference(X)
     assert_parity(C, C_ref, A_ref, str(case))
