@@ -32,6 +32,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 GROUP = 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CSRC = os.path.join(ROOT, "gemm_w4a16_group_amd", "csrc")
+KERNEL_SOURCES = {"skinny_kernel": ("device.hpp", "launch.hpp", "skinny.hip"),
+                  "tiled_kernel": ("device.hpp", "launch.hpp", "tiled.hip")}
 
 
 def alg_bytes(M, K, N):
@@ -44,6 +48,34 @@ def alg_flops(M, K, N):
     return 2 * M * K * N
 
 
+def sources_sha(kernel):
+    """sha256 over the source files a kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel.split("<")[0]]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic(kernel, M, K, N):
+    """HBM bytes per launch of `kernel` at this shape from the stored rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters, each scaled by what the same counter
+    reads for a copy kernel of known size; None when no counters were taken
+    or the kernel's sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = t.get("kernels", {}).get("%s@%dx%dx%d" % (kernel, M, K, N))
+    cal = t.get("calibration")
+    if not rec or not cal or rec.get("sources_sha256") != sources_sha(kernel):
+        return None
+    b = rec["fetch_kib"] * 1024 * cal["fetch_factor"] + rec["write_kib"] * 1024 * cal["write_factor"]
+    return int(round(b))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,7 +84,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=40, help="weight copies cycled through (cold cache)")
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
-                             "large_n", "stack"])
+                             "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -190,13 +222,32 @@ def cpu_baseline(M, K, seconds, wid):
     }
 
 
+def gemm_secondary(iters):
+    """The N = 4096 GEMM figure (one call = activation re-layout + tiled kernel)."""
+    from gemm_w4a16_group_amd import binding as B
+    M, K, N = 12288, 4096, 4096
+    gms, gplan = gemm_large(M, K, N, 4, iters)
+    tf = alg_flops(M, K, N) / (gms * 1e-3) / 1e12
+    kern = B.kernel_name(M, N, K)
+    return {
+        "metric": "W4A16 GEMM TFLOP/s (12288x4096, N=4096)", "value": round(tf, 2),
+        "unit": "TFLOP/s", "ms_per_call": round(gms, 4), "plan": gplan,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4),
+                     "traffic": traffic(kern, M, K, N), "kernel": kern,
+                     "flops_per_launch": alg_flops(M, K, N),
+                     "timed": "whole call: xpack_kernel (activation re-layout) + %s" % kern}}
+
+
 def headline(args):
     import torch
+    from gemm_w4a16_group_amd import binding as B
     M, K, N = 12288, 4096, 1
     wid = 3
     ms, plan, steps, *_ = gemv_rotation(M, K, wid, args.copies, args.steps, args.warmup)
     b = alg_bytes(M, K, N)
     gbs = b / (ms * 1e-3) / 1e9
+    kern = B.kernel_name(M, N, K)
     line = {
         "metric": "W4A16 GEMV HBM GB/s (12288x4096,N=1) + GEMM TFLOPS at N=4096; % roofline",
         "value": round(gbs, 2),
@@ -215,23 +266,30 @@ def headline(args):
                    "cold_cache_copies": args.copies, "timing": "HIP graph of %d calls, HIP events"
                    % args.copies, "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "skinny_kernel<1,1>", "bytes_per_launch": b,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic(kern, M, K, N),
+                     "kernel": kern, "bytes_per_launch": b,
                      "us_per_launch": round(ms * 1e3, 3)},
     }
     if not args.no_gemm:
-        Ng = 4096
-        gms, gplan = gemm_large(12288, 4096, Ng, 4, args.gemm_iters)
-        tf = alg_flops(12288, 4096, Ng) / (gms * 1e-3) / 1e12
-        line["secondary"] = {
-            "metric": "W4A16 GEMM TFLOP/s (12288x4096, N=4096)", "value": round(tf, 2),
-            "unit": "TFLOP/s", "ms_per_call": round(gms, 4), "plan": gplan,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "tiled_kernel<256,256>", "flops_per_launch": alg_flops(12288, 4096, Ng)}}
+        line["secondary"] = gemm_secondary(args.gemm_iters)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(M, K, args.cpu_seconds, wid)
     print(json.dumps(line), flush=True)
+
+
+def copy_calib():
+    """A plain fp16 copy kernel of known size (reads and writes 512 MiB each
+    launch): the reference that rocprofv3 FETCH_SIZE / WRITE_SIZE are scaled
+    by."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy_calib", "launches": 5, "bytes_read_per_launch": 2 * n,
+                      "bytes_written_per_launch": 2 * n}), flush=True)
 
 
 def extra(args):
@@ -240,6 +298,12 @@ def extra(args):
     from gemm_w4a16_group_amd import binding as B
     from gemm_w4a16_group_amd import inputs
     rows = []
+    if args.workload == "copy_calib":
+        copy_calib()
+        return
+    if args.workload == "gemm_12288x4096_n4096":
+        print(json.dumps(gemm_secondary(args.gemm_iters)), flush=True)
+        return
     if args.workload == "gemv_4096x4096":
         ms, plan, steps, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup)
         rows.append(("gemv_4096x4096", 4096, 4096, 1, ms, plan))

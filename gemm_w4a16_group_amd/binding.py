@@ -77,6 +77,9 @@ def load_library(path=None):
         lib.w4a16_workspace_size_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
         lib.w4a16_gemm_workspace_size.restype = sz
         lib.w4a16_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.w4a16_kernel_name.restype = ctypes.c_int
+        lib.w4a16_kernel_name.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan), ctypes.c_char_p,
+                                          ctypes.c_size_t]
         lib.w4a16_gemm.restype = ctypes.c_int
         lib.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
         lib.w4a16_gemm_plan.restype = ctypes.c_int
@@ -170,6 +173,13 @@ def plan_default(M, N, K):
     p = Plan()
     _check(lib().w4a16_plan_default(M, N, K, GROUP, ctypes.byref(p)))
     return p
+
+
+def kernel_name(M, N, K, plan=None):
+    """Name of the main kernel a plan (None: the default) launches."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().w4a16_kernel_name(M, N, K, GROUP, None if plan is None else ctypes.byref(plan), buf, 128))
+    return buf.value.decode()
 
 
 def workspace_size(M, N, K, plan=None):

@@ -89,20 +89,27 @@ TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.split
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p);
 
-// Default plan (tuned on MI355X for the LLaMA-7B shapes; any valid plan is
-// correct, this one only decides speed).
+// Default plan (measured on MI355X on the LLaMA-7B shapes; any valid plan
+// is correct, this one only decides speed).
 //
-// Skinny kernel (N <= 8, or N in {16, 32, 64}): one 16-row block per wave
-// (several waves along M share the staged activations when N grows), about
-// eight groups per wave along K so that all of a wave's weight loads are in
-// flight at once, and a split across workgroups only when the staged
-// activations would not fit in LDS.
+// Skinny kernel for N <= 8, and for N in {16, 32} when the matrix is small
+// (below 2^25 weights the tiled kernel has too few tiles to stream the
+// weights fast).  One 16-row block per wave (several waves along M share
+// the staged activations when N grows), about eight groups per wave along K
+// so that all of a wave's weight loads are in flight at once, and a split
+// across workgroups only when the staged activations would not fit in LDS.
+//
+// Tiled kernel otherwise: 256 x 128 tiles from N = 4096 on, 128 x 128 from
+// N = 512, 128 x 64 below; a split along K only when there are too few
+// tiles to fill the chip (N <= 32: two-way, four-way under 64 tiles; larger
+// N: two-way for long rows, K >= 8192).
 w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
     w4a16_plan p;
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
     const GemmArgs a = make_args(M, N, K);
-    if (skinny_columns(N)) {
+    const bool small = M * K < ((int64_t)1 << 25);
+    if (N <= 8 || (skinny_columns(N) && small)) {
         p.kernel = W4A16_KERNEL_SKINNY;
         p.ncol = (int32_t)N;
         p.rb = 1;
@@ -126,28 +133,20 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
         }
         memset(&p, 0, sizeof(p));
     }
-    {
-        p.kernel = W4A16_KERNEL_TILED;
-        const int cand[4][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}};
-        int pick = 3;
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = ((M + cand[i][0] - 1) / cand[i][0]) * ((N + cand[i][1] - 1) / cand[i][1]);
-            if (t >= 512) {
-                pick = i;
-                break;
-            }
-        }
-        p.bm = cand[pick][0];
-        p.bn = cand[pick][1];
-        const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-        int64_t splitk = 1;
-        const int64_t ng = K / 128;
-        while (t * splitk < 512 && splitk * 2 <= ng / 2 && t <= kCounterSlots) splitk *= 2;
-        p.splitk = (int32_t)splitk;
-        p.ncol = 0;
-        p.rb = p.wk = 0;
-        p.wm = 4;
+    p.kernel = W4A16_KERNEL_TILED;
+    p.wm = 4;
+    p.bm = N >= 4096 ? 256 : 128;
+    p.bn = N >= 512 ? 128 : 64;
+    const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    int64_t splitk = 1;
+    if (t < 160 && t <= kCounterSlots) {
+        if (N <= 32)
+            splitk = t < 64 ? 4 : 2;
+        else if (K >= 8192)
+            splitk = 2;
     }
+    while (splitk > G) splitk /= 2;
+    p.splitk = (int32_t)splitk;
     return p;
 }
 
@@ -325,6 +324,22 @@ size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
     if (check_dims(M, N, K, group_size)) return 0;
     GemmArgs a = make_args(M, N, K);
     return workspace_bytes_for(a, default_plan(M, N, K));
+}
+
+int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const w4a16_plan* plan, char* buf,
+                      size_t len) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    if (!buf || len == 0) return fail(W4A16_ERR_INVALID_ARG, "null or empty name buffer");
+    GemmArgs a = make_args(M, N, K);
+    const w4a16_plan p = plan ? *plan : default_plan(M, N, K);
+    st = check_plan(a, p);
+    if (st) return st;
+    if (p.kernel == W4A16_KERNEL_SKINNY)
+        snprintf(buf, len, "skinny_kernel<%d, %d>", p.ncol, skinny_pf(a, skinny_of(p)));
+    else
+        snprintf(buf, len, "tiled_kernel<%d, %d, %d>", p.bm, p.bn, p.wm == 0 ? 4 : p.wm);
+    return ok();
 }
 
 int w4a16_gemv(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x,

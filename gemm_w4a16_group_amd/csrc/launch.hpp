@@ -32,6 +32,7 @@ bool skinny_supported(const SkinnyShape& s);
 // nullptr if the skinny kernel can run this shape and plan, else the reason.
 const char* skinny_check(const GemmArgs& a, const SkinnyShape& s);
 int64_t skinny_row_tiles(const GemmArgs& a, const SkinnyShape& s);
+int skinny_pf(const GemmArgs& a, const SkinnyShape& s);   // the kernel's PF template argument
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream);
 
 bool tiled_supported(const TiledShape& t);

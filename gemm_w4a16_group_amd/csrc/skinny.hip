@@ -565,6 +565,12 @@ const char* skinny_check(const GemmArgs& a, const SkinnyShape& s) {
     return nullptr;
 }
 
+int skinny_pf(const GemmArgs& a, const SkinnyShape& s) {
+    SkinnyParams P;
+    if (!skinny_params(s.ncol, a.G, s.splitk, s.rb, s.wm, s.wk, P)) return 0;
+    return P.PF;
+}
+
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyShape& s, hipStream_t stream) {
     if (a.N != s.ncol) return hipErrorInvalidValue;
     switch (s.ncol) {

@@ -121,6 +121,14 @@ typedef struct {
 int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
                        w4a16_plan *plan);
 
+/* Name of the main kernel a plan (NULL: the default plan) launches for this
+ * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 8>"
+ * or "tiled_kernel<256, 128, 4>" (a tiled plan also launches xpack_kernel
+ * first).  Writes at most len bytes including the terminating 0 into buf.
+ * Returns a status; launches nothing. */
+int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                      const w4a16_plan *plan, char *buf, size_t len);
+
 /* Workspace bytes a plan needs (0 for a skinny plan with splitk == 1); 0 on
  * invalid input. */
 size_t w4a16_workspace_size_plan(int64_t M, int64_t N, int64_t K,

@@ -158,3 +158,15 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     st = _gemm(lib)
     assert st == HIPERR
     assert len(lib.w4a16_last_error()) > 0
+
+
+def test_kernel_name_follows_the_plan(lib):
+    assert B.kernel_name(12288, 1, 4096) == "skinny_kernel<1, 8>"
+    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<256, 128, 4>"
+    p = B.Plan.make(kernel=2, bm=128, bn=256, splitk=1, wm=2)
+    assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2>"
+    buf = ctypes.create_string_buffer(8)
+    assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
+    assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
+    assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, buf, 8) == OK           # truncated
+    assert buf.value == b"skinny_"
