@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a16.h")
 GROUP = 128
 KERNEL_SKINNY = 1
 KERNEL_TILED = 2
+KERNEL_NARROW = 3
 
 _lib = None
 _lock = threading.Lock()
@@ -37,7 +38,7 @@ class W4A16Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("ncol", ctypes.c_int32), ("rb", ctypes.c_int32),
                 ("wm", ctypes.c_int32), ("wk", ctypes.c_int32), ("bm", ctypes.c_int32),
-                ("bn", ctypes.c_int32), ("splitk", ctypes.c_int32)]
+                ("bn", ctypes.c_int32), ("splitk", ctypes.c_int32), ("pf", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}

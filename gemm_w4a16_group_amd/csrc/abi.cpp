@@ -86,13 +86,15 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
 TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm}; }
+NarrowShape narrow_of(const w4a16_plan& p) { return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb}; }
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p);
 
 // Default plan (measured on MI355X on the LLaMA-7B shapes; any valid plan
 // is correct, this one only decides speed).
 //
-// Skinny kernel for N <= 8, and for N in {16, 32} when the matrix is small
+// Narrow kernel for 8 <= N <= 32 (see below).  Skinny kernel for N < 8,
+// and for N in {16, 32} when the matrix is small and no narrow plan fits
 // (below 2^25 weights the tiled kernel has too few tiles to stream the
 // weights fast).  One 16-row block per wave (several waves along M share
 // the staged activations when N grows), about eight groups per wave along K
@@ -108,8 +110,24 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
     const GemmArgs a = make_args(M, N, K);
+    // narrow kernel for 8 <= N <= 32: 64 rows per workgroup, a ring of 8
+    // groups per wave, the smallest split whose activations fit in LDS
+    if (N >= 8 && N <= 32) {
+        p.kernel = W4A16_KERNEL_NARROW;
+        p.ncol = N <= 16 ? 16 : 32;
+        p.pf = 8;
+        p.rb = 1;
+        for (int64_t splitk = 1; splitk <= G; ++splitk) {
+            p.splitk = (int32_t)splitk;
+            const std::string saved = g_err;
+            const int st = check_plan(a, p);
+            g_err = saved;
+            if (st == W4A16_OK) return p;
+        }
+        memset(&p, 0, sizeof(p));
+    }
     const bool small = M * K < ((int64_t)1 << 25);
-    if (N <= 8 || (skinny_columns(N) && small)) {
+    if (N < 8 || (skinny_columns(N) && small)) {
         p.kernel = W4A16_KERNEL_SKINNY;
         p.ncol = (int32_t)N;
         p.rb = 1;
@@ -151,6 +169,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 int64_t tiles_of(const GemmArgs& a, const w4a16_plan& p) {
+    if (p.kernel == W4A16_KERNEL_NARROW) return narrow_row_tiles(a, narrow_of(p));
     return p.kernel == W4A16_KERNEL_SKINNY ? skinny_row_tiles(a, skinny_of(p))
                                            : tiled_tiles(a, tiled_of(p));
 }
@@ -164,7 +183,8 @@ size_t chunks_offset(const GemmArgs& a, const w4a16_plan& p) {
     return (kCounterBytes + partial_bytes(a, p) + 255) & ~(size_t)255;
 }
 size_t workspace_bytes_for(const GemmArgs& a, const w4a16_plan& p) {
-    if (p.kernel == W4A16_KERNEL_TILED) return chunks_offset(a, p) + xpack_bytes(a);
+    if (p.kernel == W4A16_KERNEL_TILED || p.kernel == W4A16_KERNEL_NARROW)
+        return chunks_offset(a, p) + xpack_bytes(a);
     if (p.splitk <= 1) return 0;
     return kCounterBytes + partial_bytes(a, p);
 }
@@ -203,6 +223,18 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p) {
         if (why) return fail(W4A16_ERR_UNSUPPORTED, "tiled plan: %s", why);
         return W4A16_OK;
     }
+    if (p.kernel == W4A16_KERNEL_NARROW) {
+        const NarrowShape n = narrow_of(p);
+        if (!narrow_supported(n))
+            return fail(W4A16_ERR_UNSUPPORTED, "narrow plan invalid (ncol=%d pf=%d splitk=%d)", p.ncol, p.pf,
+                        p.splitk);
+        if (p.splitk > 1 && tiles_of(a, p) > kCounterSlots)
+            return fail(W4A16_ERR_UNSUPPORTED, "split plans support at most %lld row tiles",
+                        (long long)kCounterSlots);
+        const char* why = narrow_check(a, n);
+        if (why) return fail(W4A16_ERR_UNSUPPORTED, "narrow plan: %s", why);
+        return W4A16_OK;
+    }
     return fail(W4A16_ERR_UNSUPPORTED, "unknown kernel id %d", p.kernel);
 }
 
@@ -238,7 +270,7 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
             return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
         a.counters = static_cast<uint32_t*>(workspace);
         a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-        if (p.kernel == W4A16_KERNEL_TILED)
+        if (p.kernel == W4A16_KERNEL_TILED || p.kernel == W4A16_KERNEL_NARROW)
             a.xp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + chunks_offset(a, p));
     }
     a.qpk = qpk;
@@ -248,8 +280,9 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
     a.c = static_cast<uint16_t*>(c);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = p.kernel == W4A16_KERNEL_SKINNY ? launch_skinny(a, skinny_of(p), s)
-                                                   : launch_tiled(a, tiled_of(p), s);
+    hipError_t e = p.kernel == W4A16_KERNEL_SKINNY   ? launch_skinny(a, skinny_of(p), s)
+                   : p.kernel == W4A16_KERNEL_NARROW ? launch_narrow(a, narrow_of(p), s)
+                                                     : launch_tiled(a, tiled_of(p), s);
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -337,6 +370,8 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     if (st) return st;
     if (p.kernel == W4A16_KERNEL_SKINNY)
         snprintf(buf, len, "skinny_kernel<%d, %d>", p.ncol, skinny_pf(a, skinny_of(p)));
+    else if (p.kernel == W4A16_KERNEL_NARROW)
+        snprintf(buf, len, "narrow_kernel<%d, %d, %d>", p.ncol / 16, p.pf, narrow_of(p).rb);
     else
         snprintf(buf, len, "tiled_kernel<%d, %d, %d>", p.bm, p.bn, p.wm == 0 ? 4 : p.wm);
     return ok();

@@ -13,44 +13,47 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;          // weights per (scale, zero) pair
-constexpr uint32_t kBias = 0x64006400u;  // fp16 1024.0 in both halves
-
 __device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 __device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 
-// (1024 + z) in both fp16 halves of a word, for a 4-bit zero code z.
-__device__ __forceinline__ uint32_t zero_bias(uint32_t z) { return kBias | z | (z << 16); }
-
-// One packed word (8 codes, nibble j = k offset j) -> 8 fp16 values (q - z),
-// exact.  Each nibble is OR-ed into the mantissa of fp16 1024 (ulp 1 there),
-// which gives 1024 + q; subtracting 1024 + z leaves the integer q - z.
-// Element order of the result: k offsets 0, 4, 1, 5, 2, 6, 3, 7 (each fp16
-// pair holds nibbles p and p + 4 of the word).  The activation operand of the
-// matrix instruction is stored in the same order.
-__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t zb) {
-    const half2v z2 = as_h2(zb);
-    half2v p0 = as_h2((w & 0x000F000Fu) | kBias) - z2;
-    half2v p1 = as_h2(((w >> 4) & 0x000F000Fu) | kBias) - z2;
-    half2v p2 = as_h2(((w >> 8) & 0x000F000Fu) | kBias) - z2;
-    half2v p3 = as_h2(((w >> 12) & 0x000F000Fu) | kBias) - z2;
-    half8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
+// (w & mask) | bias in one instruction (the bias lives in a vector register
+// so that the instruction needs only one scalar operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bias) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(mask), "v"(bias));
+    return d;
 }
 
-// Same, then multiplied by the group scale (result rounded to fp16).
-__device__ __forceinline__ half8 dequant_word_scaled(uint32_t w, uint32_t zb, half2v s2) {
-    const half2v z2 = as_h2(zb);
-    half2v p0 = (as_h2((w & 0x000F000Fu) | kBias) - z2) * s2;
-    half2v p1 = (as_h2(((w >> 4) & 0x000F000Fu) | kBias) - z2) * s2;
-    half2v p2 = (as_h2(((w >> 8) & 0x000F000Fu) | kBias) - z2) * s2;
-    half2v p3 = (as_h2(((w >> 12) & 0x000F000Fu) | kBias) - z2) * s2;
-    half8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
+// Eight fp16 weights (q - z) * s of one packed word, in the k order
+// 0, 4, 1, 5, 2, 6, 3, 7 (the order the activation chunks use).  Nibbles
+// at bits 0-3 of a half are OR-ed into fp16 1024 (ulp 1), nibbles at bits
+// 4-7 into fp16 64 (ulp 1/16); the differences with 1024 + z and 64 + z are
+// the exact integers q - z, and the product with s is the one rounding.
+struct Dequant {
+    uint32_t b1024, b64;     // fp16 1024 / 64 in both halves (vector registers)
+    half2v z1024, z64, s2;   // per row and group
+    __device__ __forceinline__ void init() {
+        b1024 = 0x64006400u;
+        b64 = 0x54005400u;
+    }
+    __device__ __forceinline__ half8 operator()(uint32_t w) const {
+        const uint32_t w8 = w >> 8;
+        const half2v p0 = (as_h2(and_or(w, 0x000F000Fu, b1024)) - z1024) * s2;
+        const half2v p1 = (as_h2(and_or(w, 0x00F000F0u, b64)) - z64) * s2;
+        const half2v p2 = (as_h2(and_or(w8, 0x000F000Fu, b1024)) - z1024) * s2;
+        const half2v p3 = (as_h2(and_or(w8, 0x00F000F0u, b64)) - z64) * s2;
+        half8 r;
+        r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+        r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+        return r;
+    }
+    // z: 4-bit zero code; sbits: fp16 bits of the scale
+    __device__ __forceinline__ void set(uint32_t z, uint32_t sbits) {
+        z1024 = as_h2(0x64006400u | z | (z << 16));
+        z64 = as_h2(0x54005400u | (z << 4) | (z << 20));
+        s2 = as_h2(sbits | (sbits << 16));
+    }
+};
 
 // 8 consecutive activations x[k0 .. k0+7] (as four fp16 pairs) reordered to
 // the dequant order 0, 4, 1, 5, 2, 6, 3, 7.

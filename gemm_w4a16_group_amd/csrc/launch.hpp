@@ -28,6 +28,13 @@ struct TiledShape {
     int wm;   // waves along M: 4 (4 x 1) or 2 (2 x 2)
 };
 
+struct NarrowShape {
+    int ncol;     // staged columns: 16, 32 or 64 (>= N)
+    int pf;       // groups of weights in flight per wave: 8 or 16
+    int splitk;
+    int rb;       // 16-row blocks per wave: 1 or 2 (64 or 128 rows per workgroup)
+};
+
 bool skinny_supported(const SkinnyShape& s);
 // nullptr if the skinny kernel can run this shape and plan, else the reason.
 const char* skinny_check(const GemmArgs& a, const SkinnyShape& s);
@@ -41,6 +48,16 @@ const char* tiled_check(const GemmArgs& a, const TiledShape& t);
 int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t);
 size_t xpack_bytes(const GemmArgs& a);   // workspace the tiled kernel's activation chunks take
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream);
+
+bool narrow_supported(const NarrowShape& s);
+// nullptr if the narrow kernel can run this shape and plan, else the reason.
+const char* narrow_check(const GemmArgs& a, const NarrowShape& s);
+int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s);
+size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s);
+hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream);
+
+// X [K, N] -> 16-byte chunks [K/8][N] in a.xp (the tiled and narrow kernels' B/A operand layout)
+hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream);
 
 hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,
                             hipStream_t stream);

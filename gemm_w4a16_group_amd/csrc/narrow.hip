@@ -1,0 +1,340 @@
+// Narrow W4A16 kernel for a few activation columns (N up to 64): still the
+// bandwidth-bound side of the PerfXLLM page on Snapdragon 8 Gen2, §3.3
+// item 1 (few tokens make B tall and thin), where the weight stream decides
+// the time and every weight byte must be read once, early and coalesced.
+//
+// A workgroup of four waves owns BM = 4 x 16 RB rows and a contiguous range
+// of groups along K (splitk workgroups share a row tile).  At the start it
+// copies the activation chunks of its groups (the 16-byte chunks of the
+// tiled path: eight k of one column in dequant order) from L2 straight into
+// LDS, where all four waves read them; it never touches them in HBM again.
+// Each wave streams the packed weights of its 16 RB rows through a ring of
+// PF register stages (one 128-k group per stage, 16 bytes per lane and
+// 16-row block), so PF groups of every wave are in flight while it works;
+// there is no barrier in the main loop.  Words are dequantized in registers
+// to fp16 (q - z) * s and meet the activations in v_mfma_f32_16x16x32_f16
+// with the activations as the A operand (16 columns as rows) and the weights
+// as B (16 weight rows as columns), so each lane ends with one weight row
+// and four consecutive output columns: one 8-byte store.  fp32 accumulation;
+// split-K partials are summed in order by the last workgroup of a tile.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kNarrowMaxLds = 160 * 1024;
+
+// Wait until at most n vector-memory operations are outstanding.  Inline
+// assembly with a memory clobber, so that the compiler keeps every load
+// issued before it above it (the count includes loads the compiler cannot
+// see, the buffer-to-LDS copies).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
+}
+
+template <int NC, int PF, int kRB>
+__global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
+    constexpr int NCOL = 16 * NC;       // staged columns (N padded to 16 NC)
+    constexpr int kNarrowBM = 64 * kRB; // rows per workgroup (16 kRB per wave)
+    constexpr int WLOADS = kRB;         // weight loads per wave and stage
+    static_assert(PF * WLOADS < 64, "vmcnt range");
+    // dynamic LDS: the activation chunks, then the split-K flag (all of
+    // the 160 KB is dynamic, so that the kernel may ask for every byte)
+    extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
+
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int G = a.G;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15;   // weight row in a 16-row block / activation column in a 16-column block
+    const int kq = lane >> 4;    // k-quarter of the 32-k MFMA step (words 4 kq .. 4 kq + 3 of a group)
+
+    const int64_t row0 = (int64_t)blockIdx.x * kNarrowBM;
+    const int sidx = blockIdx.y;
+    const int g0 = (int)((int64_t)G * sidx / splitk);
+    const int g1 = (int)((int64_t)G * (sidx + 1) / splitk);
+    const int ng = g1 - g0;      // >= 1 since splitk <= G
+    const int64_t KW = K / 8;
+
+    // ---- activation chunks of groups [g0, g1), columns [0, NCOL): LDS chunk
+    // (o, n) = X chunk (16 g0 + o, n) at (o NCOL + n) * 16.  Wave w issues
+    // instructions j = w, w + 4, ...; instruction j fills chunks
+    // [64 j, 64 j + 64).  Columns past N re-read column N - 1.
+    {
+        const i32x4 xres = raw_rsrc(a.xp + (int64_t)g0 * 16 * N * 8, (int64_t)ng * 16 * N * 16);
+        const int nins = ng * 16 * NCOL / 64;
+        for (int j = wave; j < nins; j += 4) {
+            const int c = 64 * j + lane;
+            const int o = c / NCOL, n = c % NCOL;
+            const int64_t nn = n < N ? n : N - 1;
+            buffer_load_lds16(xres, xs + 64 * j * 16, (int)((o * N + nn) * 16), 0);
+        }
+    }
+
+    // ---- weights of this lane: rows row0 + 16 (kRB wave + rb) + r16 (clamped
+    // to the last row), words 4 kq .. 4 kq + 3 of each group
+    const int64_t rows_left = M - row0;
+    const int tile_rows = (int)(rows_left < kNarrowBM ? rows_left : kNarrowBM);
+    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(a.qpk + row0 * KW, (int64_t)tile_rows * KW * 4);
+    int woff[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        int r = 16 * (kRB * wave + rb) + r16;
+        r = r < tile_rows ? r : tile_rows - 1;
+        woff[rb] = (int)((r * KW + 4 * kq) * 4);
+    }
+
+    // ---- scales and zero words of the tile's rows and groups, staged in LDS
+    // once ([group][row] halves and [word][row] words, so that the 16 rows a
+    // lane group reads are consecutive): one instruction per stage would
+    // otherwise touch 16 cache lines for 2 or 4 bytes each.  Thread t takes
+    // row t % BM and every TPR-th group / word from t / BM on; the loads are
+    // unconditional (clamped) and issued before the weight prefetch, the LDS
+    // stores after it.
+    constexpr int TPR = 256 / kNarrowBM;     // threads per row
+    constexpr int SMAX = 16, ZMAX = 3;       // loads per thread (ngmax <= 16 TPR)
+    const int ngmax = (G + splitk - 1) / splitk;
+    const int zw0 = g0 >> 3, nzw = ((g1 - 1) >> 3) - zw0 + 1;
+    uint16_t* sl = reinterpret_cast<uint16_t*>(xs + (size_t)ngmax * 16 * NCOL * 16);
+    uint32_t* zl = reinterpret_cast<uint32_t*>(sl + (size_t)ngmax * kNarrowBM);
+    const int sr_row = tid % kNarrowBM, sr_g = tid / kNarrowBM;
+    const int sr_rc = sr_row < tile_rows ? sr_row : tile_rows - 1;
+    const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(a.scales + row0 * G, (int64_t)tile_rows * G * 2);
+    const __amdgpu_buffer_rsrc_t zres = buffer_rsrc(a.zpk + row0 * a.ZW, (int64_t)tile_rows * a.ZW * 4);
+    uint32_t sv[SMAX], zv[ZMAX];
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        int g = sr_g + TPR * j;
+        g = g < ng ? g : ng - 1;
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, (sr_rc * G + g0 + g) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < ZMAX; ++j) {
+        int w = sr_g + TPR * j;
+        w = w < nzw ? w : nzw - 1;
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b32(zres, (sr_rc * a.ZW + zw0 + w) * 4, 0, 0);
+    }
+
+    // ring of PF stages of packed words
+    u32x4 wr[PF][kRB];
+    auto load = [&](int slot, int g) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+            wr[slot][rb] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, 0);
+    };
+    // groups past the range reload the last one (no branch around loads),
+    // slot by slot in the order the loop refills them, so that the wait
+    // counts at the top of a round are the same on entry and on repeat
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        load(p, g0 + (p < ng ? p : ng - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sr_row < tile_rows) {
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j)
+            if (sr_g + TPR * j < ng) sl[(sr_g + TPR * j) * kNarrowBM + sr_row] = (uint16_t)sv[j];
+#pragma unroll
+        for (int j = 0; j < ZMAX; ++j)
+            if (sr_g + TPR * j < nzw) zl[(sr_g + TPR * j) * kNarrowBM + sr_row] = zv[j];
+    }
+    // the activation copies were issued before the scale, zero and these
+    // PF * WLOADS weight loads
+    wait_vmcnt<PF * WLOADS>();
+    __syncthreads();
+
+    floatx4 acc[kRB][NC];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    Dequant dq[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) dq[rb].init();
+
+    // activation fragment of MFMA step t, block cb, local group s: chunk
+    // (16 s + 4 kq + t, 16 cb + r16)
+    const unsigned char* xl = xs + ((4 * kq) * NCOL + r16) * 16;
+
+    auto stage = [&](int p, int s) {
+        const int g = g0 + s;
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            const int r = 16 * (kRB * wave + rb) + r16;
+            const uint32_t zw = zl[((g >> 3) - zw0) * kNarrowBM + r];
+            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[s * kNarrowBM + r]);
+        }
+        const unsigned char* xg = xl + s * 16 * NCOL * 16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            half8 xf[NC];
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) xf[cb] = *reinterpret_cast<const half8*>(xg + (t * NCOL + 16 * cb) * 16);
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+                const half8 wf = dq[rb](wr[p][rb][t]);
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[cb], wf, acc[rb][cb], 0, 0, 0);
+            }
+        }
+    };
+    // full rounds of PF groups: each slot is refilled with the group PF ahead
+    // (or the last group again) right after use, with no branch around loads
+    int s0 = 0;
+    for (; s0 + PF <= ng; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            stage(p, s0 + p);
+            const int sn = s0 + p + PF < ng ? s0 + p + PF : ng - 1;
+            load(p, g0 + sn);
+            // keep the refill here: sunk to the end of the round, it would
+            // leave nothing in flight at the start of the next one
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the last ng % PF groups are already in their slots
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p)
+        if (s0 + p < ng) stage(p, s0 + p);
+
+    // ---- epilogue: lane holds row 16 (kRB wave + rb) + r16 and columns
+    // 16 cb + 4 kq .. + 3
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int64_t row = row0 + 16 * (kRB * wave + rb) + r16;
+        if (row >= M) continue;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+            const int64_t col = 16 * cb + 4 * kq;
+            if (col >= N) continue;
+            if (splitk == 1) {
+                if (col + 4 <= N && (N & 3) == 0) {
+                    uint2 v;
+                    v.x = f32_to_h16_bits(acc[rb][cb][0]) | (f32_to_h16_bits(acc[rb][cb][1]) << 16);
+                    v.y = f32_to_h16_bits(acc[rb][cb][2]) | (f32_to_h16_bits(acc[rb][cb][3]) << 16);
+                    *reinterpret_cast<uint2*>(a.c + row * N + col) = v;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (col + j < N) a.c[row * N + col + j] = (uint16_t)f32_to_h16_bits(acc[rb][cb][j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (col + j < N)
+                        __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col + j, acc[rb][cb][j],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (splitk == 1) return;
+
+    // ---- split-K: the last workgroup of a row tile sums the partials in
+    // order (agent-coherent accesses; every store done before the counter
+    // moves, so no cache flush is needed)
+    int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * kNarrowBM);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == (unsigned)(splitk - 1);
+        if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
+    const int64_t total = (int64_t)tile_rows * N;
+    for (int64_t e = tid; e < total; e += 256) {
+        const int64_t row = row0 + e / N;
+        const int64_t col = e % N;
+        float v = 0.f;
+        for (int s = 0; s < splitk; ++s)
+            v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        a.c[row * N + col] = (uint16_t)f32_to_h16_bits(v);
+    }
+}
+
+template <int NC, int PF, int RB>
+hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    dim3 grid((unsigned)((a.M + 64 * RB - 1) / (64 * RB)), (unsigned)s.splitk);
+    const size_t lds = narrow_lds_bytes(a, s);
+    // allow up to 160 KB of dynamic LDS, once per kernel; a refusal is kept
+    // here (and cleared from the runtime's last error) and reported only to
+    // a launch that needs more than the default 64 KB
+    static const hipError_t lds_ok = [] {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kNarrowMaxLds);
+        if (e != hipSuccess) (void)hipGetLastError();
+        return e;
+    }();
+    if (lds_ok != hipSuccess && lds > 65536) return lds_ok;
+    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB>), grid, dim3(256), lds, stream, a, s.splitk);
+    return hipGetLastError();
+}
+
+template <int NC, int RB>
+hipError_t launch_pf(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    switch (s.pf) {
+        case 8: return launch_nc<NC, 8, RB>(a, s, stream);
+        case 16: return launch_nc<NC, 16, RB>(a, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int NC>
+hipError_t launch_rb(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    return s.rb == 1 ? launch_pf<NC, 1>(a, s, stream) : launch_pf<NC, 2>(a, s, stream);
+}
+
+}  // namespace
+
+size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
+    const int64_t ngmax = (a.G + s.splitk - 1) / s.splitk;
+    const int64_t bm = 64 * s.rb;
+    return (size_t)ngmax * 16 * s.ncol * 16          // activation chunks
+           + (size_t)ngmax * bm * 2                  // scales
+           + (size_t)((ngmax + 15) / 8) * bm * 4     // zero words (a range of ngmax groups spans at most this many)
+           + 16;                                     // split-K flag
+}
+
+bool narrow_supported(const NarrowShape& s) {
+    return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 8 || s.pf == 16) &&
+           (s.rb == 1 || s.rb == 2) && s.splitk >= 1;
+}
+
+const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
+    if (!narrow_supported(s)) return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2";
+    if (a.N > s.ncol) return "N exceeds the plan's columns";
+    if (s.splitk > a.G) return "splitk exceeds the number of groups";
+    if ((a.G + s.splitk - 1) / s.splitk > 16 * (256 / (64 * s.rb)))
+        return "more than 32 (rb 2) or 64 (rb 1) groups per workgroup; raise splitk";
+    if (narrow_lds_bytes(a, s) > (size_t)kNarrowMaxLds)
+        return "the workgroup's activation chunks exceed 160 KB of LDS; raise splitk";
+    // 32-bit buffer offsets over the activation chunks and a 128-row weight tile
+    if (a.K * a.N * 2 >= ((int64_t)1 << 31)) return "K * N too large";
+    if (a.K > ((int64_t)1 << 24)) return "K above 2^24";
+    return nullptr;
+}
+
+int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s) { return (a.M + 64 * s.rb - 1) / (64 * s.rb); }
+
+hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    hipError_t e = launch_xpack(a, stream);
+    if (e != hipSuccess) return e;
+    switch (s.ncol) {
+        case 16: return launch_rb<1>(a, s, stream);
+        case 32: return launch_rb<2>(a, s, stream);
+        case 64: return launch_rb<4>(a, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4a16

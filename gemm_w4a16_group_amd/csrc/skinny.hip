@@ -520,9 +520,12 @@ hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, const SkinnyParam
     dim3 grid((unsigned)((a.M + P.rows - 1) / P.rows), (unsigned)s.splitk);
     dim3 block((unsigned)(64 * s.wm * s.wk));
     // dynamic LDS above 64 KB must be allowed per kernel, once
-    static const hipError_t lds_ok = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&skinny_kernel<NT, PF>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)kMaxLds);
+    static const hipError_t lds_ok = [] {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<NT, PF>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+        if (e != hipSuccess) (void)hipGetLastError();   // keep a refusal out of later launches' status
+        return e;
+    }();
     if (lds_ok != hipSuccess && P.total > 65536) return lds_ok;
     hipLaunchKernelGGL((skinny_kernel<NT, PF>), grid, block, P.total, stream, a, P);
     return hipGetLastError();

@@ -26,39 +26,6 @@ namespace {
 
 constexpr int kStageRows = kGroup / 8;   // k-octets per stage
 
-// (w & mask) | bias in one instruction (the bias lives in a vector register
-// so that the instruction needs only one scalar operand).
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bias) {
-    uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(mask), "v"(bias));
-    return d;
-}
-
-// Eight fp16 weights (q - z) * s of one packed word, in the k order
-// 0, 4, 1, 5, 2, 6, 3, 7.  Nibbles at bits 0-3 of a half are OR-ed into
-// fp16 1024 (ulp 1), nibbles at bits 4-7 into fp16 64 (ulp 1/16); the
-// differences with 1024 + z and 64 + z are the exact integers q - z.
-struct Dequant {
-    uint32_t b1024, b64;     // fp16 1024 / 64 in both halves (vector registers)
-    half2v z1024, z64, s2;   // per row and group
-    __device__ __forceinline__ half8 operator()(uint32_t w) const {
-        const uint32_t w8 = w >> 8;
-        const half2v p0 = (as_h2(and_or(w, 0x000F000Fu, b1024)) - z1024) * s2;
-        const half2v p1 = (as_h2(and_or(w, 0x00F000F0u, b64)) - z64) * s2;
-        const half2v p2 = (as_h2(and_or(w8, 0x000F000Fu, b1024)) - z1024) * s2;
-        const half2v p3 = (as_h2(and_or(w8, 0x00F000F0u, b64)) - z64) * s2;
-        half8 r;
-        r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-        r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-        return r;
-    }
-    __device__ __forceinline__ void set(uint32_t z, uint32_t sbits) {
-        z1024 = as_h2(0x64006400u | z | (z << 16));
-        z64 = as_h2(0x54005400u | (z << 4) | (z << 20));
-        s2 = as_h2(sbits | (sbits << 16));
-    }
-};
-
 // ---------------------------------------------------------------------------
 // X [K, N] -> chunks [K/8][N] of 16 bytes.  One thread per (k-octet, column
 // octet): eight 16-byte row loads (or element loads when N % 8 != 0),
@@ -216,10 +183,7 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
 
     Dequant dq[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-        dq[rb].b1024 = 0x64006400u;
-        dq[rb].b64 = 0x54005400u;
-    }
+    for (int rb = 0; rb < RBW; ++rb) dq[rb].init();
     // B fragment of lane (l32, hh), block cb, MFMA step t: chunk row 8 hh + t,
     // column WN wave_n + 32 cb + l32 -> one base plus an immediate offset
     const int bbase = ((8 * hh) * BN + WN * wave_n + l32) * 16;

@@ -89,8 +89,10 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  * w4a16_plan_default(); tests and tuning may pass their own.
  *   kernel : W4A16_KERNEL_SKINNY (N <= 8, 16 or 32: weights streamed once,
  *            products on 16x16x32 fp16 MFMA, activations staged per wave in
- *            LDS) or W4A16_KERNEL_TILED (tiles of BM x BN outputs, 32x32x16
- *            fp16 MFMA; any N).
+ *            LDS), W4A16_KERNEL_NARROW (N <= 64: weights streamed once
+ *            through a register ring, activations staged once per
+ *            workgroup, 16x16x32 fp16 MFMA) or W4A16_KERNEL_TILED (tiles of
+ *            BM x BN outputs, 32x32x16 fp16 MFMA; any N).
  *   skinny : ncol = N exactly (1..8, 16 or 32); rb = 1 (16 rows per wave);
  *            wm / wk = waves per workgroup along rows / along K
  *            (wm * wk <= 16); splitk = number of workgroups sharing one row
@@ -101,10 +103,16 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            wm = waves along rows: 4 (each wave owns bm/4 rows and all
  *            bn columns) or 2 (2 x 2 waves, bn >= 128); 0 means 4;
  *            splitk as above; K <= 2^24 and N <= 2^23.
- * Skinny plans with splitk > 1 and every tiled plan need a workspace
- * (w4a16_workspace_size_plan).
+ *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
+ *            weights in flight per wave (4 or 8); 128 rows per workgroup;
+ *            splitk as above, and large enough that a workgroup's
+ *            activations, ceil(G / splitk) * 256 * ncol bytes, fit in
+ *            160 KB of LDS; K <= 2^24 and 2 K N < 2^31.
+ * Skinny plans with splitk > 1 and every tiled or narrow plan need a
+ * workspace (w4a16_workspace_size_plan).  Fields a kernel does not use are
+ * ignored.
  */
-enum { W4A16_KERNEL_SKINNY = 1, W4A16_KERNEL_TILED = 2 };
+enum { W4A16_KERNEL_SKINNY = 1, W4A16_KERNEL_TILED = 2, W4A16_KERNEL_NARROW = 3 };
 
 typedef struct {
     int32_t kernel;
@@ -115,6 +123,7 @@ typedef struct {
     int32_t bm;
     int32_t bn;
     int32_t splitk;
+    int32_t pf;
 } w4a16_plan;
 
 /* The plan w4a16_gemm uses for this shape.  Returns a status. */
@@ -122,9 +131,9 @@ int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
                        w4a16_plan *plan);
 
 /* Name of the main kernel a plan (NULL: the default plan) launches for this
- * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 8>"
- * or "tiled_kernel<256, 128, 4>" (a tiled plan also launches xpack_kernel
- * first).  Writes at most len bytes including the terminating 0 into buf.
+ * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 8>",
+ * "narrow_kernel<1, 8>" or "tiled_kernel<256, 128, 4>" (tiled and narrow
+ * plans also launch xpack_kernel first).  Writes at most len bytes including the terminating 0 into buf.
  * Returns a status; launches nothing. */
 int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size,
                       const w4a16_plan *plan, char *buf, size_t len);

@@ -110,6 +110,12 @@ def test_plan_checks(lib):
     assert gp(kernel=2, bm=128, bn=64, splitk=9) == UNSUPPORTED             # > 8 groups
     assert gp(kernel=2, bm=128, bn=64, splitk=1, wm=2) == UNSUPPORTED       # 2 x 2 needs bn >= 128
     assert gp(kernel=2, bm=128, bn=128, splitk=1, wm=3) == UNSUPPORTED
+    assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2) == WORKSPACE        # valid narrow plan
+    assert gp(kernel=3, ncol=8, pf=8, splitk=1, rb=2) == UNSUPPORTED       # 16, 32 or 64 columns
+    assert gp(kernel=3, ncol=16, pf=4, splitk=1, rb=2) == UNSUPPORTED      # ring of 8 or 16
+    assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=3) == UNSUPPORTED
+    assert gp(kernel=3, ncol=16, pf=8, splitk=9, rb=2) == UNSUPPORTED      # > 8 groups
+    assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2, N=17) == UNSUPPORTED  # N > ncol
     assert lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, 4, 1024, 128, None, NULL, 0, NULL) == INVALID
     bad = B.Plan.make(kernel=2, bm=64, bn=64, splitk=1)
     assert lib.w4a16_workspace_size_plan(64, 4, 1024, 128, ctypes.byref(bad)) == 0
@@ -124,9 +130,9 @@ def test_default_plans_are_valid(lib):
             assert lib.w4a16_plan_default(M, N, K, 128, ctypes.byref(p)) == OK
             ws = lib.w4a16_workspace_size_plan(M, N, K, 128, ctypes.byref(p))
             assert ws == lib.w4a16_gemm_workspace_size(M, N, K, 128)
-            needs = p.kernel == 2 or p.splitk > 1
+            needs = p.kernel in (2, 3) or p.splitk > 1
             assert (ws == 0) == (not needs), (M, N, K, p.as_dict())
-            if p.kernel == 2:
+            if p.kernel in (2, 3):
                 assert ws >= 65536 + K * N * 2
             # a valid plan passes every check: with fake pointers the call
             # then fails only on the workspace (if any), never on the plan
