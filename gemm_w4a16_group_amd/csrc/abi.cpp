@@ -86,7 +86,9 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
 TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm}; }
-NarrowShape narrow_of(const w4a16_plan& p) { return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb}; }
+NarrowShape narrow_of(const w4a16_plan& p) {
+    return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb, p.wk == 0 ? 1 : p.wk};
+}
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p);
 
@@ -371,7 +373,7 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     if (p.kernel == W4A16_KERNEL_SKINNY)
         snprintf(buf, len, "skinny_kernel<%d, %d>", p.ncol, skinny_pf(a, skinny_of(p)));
     else if (p.kernel == W4A16_KERNEL_NARROW)
-        snprintf(buf, len, "narrow_kernel<%d, %d, %d>", p.ncol / 16, p.pf, narrow_of(p).rb);
+        snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d>", p.ncol / 16, p.pf, narrow_of(p).rb, narrow_of(p).wk);
     else
         snprintf(buf, len, "tiled_kernel<%d, %d, %d>", p.bm, p.bn, p.wm == 0 ? 4 : p.wm);
     return ok();

@@ -33,6 +33,7 @@ struct NarrowShape {
     int pf;       // groups of weights in flight per wave: 8 or 16
     int splitk;
     int rb;       // 16-row blocks per wave: 1 or 2 (64 or 128 rows per workgroup)
+    int wk;       // waves along K per row block: 1, 2 or 4 (256 wk threads)
 };
 
 bool skinny_supported(const SkinnyShape& s);

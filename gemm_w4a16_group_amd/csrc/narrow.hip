@@ -36,10 +36,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
 }
 
-template <int NC, int PF, int kRB>
-__global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
+template <int NC, int PF, int kRB, int WK>
+__global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk) {
     constexpr int NCOL = 16 * NC;       // staged columns (N padded to 16 NC)
     constexpr int kNarrowBM = 64 * kRB; // rows per workgroup (16 kRB per wave)
+    constexpr int NT = 256 * WK;        // threads: 4 waves along M times WK along K
     constexpr int WLOADS = kRB;         // weight loads per wave and stage
     static_assert(PF * WLOADS < 64, "vmcnt range");
     // dynamic LDS: the activation chunks, then the split-K flag (all of
@@ -51,6 +52,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave & 3, wave_k = wave >> 2;
     const int r16 = lane & 15;   // weight row in a 16-row block / activation column in a 16-column block
     const int kq = lane >> 4;    // k-quarter of the 32-k MFMA step (words 4 kq .. 4 kq + 3 of a group)
 
@@ -58,17 +60,19 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     const int sidx = blockIdx.y;
     const int g0 = (int)((int64_t)G * sidx / splitk);
     const int g1 = (int)((int64_t)G * (sidx + 1) / splitk);
-    const int ng = g1 - g0;      // >= 1 since splitk <= G
+    const int ng = g1 - g0;      // >= WK since splitk <= G / WK
     const int64_t KW = K / 8;
+    // the groups of this wave: [gw0, gw0 + ngw) of the workgroup's range
+    const int gw0 = ng * wave_k / WK, ngw = ng * (wave_k + 1) / WK - gw0;
 
     // ---- activation chunks of groups [g0, g1), columns [0, NCOL): LDS chunk
     // (o, n) = X chunk (16 g0 + o, n) at (o NCOL + n) * 16.  Wave w issues
-    // instructions j = w, w + 4, ...; instruction j fills chunks
+    // instructions j = w, w + 4 WK, ...; instruction j fills chunks
     // [64 j, 64 j + 64).  Columns past N re-read column N - 1.
     {
         const i32x4 xres = raw_rsrc(a.xp + (int64_t)g0 * 16 * N * 8, (int64_t)ng * 16 * N * 16);
         const int nins = ng * 16 * NCOL / 64;
-        for (int j = wave; j < nins; j += 4) {
+        for (int j = wave; j < nins; j += 4 * WK) {
             const int c = 64 * j + lane;
             const int o = c / NCOL, n = c % NCOL;
             const int64_t nn = n < N ? n : N - 1;
@@ -84,7 +88,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     int woff[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-        int r = 16 * (kRB * wave + rb) + r16;
+        int r = 16 * (kRB * wave_m + rb) + r16;
         r = r < tile_rows ? r : tile_rows - 1;
         woff[rb] = (int)((r * KW + 4 * kq) * 4);
     }
@@ -96,7 +100,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     // row t % BM and every TPR-th group / word from t / BM on; the loads are
     // unconditional (clamped) and issued before the weight prefetch, the LDS
     // stores after it.
-    constexpr int TPR = 256 / kNarrowBM;     // threads per row
+    constexpr int TPR = NT / kNarrowBM;      // threads per row
     constexpr int SMAX = 16, ZMAX = 3;       // loads per thread (ngmax <= 16 TPR)
     const int ngmax = (G + splitk - 1) / splitk;
     const int zw0 = g0 >> 3, nzw = ((g1 - 1) >> 3) - zw0 + 1;
@@ -132,7 +136,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     // counts at the top of a round are the same on entry and on repeat
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-        load(p, g0 + (p < ng ? p : ng - 1));
+        load(p, g0 + gw0 + (p < ngw ? p : ngw - 1));
         __builtin_amdgcn_sched_barrier(0);
     }
     if (sr_row < tile_rows) {
@@ -161,15 +165,16 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     // (16 s + 4 kq + t, 16 cb + r16)
     const unsigned char* xl = xs + ((4 * kq) * NCOL + r16) * 16;
 
+    // stage s of this wave: group g0 + gw0 + s, local index gw0 + s
     auto stage = [&](int p, int s) {
-        const int g = g0 + s;
+        const int gl = gw0 + s, g = g0 + gl;
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
-            const int r = 16 * (kRB * wave + rb) + r16;
+            const int r = 16 * (kRB * wave_m + rb) + r16;
             const uint32_t zw = zl[((g >> 3) - zw0) * kNarrowBM + r];
-            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[s * kNarrowBM + r]);
+            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[gl * kNarrowBM + r]);
         }
-        const unsigned char* xg = xl + s * 16 * NCOL * 16;
+        const unsigned char* xg = xl + gl * 16 * NCOL * 16;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             half8 xf[NC];
@@ -187,28 +192,52 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     // full rounds of PF groups: each slot is refilled with the group PF ahead
     // (or the last group again) right after use, with no branch around loads
     int s0 = 0;
-    for (; s0 + PF <= ng; s0 += PF) {
+    for (; s0 + PF <= ngw; s0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             stage(p, s0 + p);
-            const int sn = s0 + p + PF < ng ? s0 + p + PF : ng - 1;
-            load(p, g0 + sn);
+            const int sn = s0 + p + PF < ngw ? s0 + p + PF : ngw - 1;
+            load(p, g0 + gw0 + sn);
             // keep the refill here: sunk to the end of the round, it would
             // leave nothing in flight at the start of the next one
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the last ng % PF groups are already in their slots
+    // the last ngw % PF groups are already in their slots
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p)
-        if (s0 + p < ng) stage(p, s0 + p);
+        if (s0 + p < ngw) stage(p, s0 + p);
+
+    // ---- waves along K meet in LDS (over the activation chunks, which
+    // every wave has finished reading): wave_k > 0 parks its sums, wave_k 0
+    // adds them in order and goes on alone
+    if (WK > 1) {
+        floatx4* red = reinterpret_cast<floatx4*>(xs);
+        __syncthreads();
+        if (wave_k > 0) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb)
+                    red[((((wave_k - 1) * 4 + wave_m) * kRB + rb) * NC + cb) * 64 + lane] = acc[rb][cb];
+        }
+        __syncthreads();
+        if (wave_k == 0) {
+            for (int k = 1; k < WK; ++k)
+#pragma unroll
+                for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < NC; ++cb)
+                        acc[rb][cb] += red[((((k - 1) * 4 + wave_m) * kRB + rb) * NC + cb) * 64 + lane];
+        }
+    }
 
     // ---- epilogue: lane holds row 16 (kRB wave + rb) + r16 and columns
     // 16 cb + 4 kq .. + 3
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-        const int64_t row = row0 + 16 * (kRB * wave + rb) + r16;
-        if (row >= M) continue;
+        const int64_t row = row0 + 16 * (kRB * wave_m + rb) + r16;
+        if (wave_k != 0 || row >= M) continue;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
             const int64_t col = 16 * cb + 4 * kq;
@@ -251,7 +280,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     __syncthreads();
     if (!*flag) return;
     const int64_t total = (int64_t)tile_rows * N;
-    for (int64_t e = tid; e < total; e += 256) {
+    for (int64_t e = tid; e < total; e += NT) {
         const int64_t row = row0 + e / N;
         const int64_t col = e % N;
         float v = 0.f;
@@ -262,7 +291,7 @@ __global__ void __launch_bounds__(256) narrow_kernel(GemmArgs a, int splitk) {
     }
 }
 
-template <int NC, int PF, int RB>
+template <int NC, int PF, int RB, int WK>
 hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     dim3 grid((unsigned)((a.M + 64 * RB - 1) / (64 * RB)), (unsigned)s.splitk);
     const size_t lds = narrow_lds_bytes(a, s);
@@ -270,28 +299,38 @@ hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream
     // here (and cleared from the runtime's last error) and reported only to
     // a launch that needs more than the default 64 KB
     static const hipError_t lds_ok = [] {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB, WK>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kNarrowMaxLds);
         if (e != hipSuccess) (void)hipGetLastError();
         return e;
     }();
     if (lds_ok != hipSuccess && lds > 65536) return lds_ok;
-    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB>), grid, dim3(256), lds, stream, a, s.splitk);
+    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB, WK>), grid, dim3(256 * WK), lds, stream, a, s.splitk);
     return hipGetLastError();
 }
 
-template <int NC, int RB>
+template <int NC, int RB, int WK>
 hipError_t launch_pf(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     switch (s.pf) {
-        case 8: return launch_nc<NC, 8, RB>(a, s, stream);
-        case 16: return launch_nc<NC, 16, RB>(a, s, stream);
+        case 8: return launch_nc<NC, 8, RB, WK>(a, s, stream);
+        case 16: return launch_nc<NC, 16, RB, WK>(a, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int NC, int RB>
+hipError_t launch_wk(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    switch (s.wk) {
+        case 1: return launch_pf<NC, RB, 1>(a, s, stream);
+        case 2: return launch_pf<NC, RB, 2>(a, s, stream);
+        case 4: return launch_pf<NC, RB, 4>(a, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int NC>
 hipError_t launch_rb(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
-    return s.rb == 1 ? launch_pf<NC, 1>(a, s, stream) : launch_pf<NC, 2>(a, s, stream);
+    return s.rb == 1 ? launch_wk<NC, 1>(a, s, stream) : launch_wk<NC, 2>(a, s, stream);
 }
 
 }  // namespace
@@ -299,7 +338,9 @@ hipError_t launch_rb(const GemmArgs& a, const NarrowShape& s, hipStream_t stream
 size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
     const int64_t ngmax = (a.G + s.splitk - 1) / s.splitk;
     const int64_t bm = 64 * s.rb;
-    return (size_t)ngmax * 16 * s.ncol * 16          // activation chunks
+    const size_t chunks = (size_t)ngmax * 16 * s.ncol * 16;                        // activation chunks
+    const size_t red = (size_t)(s.wk - 1) * 4 * s.rb * (s.ncol / 16) * 64 * 16;   // K-wave sums (reuse)
+    return (chunks > red ? chunks : red)
            + (size_t)ngmax * bm * 2                  // scales
            + (size_t)((ngmax + 15) / 8) * bm * 4     // zero words (a range of ngmax groups spans at most this many)
            + 16;                                     // split-K flag
@@ -307,15 +348,15 @@ size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
 
 bool narrow_supported(const NarrowShape& s) {
     return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 8 || s.pf == 16) &&
-           (s.rb == 1 || s.rb == 2) && s.splitk >= 1;
+           (s.rb == 1 || s.rb == 2) && (s.wk == 1 || s.wk == 2 || s.wk == 4) && s.splitk >= 1;
 }
 
 const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
-    if (!narrow_supported(s)) return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2";
+    if (!narrow_supported(s)) return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2, wk 1, 2 or 4";
     if (a.N > s.ncol) return "N exceeds the plan's columns";
-    if (s.splitk > a.G) return "splitk exceeds the number of groups";
-    if ((a.G + s.splitk - 1) / s.splitk > 16 * (256 / (64 * s.rb)))
-        return "more than 32 (rb 2) or 64 (rb 1) groups per workgroup; raise splitk";
+    if ((int64_t)s.splitk * s.wk > a.G) return "splitk * wk exceeds the number of groups";
+    if ((a.G + s.splitk - 1) / s.splitk > 16 * (256 * s.wk / (64 * s.rb)))
+        return "more than 16 * 4 wk / rb groups per workgroup; raise splitk";
     if (narrow_lds_bytes(a, s) > (size_t)kNarrowMaxLds)
         return "the workgroup's activation chunks exceed 160 KB of LDS; raise splitk";
     // 32-bit buffer offsets over the activation chunks and a 128-row weight tile

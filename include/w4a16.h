@@ -104,10 +104,13 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            bn columns) or 2 (2 x 2 waves, bn >= 128); 0 means 4;
  *            splitk as above; K <= 2^24 and N <= 2^23.
  *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
- *            weights in flight per wave (4 or 8); 128 rows per workgroup;
- *            splitk as above, and large enough that a workgroup's
- *            activations, ceil(G / splitk) * 256 * ncol bytes, fit in
- *            160 KB of LDS; K <= 2^24 and 2 K N < 2^31.
+ *            weights in flight per wave (8 or 16); rb = 16-row blocks per
+ *            wave (1 or 2: 64 or 128 rows per workgroup, 0 means 2); wk =
+ *            waves along K per row block (1, 2 or 4; 0 means 1); splitk as
+ *            above, with splitk * wk <= G, and large enough that a
+ *            workgroup's activations, ceil(G / splitk) * 256 * ncol bytes
+ *            plus its scales and zeros, fit in 160 KB of LDS;
+ *            K <= 2^24 and 2 K N < 2^31.
  * Skinny plans with splitk > 1 and every tiled or narrow plan need a
  * workspace (w4a16_workspace_size_plan).  Fields a kernel does not use are
  * ignored.

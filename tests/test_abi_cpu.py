@@ -114,6 +114,9 @@ def test_plan_checks(lib):
     assert gp(kernel=3, ncol=8, pf=8, splitk=1, rb=2) == UNSUPPORTED       # 16, 32 or 64 columns
     assert gp(kernel=3, ncol=16, pf=4, splitk=1, rb=2) == UNSUPPORTED      # ring of 8 or 16
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=3) == UNSUPPORTED
+    assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2, wk=3) == UNSUPPORTED
+    assert gp(kernel=3, ncol=16, pf=8, splitk=3, rb=2, wk=4) == UNSUPPORTED  # 12 > 8 groups
+    assert gp(kernel=3, ncol=16, pf=8, splitk=2, rb=2, wk=4) == WORKSPACE
     assert gp(kernel=3, ncol=16, pf=8, splitk=9, rb=2) == UNSUPPORTED      # > 8 groups
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2, N=17) == UNSUPPORTED  # N > ncol
     assert lib.w4a16_gemm_plan(Q, S, Z, X, C, 64, 4, 1024, 128, None, NULL, 0, NULL) == INVALID

@@ -104,36 +104,41 @@ def test_tiled_plan(case):
 
 
 NARROW = [
-    # (M, K, N, ncol, pf, splitk, rb): 64- or 128-row tiles with ragged
+    # (M, K, N, ncol, pf, splitk, rb, wk): 64- or 128-row tiles with ragged
     # tails, every column width, columns past N, fewer groups than the ring,
-    # remainders of the ring, splits
-    (1, 128, 1, 16, 8, 1, 2),
-    (100, 384, 9, 16, 8, 1, 1),
-    (129, 384, 16, 16, 16, 1, 2),
-    (300, 1152, 16, 16, 8, 1, 2),
-    (300, 1152, 13, 16, 16, 2, 1),
-    (300, 1152, 16, 16, 8, 9, 2),
-    (257, 4096, 16, 16, 8, 1, 2),
-    (257, 4096, 11, 16, 16, 3, 1),
-    (200, 640, 32, 32, 8, 1, 1),
-    (200, 640, 17, 32, 16, 2, 2),
-    (131, 1152, 31, 32, 8, 3, 2),
-    (64, 11008, 32, 32, 8, 5, 1),
-    (250, 1152, 64, 64, 8, 1, 2),
-    (250, 1152, 33, 64, 16, 2, 1),
-    (130, 2048, 64, 64, 8, 4, 2),
-    (129, 1152, 3, 64, 16, 1, 1),
-    (70, 5120, 20, 32, 16, 3, 1),
+    # remainders of the ring, splits across workgroups and across waves
+    (1, 128, 1, 16, 8, 1, 2, 1),
+    (100, 384, 9, 16, 8, 1, 1, 1),
+    (129, 384, 16, 16, 16, 1, 2, 1),
+    (300, 1152, 16, 16, 8, 1, 2, 1),
+    (300, 1152, 13, 16, 16, 2, 1, 1),
+    (300, 1152, 16, 16, 8, 9, 2, 1),
+    (257, 4096, 16, 16, 8, 1, 2, 1),
+    (257, 4096, 11, 16, 16, 3, 1, 1),
+    (200, 640, 32, 32, 8, 1, 1, 1),
+    (200, 640, 17, 32, 16, 2, 2, 1),
+    (131, 1152, 31, 32, 8, 3, 2, 1),
+    (64, 11008, 32, 32, 8, 5, 1, 1),
+    (250, 1152, 64, 64, 8, 1, 2, 1),
+    (250, 1152, 33, 64, 16, 2, 1, 1),
+    (130, 2048, 64, 64, 8, 4, 2, 1),
+    (129, 1152, 3, 64, 16, 1, 1, 1),
+    (70, 5120, 20, 32, 16, 3, 1, 1),
+    (300, 4096, 16, 16, 8, 1, 1, 2),
+    (300, 4096, 16, 16, 8, 1, 1, 4),
+    (190, 1152, 9, 16, 8, 2, 2, 4),
+    (129, 11008, 24, 32, 8, 6, 1, 2),
+    (77, 384, 64, 64, 8, 1, 2, 2),
 ]
 
 
-@pytest.mark.parametrize("case", NARROW, ids=lambda c: "M%d_K%d_N%d_c%d_pf%d_s%d_rb%d" % c)
+@pytest.mark.parametrize("case", NARROW, ids=lambda c: "M%d_K%d_N%d_c%d_pf%d_s%d_rb%d_wk%d" % c)
 def test_narrow_plan(case):
-    M, K, N, ncol, pf, splitk, rb = case
+    M, K, N, ncol, pf, splitk, rb, wk = case
     log("narrow %s" % (case,))
     p = prob(M, K)
     X = X_for(K, N)
-    plan = B.Plan.make(kernel=B.KERNEL_NARROW, ncol=ncol, pf=pf, splitk=splitk, rb=rb)
+    plan = B.Plan.make(kernel=B.KERNEL_NARROW, ncol=ncol, pf=pf, splitk=splitk, rb=rb, wk=wk)
     C = run(p, X, plan=plan)
     C_ref, A_ref = p.reference(X)
     assert_parity(C, C_ref, A_ref, str(case))
@@ -169,7 +174,8 @@ def test_repeatable_bitwise():
     for N, plan in [(1, None), (16, None), (200, None),
                     (8, B.Plan.make(kernel=1, ncol=8, rb=1, wm=2, wk=2, splitk=3)),
                     (264, B.Plan.make(kernel=2, bm=128, bn=256, splitk=2)),
-                    (30, B.Plan.make(kernel=3, ncol=32, pf=8, splitk=3, rb=2))]:
+                    (30, B.Plan.make(kernel=3, ncol=32, pf=8, splitk=3, rb=2, wk=1)),
+                    (12, B.Plan.make(kernel=3, ncol=16, pf=8, splitk=1, rb=1, wk=4))]:
         X = X_for(K, N, seed=3)
         a = run(p, X, plan=plan)
         b = run(p, X, plan=plan)
