@@ -84,7 +84,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=40, help="weight copies cycled through (cold cache)")
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
-                             "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib"])
+                             "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
+                             "quantize_12288x4096"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -303,6 +304,28 @@ def extra(args):
         return
     if args.workload == "gemm_12288x4096_n4096":
         print(json.dumps(gemm_secondary(args.gemm_iters)), flush=True)
+        return
+    if args.workload == "quantize_12288x4096":
+        # fp16 weights -> packed codes, scales, packed zeros; 4 copies of the
+        # 100 MB input cycled through (400 MB, past the last-level cache)
+        M, K = 12288, 4096
+        G = K // GROUP
+        w0 = torch.from_numpy(inputs.fp16_weights(M, K, wid=6)).cuda()
+        ws = [w0] + [w0.clone() for _ in range(3)]
+        outs = [B.quantize(w) for w in ws]
+        calls = [(lambda w=w, o=o: B.lib().w4a16_quantize(
+            w.data_ptr(), M, K, GROUP, o[0].data_ptr(), o[1].data_ptr(), o[2].data_ptr(),
+            torch.cuda.current_stream().cuda_stream)) for w, o in zip(ws, outs)]
+        stream = torch.cuda.Stream()
+        g = capture(calls, stream)
+        time_graph(g, 5, stream)
+        reps = 50
+        ms = time_graph(g, reps, stream) / (reps * len(calls))
+        b = 2 * M * K + M * K // 2 + 2 * M * G + M * G // 2
+        print(json.dumps({"workload": "quantize_12288x4096", "us": round(ms * 1e3, 3), "bytes_per_call": b,
+                          "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "kernel": "quantize_kernel"}), flush=True)
         return
     if args.workload == "gemv_4096x4096":
         ms, plan, steps, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup)

@@ -78,6 +78,8 @@ def load_library(path=None):
         lib.w4a16_workspace_size_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
         lib.w4a16_gemm_workspace_size.restype = sz
         lib.w4a16_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.w4a16_quantize.restype = ctypes.c_int
+        lib.w4a16_quantize.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
         lib.w4a16_kernel_name.restype = ctypes.c_int
         lib.w4a16_kernel_name.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan), ctypes.c_char_p,
                                           ctypes.c_size_t]
@@ -150,6 +152,20 @@ def pack(q=None, z=None):
     zpk = torch.empty((M, (G + 7) // 8), dtype=torch.int32, device=ref.device) if z is not None else None
     _check(lib().w4a16_pack(_p(q), _p(z), M, K, GROUP, _p(qpk), _p(zpk), _stream()))
     return qpk, zpk
+
+
+def quantize(w):
+    """Round-to-nearest group quantization on the GPU: fp16 w [M, K] ->
+    (q_packed int32 [M, K/8], scales fp16 [M, K/128], z_packed int32
+    [M, ceil(G/8)]), ready for gemm()."""
+    _need(w, "w", torch.float16)
+    M, K = w.shape
+    G = K // GROUP
+    qpk = torch.empty((M, K // 8), dtype=torch.int32, device=w.device)
+    s = torch.empty((M, G), dtype=torch.float16, device=w.device)
+    zpk = torch.empty((M, (G + 7) // 8), dtype=torch.int32, device=w.device)
+    _check(lib().w4a16_quantize(_p(w), M, K, GROUP, _p(qpk), _p(s), _p(zpk), _stream()))
+    return qpk, s, zpk
 
 
 def _dims(qpk, s, zpk, x):

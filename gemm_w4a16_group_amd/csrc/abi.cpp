@@ -339,6 +339,26 @@ int w4a16_pack(const uint8_t* q, const uint8_t* z, int64_t M, int64_t K, int32_t
     return ok();
 }
 
+int w4a16_quantize(const void* w, int64_t M, int64_t K, int32_t group_size, uint32_t* q_packed, void* scales,
+                   uint32_t* z_packed, void* stream) {
+    int st = check_dims(M, 1, K, group_size);
+    if (st) return st;
+    if (!w || !q_packed || !scales || !z_packed) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(w) || !aligned16(q_packed) || !aligned16(scales) || !aligned16(z_packed))
+        return fail(W4A16_ERR_MISALIGNED, "every pointer must be 16-byte aligned");
+    const int64_t G = groups_of(K);
+    const size_t nw = (size_t)M * K * 2, nq = (size_t)M * (K / 8) * 4, ns = (size_t)M * G * 2,
+                 nz = (size_t)M * zwords_of(K) * 4;
+    if (overlaps(q_packed, nq, w, nw) || overlaps(scales, ns, w, nw) || overlaps(z_packed, nz, w, nw) ||
+        overlaps(q_packed, nq, scales, ns) || overlaps(q_packed, nq, z_packed, nz) ||
+        overlaps(scales, ns, z_packed, nz))
+        return fail(W4A16_ERR_INVALID_ARG, "the outputs overlap each other or the input");
+    hipError_t e = launch_quantize(static_cast<const uint16_t*>(w), q_packed, static_cast<uint16_t*>(scales),
+                                   z_packed, M, K, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size, w4a16_plan* plan) {
     int st = check_dims(M, N, K, group_size);
     if (st) return st;

@@ -60,6 +60,10 @@ hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t st
 // X [K, N] -> 16-byte chunks [K/8][N] in a.xp (the tiled and narrow kernels' B/A operand layout)
 hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream);
 
+// fp16 W [M, K] -> q_packed, fp16 scales, z_packed (round to nearest per group)
+hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,
+                           hipStream_t stream);
+
 hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,
                             hipStream_t stream);
 

@@ -99,3 +99,15 @@ def fp16_weights(M, K, seed):
     """Unquantized fp16 weights ~ N(0, 0.02^2), for the quantizer's tests."""
     rng = np.random.default_rng([seed, 7])
     return (0.02 * rng.standard_normal((M, K))).astype(np.float16)
+
+
+def fp16_weights(M, K, wid=0, layer=0, proj=0, sigma=0.02, outliers=1e-3):
+    """Unquantized weights for the quantizer, fp16 [M, K]: normal with
+    standard deviation sigma (drawn in float32, rounded to fp16), a fraction
+    `outliers` of them scaled by 20 (the heavy tail of trained linears).
+    Stream 2 of the weight seed, so it is independent of the code draws."""
+    rng = np.random.default_rng([wid, layer, proj, 2])
+    w = rng.standard_normal((M, K), dtype=np.float32) * np.float32(sigma)
+    mask = rng.random((M, K)) < outliers
+    w[mask] *= np.float32(20.0)
+    return w.astype(np.float16)

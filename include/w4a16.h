@@ -64,6 +64,28 @@ const char *w4a16_last_error(void);
 int w4a16_version(void);
 
 /*
+ * Round-to-nearest group quantizer: the step that produces the layer's
+ * weights (PerfXLLM §3.1: weights only, int4, group size 128, a scale and a
+ * zero per group), in its plain min/max form (AWQ's activation-aware scale
+ * search is not part of it).  Per row m and group g of 128 k, in float32
+ * with correctly rounded divides and round-half-to-even:
+ *   lo = min(min_k w, 0), hi = max(max_k w, 0)
+ *   s  = fp16(max(hi - lo, 1e-5) / 15)
+ *   z  = clamp(rint(-lo / s), 0, 15)
+ *   q  = clamp(rint(w / s) + z, 0, 15)
+ *   w        : fp16 [M, K] row-major, finite values (NaN handling unspecified)
+ *   q_packed : out, [M, K / 8] words, as w4a16_pack writes them
+ *   scales   : out, fp16 [M, G]
+ *   z_packed : out, [M, ceil(G / 8)] words (padding nibbles 0)
+ * Requires M >= 1, K >= 128, K % 128 == 0, group_size == 128, 16-byte
+ * aligned pointers and outputs that overlap neither each other nor w.
+ * Bit-exact: the result is a pure function of w.  Work goes on stream.
+ */
+int w4a16_quantize(const void *w, int64_t M, int64_t K, int32_t group_size,
+                   uint32_t *q_packed, void *scales, uint32_t *z_packed,
+                   void *stream);
+
+/*
  * Pack 4-bit codes into the storage format above (PerfXLLM §3.1 storage).
  *   q : uint8 [M, K] weight codes, or NULL to pack zeros only
  *   z : uint8 [M, K / group_size] zero codes, or NULL to pack weights only

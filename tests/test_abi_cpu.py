@@ -179,3 +179,14 @@ def test_kernel_name_follows_the_plan(lib):
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, buf, 8) == OK           # truncated
     assert buf.value == b"skinny_"
+
+
+def test_quantize_argument_checks(lib):
+    w, q, s, z = (ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(4))
+    assert lib.w4a16_quantize(w, 64, 1024, 64, q, s, z, NULL) == UNSUPPORTED     # group size
+    assert lib.w4a16_quantize(w, 64, 1000, 128, q, s, z, NULL) == INVALID       # K % 128
+    assert lib.w4a16_quantize(NULL, 64, 1024, 128, q, s, z, NULL) == INVALID
+    assert lib.w4a16_quantize(w, 64, 1024, 128, ctypes.c_void_p(0x20000008), s, z, NULL) == MISALIGNED
+    # packed codes on top of the input
+    assert lib.w4a16_quantize(w, 64, 1024, 128, ctypes.c_void_p(0x10000000 + 4096), s, z, NULL) == INVALID
+    assert b"overlap" in lib.w4a16_last_error()
