@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--token", action="store_true",
+                    help="small_n / large_n: token-major x [N, K] and c [N, M]")
     return ap.parse_args()
 
 
@@ -341,18 +343,22 @@ def extra(args):
         M, K = 12288, 4096
         cps = 40
         lay = Layer(M, K, wid, copies=cps)
+        layout = B.LAYOUT_TOKEN if args.token else B.LAYOUT_KN
         for N in Ns:
-            x = torch.from_numpy(inputs.activations(K, N, wid=wid)).cuda()
-            outs = [torch.empty((M, N), dtype=torch.float16, device="cuda") for _ in range(cps)]
+            xh = inputs.activations(K, N, wid=wid)
+            x = torch.from_numpy(xh.T.copy() if args.token else xh).cuda()
+            shape = (N, M) if args.token else (M, N)
+            outs = [torch.empty(shape, dtype=torch.float16, device="cuda") for _ in range(cps)]
             ncalls = cps if N <= 256 else 4
-            calls = [(lambda c=c, o=o: B.gemm(c[0], c[1], c[2], x, out=o))
+            calls = [(lambda c=c, o=o: B.gemm(c[0], c[1], c[2], x, out=o, layout=layout))
                      for c, o in zip(lay.copies[:ncalls], outs[:ncalls])]
             stream = torch.cuda.Stream()
             g = capture(calls, stream)
             reps = max(2, (args.steps // ncalls) if N <= 256 else 5)
             time_graph(g, 2, stream)
             ms = time_graph(g, reps, stream) / (reps * ncalls)
-            rows.append(("12288x4096", M, K, N, ms, B.plan_default(M, N, K).as_dict()))
+            rows.append(("12288x4096" + ("_token" if args.token else ""), M, K, N, ms,
+                         B.plan_default(M, N, K, layout).as_dict()))
     elif args.workload == "stack":
         for N in (1, 16):
             mats = []

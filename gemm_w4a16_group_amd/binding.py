@@ -22,6 +22,8 @@ GROUP = 128
 KERNEL_SKINNY = 1
 KERNEL_TILED = 2
 KERNEL_NARROW = 3
+LAYOUT_KN = 0      # x [K, N], c [M, N]
+LAYOUT_TOKEN = 1   # x [N, K], c [N, M]
 
 _lib = None
 _lock = threading.Lock()
@@ -88,6 +90,13 @@ def load_library(path=None):
         lib.w4a16_gemm_plan.restype = ctypes.c_int
         lib.w4a16_gemm_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32,
                                         ctypes.POINTER(Plan), vp, sz, vp]
+        lib.w4a16_gemm_ex.restype = ctypes.c_int
+        lib.w4a16_gemm_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                      ctypes.POINTER(Plan), vp, sz, vp]
+        lib.w4a16_plan_default_ex.restype = ctypes.c_int
+        lib.w4a16_plan_default_ex.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan)]
+        lib.w4a16_workspace_size_ex.restype = sz
+        lib.w4a16_workspace_size_ex.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan)]
         if path is None:
             _lib = lib
         return lib
@@ -168,7 +177,7 @@ def quantize(w):
     return qpk, s, zpk
 
 
-def _dims(qpk, s, zpk, x):
+def _dims(qpk, s, zpk, x, layout=LAYOUT_KN):
     _need(qpk, "q_packed", torch.int32)
     M, KW = qpk.shape
     K = KW * 8
@@ -178,17 +187,25 @@ def _dims(qpk, s, zpk, x):
     if x.dim() == 1:
         _need(x, "x", torch.float16, (K,))
         N = 1
+    elif layout == LAYOUT_TOKEN:
+        _need(x, "x", torch.float16)
+        if x.dim() != 2 or x.shape[1] != K:
+            raise ValueError("x must be [N, K=%d], got %s" % (K, tuple(x.shape)))
+        N = x.shape[0]
     else:
         _need(x, "x", torch.float16)
-        if x.shape[0] != K:
+        if x.dim() != 2 or x.shape[0] != K:
             raise ValueError("x must be [K=%d, N], got %s" % (K, tuple(x.shape)))
         N = x.shape[1]
     return M, N, K
 
 
-def plan_default(M, N, K):
+def plan_default(M, N, K, layout=LAYOUT_KN):
     p = Plan()
-    _check(lib().w4a16_plan_default(M, N, K, GROUP, ctypes.byref(p)))
+    if layout == LAYOUT_KN:
+        _check(lib().w4a16_plan_default(M, N, K, GROUP, ctypes.byref(p)))
+    else:
+        _check(lib().w4a16_plan_default_ex(M, N, K, GROUP, layout, ctypes.byref(p)))
     return p
 
 
@@ -199,7 +216,10 @@ def kernel_name(M, N, K, plan=None):
     return buf.value.decode()
 
 
-def workspace_size(M, N, K, plan=None):
+def workspace_size(M, N, K, plan=None, layout=LAYOUT_KN):
+    if layout != LAYOUT_KN:
+        return int(lib().w4a16_workspace_size_ex(M, N, K, GROUP, layout,
+                                                 None if plan is None else ctypes.byref(plan)))
     if plan is None:
         return int(lib().w4a16_gemm_workspace_size(M, N, K, GROUP))
     return int(lib().w4a16_workspace_size_plan(M, N, K, GROUP, ctypes.byref(plan)))
@@ -247,16 +267,21 @@ def gemv(qpk, s, zpk, x, out=None):
     return out
 
 
-def gemm(qpk, s, zpk, x, out=None, plan=None, workspace=None):
-    """c[M, N] = Wdeq[M, K] . x[K, N] with the library's dispatch (or a plan)."""
-    M, N, K = _dims(qpk, s, zpk, x)
+def gemm(qpk, s, zpk, x, out=None, plan=None, workspace=None, layout=LAYOUT_KN):
+    """c[M, N] = Wdeq[M, K] . x[K, N] with the library's dispatch (or a plan).
+    With layout=LAYOUT_TOKEN, x is [N, K] and the result [N, M]
+    (c = x . Wdeq^T, one row per token)."""
+    if layout not in (LAYOUT_KN, LAYOUT_TOKEN):
+        raise ValueError("unknown layout %r" % (layout,))
+    M, N, K = _dims(qpk, s, zpk, x, layout)
+    shape = (N, M) if layout == LAYOUT_TOKEN else (M, N)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+        out = torch.empty(shape, dtype=torch.float16, device=x.device)
     else:
         _need(out, "out", torch.float16)
         if out.numel() != M * N:
             raise ValueError("out must hold M*N=%d values" % (M * N))
-    need = workspace_size(M, N, K, plan)
+    need = workspace_size(M, N, K, plan, layout)
     if plan is not None and need == 0:
         # invalid plans report size 0; let the library say why
         need = 0
@@ -267,7 +292,10 @@ def gemm(qpk, s, zpk, x, out=None, plan=None, workspace=None):
         else:
             ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    if plan is None:
+    if layout != LAYOUT_KN:
+        _check(lib().w4a16_gemm_ex(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP, layout,
+                                   None if plan is None else ctypes.byref(plan), _p(ws), ws_bytes, _stream()))
+    elif plan is None:
         _check(lib().w4a16_gemm(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP,
                                 _p(ws), ws_bytes, _stream()))
     else:

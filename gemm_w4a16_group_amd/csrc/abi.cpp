@@ -73,9 +73,10 @@ int64_t zwords_of(int64_t K) { return (groups_of(K) + 7) / 8; }
 
 bool skinny_columns(int64_t N) { return (N >= 1 && N <= 8) || N == 16 || N == 32; }
 
-GemmArgs make_args(int64_t M, int64_t N, int64_t K) {
+GemmArgs make_args(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_LAYOUT_KN) {
     GemmArgs a;
     memset(&a, 0, sizeof(a));
+    a.tm = layout == W4A16_LAYOUT_TOKEN ? 1 : 0;
     a.M = M;
     a.N = N;
     a.K = K;
@@ -107,11 +108,15 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // N = 512, 128 x 64 below; a split along K only when there are too few
 // tiles to fill the chip (N <= 32: two-way, four-way under 64 tiles; larger
 // N: two-way for long rows, K >= 8192).
-w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
+//
+// Token-major layout: the same choice, except that the skinny kernel takes
+// token-major activations only up to N = 8 (N = 16 and 32 go to the narrow
+// or tiled kernel).
+w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_LAYOUT_KN) {
     w4a16_plan p;
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
-    const GemmArgs a = make_args(M, N, K);
+    const GemmArgs a = make_args(M, N, K, layout);
     // narrow kernel for 8 <= N <= 32: 64 rows per workgroup, a ring of 8
     // groups per wave, the smallest split whose activations fit in LDS
     if (N >= 8 && N <= 32) {
@@ -129,7 +134,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K) {
         memset(&p, 0, sizeof(p));
     }
     const bool small = M * K < ((int64_t)1 << 25);
-    if (N < 8 || (skinny_columns(N) && small)) {
+    if (N < 8 || (!a.tm && skinny_columns(N) && small)) {
         p.kernel = W4A16_KERNEL_SKINNY;
         p.ncol = (int32_t)N;
         p.rb = 1;
@@ -240,10 +245,18 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p) {
     return fail(W4A16_ERR_UNSUPPORTED, "unknown kernel id %d", p.kernel);
 }
 
+int check_layout(int32_t layout) {
+    if (layout != W4A16_LAYOUT_KN && layout != W4A16_LAYOUT_TOKEN)
+        return fail(W4A16_ERR_INVALID_ARG, "unknown layout %d", layout);
+    return W4A16_OK;
+}
+
 int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, void* c,
-             int64_t M, int64_t N, int64_t K, int32_t group_size, const w4a16_plan* plan_in,
+             int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, const w4a16_plan* plan_in,
              void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    st = check_layout(layout);
     if (st) return st;
     if (!qpk || !scales || !zpk || !x || !c)
         return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
@@ -256,8 +269,8 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
         overlaps(c, nc, x, nx))
         return fail(W4A16_ERR_INVALID_ARG, "output overlaps an input");
 
-    GemmArgs a = make_args(M, N, K);
-    const w4a16_plan p = plan_in ? *plan_in : default_plan(M, N, K);
+    GemmArgs a = make_args(M, N, K, layout);
+    const w4a16_plan p = plan_in ? *plan_in : default_plan(M, N, K, layout);
     st = check_plan(a, p);
     if (st) return st;
     const size_t need = workspace_bytes_for(a, p);
@@ -407,13 +420,14 @@ int w4a16_gemv(const uint32_t* q_packed, const void* scales, const uint32_t* z_p
     GemmArgs a = make_args(M, 1, K);
     if (workspace_bytes_for(a, p) != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "K=%lld needs a split reduction; use w4a16_gemm", (long long)K);
-    return run_gemm(q_packed, scales, z_packed, x, c, M, 1, K, group_size, &p, nullptr, 0, stream);
+    return run_gemm(q_packed, scales, z_packed, x, c, M, 1, K, group_size, W4A16_LAYOUT_KN, &p, nullptr, 0,
+                    stream);
 }
 
 int w4a16_gemm(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x,
                void* c, int64_t M, int64_t N, int64_t K, int32_t group_size, void* workspace,
                size_t workspace_bytes, void* stream) {
-    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, nullptr, workspace,
+    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, W4A16_LAYOUT_KN, nullptr, workspace,
                     workspace_bytes, stream);
 }
 
@@ -421,8 +435,34 @@ int w4a16_gemm_plan(const uint32_t* q_packed, const void* scales, const uint32_t
                     const void* x, void* c, int64_t M, int64_t N, int64_t K, int32_t group_size,
                     const w4a16_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
     if (!plan) return fail(W4A16_ERR_INVALID_ARG, "plan is NULL");
-    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, plan, workspace,
+    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, W4A16_LAYOUT_KN, plan, workspace,
                     workspace_bytes, stream);
+}
+
+int w4a16_gemm_ex(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x, void* c,
+                  int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, const w4a16_plan* plan,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, layout, plan, workspace,
+                    workspace_bytes, stream);
+}
+
+int w4a16_plan_default_ex(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, w4a16_plan* plan) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    st = check_layout(layout);
+    if (st) return st;
+    if (!plan) return fail(W4A16_ERR_INVALID_ARG, "plan is NULL");
+    *plan = default_plan(M, N, K, layout);
+    return ok();
+}
+
+size_t w4a16_workspace_size_ex(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout,
+                               const w4a16_plan* plan) {
+    if (check_dims(M, N, K, group_size) || check_layout(layout)) return 0;
+    GemmArgs a = make_args(M, N, K, layout);
+    const w4a16_plan p = plan ? *plan : default_plan(M, N, K, layout);
+    if (check_plan(a, p)) return 0;
+    return workspace_bytes_for(a, p);
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@ struct GemmArgs {
     uint32_t* counters;       // one arrival counter per output tile (splitk > 1)
     int64_t M, N, K;
     int32_t G, ZW;
+    int32_t tm;               // 1: token-major x [N, K] and c [N, M] (tiled and narrow kernels; skinny at N = 1)
 };
 
 struct SkinnyShape {

@@ -242,7 +242,13 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         for (int cb = 0; cb < NC; ++cb) {
             const int64_t col = 16 * cb + 4 * kq;
             if (col >= N) continue;
-            if (splitk == 1) {
+            if (splitk == 1 && a.tm) {
+                // token-major output: the 16 lanes of a k-quarter write 16
+                // consecutive rows of one column
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (col + j < N) a.c[(col + j) * M + row] = (uint16_t)f32_to_h16_bits(acc[rb][cb][j]);
+            } else if (splitk == 1) {
                 if (col + 4 <= N && (N & 3) == 0) {
                     uint2 v;
                     v.x = f32_to_h16_bits(acc[rb][cb][0]) | (f32_to_h16_bits(acc[rb][cb][1]) << 16);
@@ -287,7 +293,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         for (int s = 0; s < splitk; ++s)
             v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        a.c[row * N + col] = (uint16_t)f32_to_h16_bits(v);
+        a.c[a.tm ? col * M + row : row * N + col] = (uint16_t)f32_to_h16_bits(v);
     }
 }
 

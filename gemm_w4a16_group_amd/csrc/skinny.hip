@@ -147,7 +147,8 @@ __device__ __forceinline__ half8 unscale_ones() {
 // Activation block: eight consecutive k (one octet) of T8 = min(NT, 8)
 // columns, loaded with 16-byte loads.  With N == NT every block is 16-byte
 // aligned: for NT <= 8 the block is 16 * NT contiguous bytes, otherwise
-// eight rows of 16 bytes.  It becomes T8 LDS chunks, one per column, each
+// eight rows of 16 bytes.  Token-major activations (x^T [N, K], NT <= 8):
+// one 16-byte load per column, which is already that column's octet.  It becomes T8 LDS chunks, one per column, each
 // holding the octet in the order 0, 4, 1, 5, 2, 6, 3, 7, with k 1, 5, 3, 7
 // divided by 16 (exact unless the quotient is subnormal: then rounded once).
 template <int NT>
@@ -156,11 +157,13 @@ struct XStage {
     static constexpr int NB8 = NT <= 8 ? 1 : NT / 8;   // column octets
     u32x4 v[T8];
 
-    __device__ __forceinline__ void load(const uint16_t* x, int64_t k0, int nb8) {
+    __device__ __forceinline__ void load(const uint16_t* x, int64_t k0, int nb8, bool tm, int64_t K) {
         if (NT <= 8) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(x + k0 * NT);
 #pragma unroll
-            for (int t = 0; t < T8; ++t) v[t] = p[t];
+            for (int t = 0; t < T8; ++t) {
+                const uint16_t* src = tm ? x + (int64_t)t * K + k0 : x + k0 * NT + 8 * t;
+                v[t] = *reinterpret_cast<const u32x4*>(src);
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
@@ -174,13 +177,16 @@ struct XStage {
         return j == 0 ? v[t].x : j == 1 ? v[t].y : j == 2 ? v[t].z : v[t].w;
     }
 
-    __device__ __forceinline__ void store(unsigned char* xs, int o, int nb8) const {
+    __device__ __forceinline__ void store(unsigned char* xs, int o, int nb8, bool tm) const {
         const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-        if (T8 == 1) {
-            u32x4 r = permute_k8(v[0]);
-            r.y = as_u32(as_h2(r.y) * sixteenth);
-            r.w = as_u32(as_h2(r.w) * sixteenth);
-            *reinterpret_cast<u32x4*>(xs + (size_t)o * 16) = r;
+        if (T8 == 1 || (NT <= 8 && tm)) {
+#pragma unroll
+            for (int c = 0; c < T8; ++c) {
+                u32x4 r = permute_k8(v[c]);
+                r.y = as_u32(as_h2(r.y) * sixteenth);
+                r.w = as_u32(as_h2(r.w) * sixteenth);
+                *reinterpret_cast<u32x4*>(xs + ((size_t)o * NT + c) * 16) = r;
+            }
             return;
         }
 #pragma unroll
@@ -279,7 +285,7 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
         const int o = b / NB8, nb8 = b % NB8;     // NB8 is a power of two
         int64_t k0 = (int64_t)gw0 * kGroup + (int64_t)o * 8;
         k0 = k0 < a.K - 8 ? k0 : a.K - 8;
-        xst[j].load(a.x, k0, nb8);
+        xst[j].load(a.x, k0, nb8, a.tm != 0, a.K);
     }
     // ---- 2. scales: lane (row li, group 4 j + kb); zero words: lane (row
     // li, word kb)
@@ -321,7 +327,7 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
 #pragma unroll
     for (int j = 0; j < F; ++j) {
         const int b = lane + j * 64;
-        if (b < nxb) xst[j].store(xs, b / NB8, b % NB8);
+        if (b < nxb) xst[j].store(xs, b / NB8, b % NB8, a.tm != 0);
     }
 #pragma unroll
     for (int j = 0; j < SZL; ++j) {
@@ -464,7 +470,12 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             const int t0 = tb * 16 + kb * 4;
-            if (splitk == 1) {
+            if (splitk == 1 && a.tm) {
+                // token-major output: consecutive lanes hold consecutive rows
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (t0 + r < N) a.c[(t0 + r) * M + row] = (uint16_t)f32_to_h16_bits(acc[tb][r]);
+            } else if (splitk == 1) {
                 if ((N & 3) == 0 && t0 + 3 < N) {
                     const uint32_t lo = f32_to_h16_bits(acc[tb][0]) | (f32_to_h16_bits(acc[tb][1]) << 16);
                     const uint32_t hi = f32_to_h16_bits(acc[tb][2]) | (f32_to_h16_bits(acc[tb][3]) << 16);
@@ -511,7 +522,7 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
         for (int s = 0; s < splitk; ++s)
             v += __hip_atomic_load(a.part + ((int64_t)s * M + rr) * N + col, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        a.c[rr * N + col] = (uint16_t)f32_to_h16_bits(v);
+        a.c[a.tm ? col * M + rr : rr * N + col] = (uint16_t)f32_to_h16_bits(v);
     }
 }
 
@@ -561,6 +572,7 @@ const char* skinny_check(const GemmArgs& a, const SkinnyShape& s) {
     if (!skinny_supported(s))
         return "ncol must be 1..8, 16, 32 or 64, rb 1, wm * wk <= 16";
     if (s.splitk > a.G) return "splitk exceeds the number of groups";
+    if (a.tm && a.N > 8) return "token-major activations only for N <= 8";
     SkinnyParams P;
     if (!skinny_params(s.ncol, a.G, s.splitk, s.rb, s.wm, s.wk, P))
         return "a wave's groups exceed its load registers, or the staged data the workgroup's LDS; "

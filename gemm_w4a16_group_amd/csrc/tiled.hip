@@ -71,6 +71,43 @@ __global__ void __launch_bounds__(256) xpack_kernel(const uint16_t* __restrict__
     }
 }
 
+// The same rewrite for few columns (N <= 32), where one thread per column
+// octet would leave most of the chip idle: one thread per chunk (ko, n),
+// eight 2-byte loads down column n (consecutive threads take consecutive
+// columns, so each load instruction reads whole rows), one 16-byte store.
+__global__ void __launch_bounds__(256) xpack_col_kernel(const uint16_t* __restrict__ x, u32x4* __restrict__ xp,
+                                                        int64_t K, int64_t N) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (K / 8) * N) return;
+    const int64_t ko = t / N, n = t % N;
+    const uint16_t* src = x + ko * 8 * N + n;
+    uint32_t h[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) h[r] = src[r * N];
+    // k order 0, 4, 1, 5, 2, 6, 3, 7
+    xp[t] = u32x4{h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16)};
+}
+
+// Token-major X^T [N, K] -> the same chunks.  Chunk (ko, n) is the 16 bytes
+// X^T[n][8 ko .. 8 ko + 7], reordered, so this is a transpose of a [N][K/8]
+// matrix of 16-byte elements.  A workgroup moves a 16 x 16 block through LDS
+// so that both its reads (16 chunks of one token, 256 contiguous bytes) and
+// its writes (16 tokens of one k-octet) are 256-byte runs; rows of 17
+// elements keep the LDS stores of consecutive threads on distinct banks.
+// K / 8 is a multiple of 16; tokens past N are skipped.
+__global__ void __launch_bounds__(256) xpack_tm_kernel(const uint16_t* __restrict__ xt, u32x4* __restrict__ xp,
+                                                       int64_t K, int64_t N) {
+    __shared__ u32x4 tile[16 * 17];
+    const int64_t KO = K / 8;
+    const int64_t kob = KO / 16;
+    const int64_t ko0 = ((int64_t)blockIdx.x % kob) * 16, n0 = ((int64_t)blockIdx.x / kob) * 16;
+    const int t = threadIdx.x, lo = t & 15, hi = t >> 4;
+    if (n0 + hi < N)
+        tile[lo * 17 + hi] = permute_k8(*reinterpret_cast<const u32x4*>(xt + (n0 + hi) * K + (ko0 + lo) * 8));
+    __syncthreads();
+    if (n0 + lo < N) xp[(ko0 + hi) * N + n0 + lo] = tile[hi * 17 + lo];
+}
+
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM>
 __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
@@ -252,21 +289,40 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
     }
 
     // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
+    // (token-major output: the four consecutive rows e = 4 j .. 4 j + 3 of a
+    // column are one 8-byte store)
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CBW; ++cb) {
             const int64_t col = col0 + WN * wave_n + cb * 32 + l32;
             if (col < N) {
+                if (splitk == 1 && a.tm) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
-                    if (row < M) {
-                        if (splitk == 1)
-                            a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rb][cb][e]);
-                        else
-                            __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col, acc[rb][cb][e],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int j = 0; j < 4; ++j) {
+                        const int64_t row = row0 + WM * wave_m + 32 * rb + j * 8 + 4 * hh;
+                        if ((M & 3) == 0 && row + 3 < M) {
+                            uint2 v;
+                            v.x = f32_to_h16_bits(acc[rb][cb][4 * j]) | (f32_to_h16_bits(acc[rb][cb][4 * j + 1]) << 16);
+                            v.y = f32_to_h16_bits(acc[rb][cb][4 * j + 2]) | (f32_to_h16_bits(acc[rb][cb][4 * j + 3]) << 16);
+                            *reinterpret_cast<uint2*>(a.c + col * M + row) = v;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (row + i < M) a.c[col * M + row + i] = (uint16_t)f32_to_h16_bits(acc[rb][cb][4 * j + i]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
+                        if (row < M) {
+                            if (splitk == 1)
+                                a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rb][cb][e]);
+                            else
+                                __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col, acc[rb][cb][e],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
                     }
                 }
             }
@@ -298,7 +354,7 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
         for (int s = 0; s < splitk; ++s)
             v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        a.c[row * N + col] = (uint16_t)f32_to_h16_bits(v);
+        a.c[a.tm ? col * M + row : row * N + col] = (uint16_t)f32_to_h16_bits(v);
     }
 }
 
@@ -334,9 +390,21 @@ int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t) {
 size_t xpack_bytes(const GemmArgs& a) { return (size_t)a.K * (size_t)a.N * 2; }
 
 hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
+    if (a.tm) {
+        const int64_t blocks = (a.K / 128) * ((a.N + 15) / 16);
+        hipLaunchKernelGGL(xpack_tm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.x,
+                           reinterpret_cast<u32x4*>(a.xp), a.K, a.N);
+        return hipGetLastError();
+    }
+    u32x4* xp = reinterpret_cast<u32x4*>(a.xp);
+    if (a.N <= 32) {
+        const int64_t chunks = (a.K / 8) * a.N;
+        hipLaunchKernelGGL(xpack_col_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a.x, xp,
+                           a.K, a.N);
+        return hipGetLastError();
+    }
     const int64_t total = (a.K / 8) * ((a.N + 7) / 8);
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    u32x4* xp = reinterpret_cast<u32x4*>(a.xp);
     if (a.N % 8 == 0)
         hipLaunchKernelGGL((xpack_kernel<true>), dim3(blocks), dim3(256), 0, stream, a.x, xp, a.K, a.N);
     else

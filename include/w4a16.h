@@ -17,8 +17,10 @@
  *   scales    fp16   [M, G], G = K / 128
  *   z_packed  uint32 [M, ceil(G / 8)]    nibble j of word w of row m holds
  *                                        z[m, 8w + j]; padding nibbles are 0
- *   x         fp16   [K, N]              (N contiguous)
- *   c         fp16   [M, N]              (N contiguous), written, never read
+ *   x         fp16   [K, N]              (N contiguous; [N, K] under
+ *                                        W4A16_LAYOUT_TOKEN, see below)
+ *   c         fp16   [M, N]              (N contiguous; [N, M] under
+ *                                        W4A16_LAYOUT_TOKEN), written, never read
  *
  * Conventions shared by every entry point:
  *   - functions never throw, abort or allocate device memory, and never
@@ -199,6 +201,47 @@ int w4a16_gemm_plan(const uint32_t *q_packed, const void *scales,
                     int64_t M, int64_t N, int64_t K, int32_t group_size,
                     const w4a16_plan *plan, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * Activation and output layouts for the _ex entry points.
+ *   W4A16_LAYOUT_KN    : x fp16 [K, N] and c fp16 [M, N] (the product of
+ *                        PerfXLLM §3.3 item 1 as written; what w4a16_gemm
+ *                        takes)
+ *   W4A16_LAYOUT_TOKEN : x fp16 [N, K] and c fp16 [N, M], both row-major:
+ *                        one row per token, the layout a model's hidden
+ *                        states have, so that c = x . Wdeq^T feeds the next
+ *                        layer without a transpose.  Same arithmetic, same
+ *                        rounding: c_token[n, m] equals c_kn[m, n] bit for
+ *                        bit under the same plan.
+ * With N = 1 both layouts are the same memory.
+ */
+enum { W4A16_LAYOUT_KN = 0, W4A16_LAYOUT_TOKEN = 1 };
+
+/*
+ * w4a16_gemm for either layout, with an optional plan (NULL: the layout's
+ * default plan, w4a16_plan_default_ex).  The skinny kernel takes the token
+ * layout for N <= 8 (W4A16_ERR_UNSUPPORTED for its 16- and 32-column plans);
+ * the narrow and tiled kernels take both layouts at any N they support.
+ * Workspace needs are those of the plan, as for w4a16_gemm.  An unknown
+ * layout is W4A16_ERR_INVALID_ARG.  Other checks, workspace rules and error
+ * behaviour as w4a16_gemm.
+ */
+int w4a16_gemm_ex(const uint32_t *q_packed, const void *scales,
+                  const uint32_t *z_packed, const void *x, void *c,
+                  int64_t M, int64_t N, int64_t K, int32_t group_size,
+                  int32_t layout, const w4a16_plan *plan, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* The plan w4a16_gemm_ex uses for this shape and layout (plan NULL there).
+ * Returns a status. */
+int w4a16_plan_default_ex(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                          int32_t layout, w4a16_plan *plan);
+
+/* Workspace bytes w4a16_gemm_ex needs for this layout and plan (NULL: the
+ * layout's default plan); 0 on invalid input or when none is needed. */
+size_t w4a16_workspace_size_ex(int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, int32_t layout,
+                               const w4a16_plan *plan);
 
 #ifdef __cplusplus
 }

@@ -66,19 +66,24 @@ def guards_intact(buf, M, N):
     return bool(np.all(h[:GUARD] == GUARD_BITS) and np.all(h[GUARD + M * N:] == GUARD_BITS))
 
 
-def run(prob, X, plan=None, guard=True):
-    """Run the GEMM on the GPU; returns the fp16 result as numpy [M, N]."""
+def run(prob, X, plan=None, guard=True, layout=B.LAYOUT_KN):
+    """Run the GEMM on the GPU; returns the fp16 result as numpy [M, N].
+    X is always given as [K, N]; with the token layout it goes to the device
+    as [N, K] and the [N, M] result comes back transposed."""
     M, N = prob.M, X.shape[1]
-    xd = dev(X)
+    token = layout == B.LAYOUT_TOKEN
+    xd = dev(X.T if token else X)
+    shape = (N, M) if token else (M, N)
     if guard:
-        buf, out = guarded_out(M, N)
+        buf, out = guarded_out(*shape)
     else:
-        buf, out = None, torch.empty((M, N), dtype=torch.float16, device="cuda")
-    B.gemm(prob.qpk, prob.s_d, prob.zpk, xd, out=out, plan=plan)
+        buf, out = None, torch.empty(shape, dtype=torch.float16, device="cuda")
+    B.gemm(prob.qpk, prob.s_d, prob.zpk, xd, out=out, plan=plan, layout=layout)
     torch.cuda.synchronize()
     if guard:
         assert guards_intact(buf, M, N), "write outside the output"
-    return out.cpu().numpy()
+    res = out.cpu().numpy()
+    return np.ascontiguousarray(res.T) if token else res
 
 
 def assert_parity(C_gpu, C_ref, A_ref, what=""):

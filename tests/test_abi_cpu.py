@@ -190,3 +190,60 @@ def test_quantize_argument_checks(lib):
     # packed codes on top of the input
     assert lib.w4a16_quantize(w, 64, 1024, 128, ctypes.c_void_p(0x10000000 + 4096), s, z, NULL) == INVALID
     assert b"overlap" in lib.w4a16_last_error()
+
+
+def test_token_layout_plans_and_checks(lib):
+    def plan_ex(M, N, K, layout):
+        p = B.Plan()
+        st = lib.w4a16_plan_default_ex(M, N, K, 128, layout, ctypes.byref(p))
+        return st, p
+
+    # N = 1: both layouts are the same memory and take the same plan
+    for M, K in ((4096, 4096), (12288, 4096), (100, 256)):
+        st, p = plan_ex(M, 1, K, B.LAYOUT_TOKEN)
+        assert st == OK
+        q = B.Plan()
+        assert lib.w4a16_plan_default(M, 1, K, 128, ctypes.byref(q)) == OK
+        assert p.as_dict() == q.as_dict()
+    # the skinny kernel only up to N = 8; the chunk-staging kernels need a
+    # workspace for the rewritten activations
+    for N in (2, 5, 7, 8, 16, 17, 32, 33, 64, 200, 4096):
+        for M, K in ((4096, 4096), (11008, 4096), (4096, 11008), (96, 128), (96, 1152)):
+            st, p = plan_ex(M, N, K, B.LAYOUT_TOKEN)
+            assert st == OK, (M, N, K)
+            need = lib.w4a16_workspace_size_ex(M, N, K, 128, B.LAYOUT_TOKEN, ctypes.byref(p))
+            assert lib.w4a16_workspace_size_ex(M, N, K, 128, B.LAYOUT_TOKEN, None) == need
+            if N > 8:
+                assert p.kernel in (B.KERNEL_NARROW, B.KERNEL_TILED), (M, N, K, p.as_dict())
+            if p.kernel != B.KERNEL_SKINNY:
+                assert need >= K * N * 2
+    # the default of the KN layout through the _ex calls equals the plain calls
+    for M, N, K in ((4096, 3, 4096), (4096, 16, 4096), (4096, 4096, 4096)):
+        st, p = plan_ex(M, N, K, B.LAYOUT_KN)
+        q = B.Plan()
+        assert st == OK and lib.w4a16_plan_default(M, N, K, 128, ctypes.byref(q)) == OK
+        assert p.as_dict() == q.as_dict()
+        assert (lib.w4a16_workspace_size_ex(M, N, K, 128, B.LAYOUT_KN, None)
+                == lib.w4a16_gemm_workspace_size(M, N, K, 128))
+    # unknown layout
+    assert plan_ex(64, 4, 256, 2)[0] == INVALID
+    assert b"layout" in lib.w4a16_last_error()
+    assert lib.w4a16_workspace_size_ex(64, 4, 256, 128, -1, None) == 0
+    assert lib.w4a16_gemm_ex(Q, S, Z, X, C, 64, 4, 256, 128, 7, None, NULL, 0, NULL) == INVALID
+    # a 16-column skinny plan under the token layout is refused
+    sk = B.Plan.make(kernel=B.KERNEL_SKINNY, ncol=16, rb=1, wm=1, wk=4, splitk=1)
+    assert lib.w4a16_workspace_size_plan(64, 16, 1152, 128, ctypes.byref(sk)) == 0   # valid, no workspace
+    assert lib.w4a16_kernel_name(64, 16, 1152, 128, ctypes.byref(sk), ctypes.create_string_buffer(64), 64) == OK
+    assert (lib.w4a16_gemm_ex(Q, S, Z, X, C, 64, 16, 1152, 128, B.LAYOUT_TOKEN, ctypes.byref(sk), NULL, 0, NULL)
+            == UNSUPPORTED)
+    assert b"token-major" in lib.w4a16_last_error()
+    assert lib.w4a16_workspace_size_ex(64, 16, 1152, 128, B.LAYOUT_TOKEN, ctypes.byref(sk)) == 0
+    # token layout on a chunk-staging plan, no workspace
+    nr = B.Plan.make(kernel=B.KERNEL_NARROW, ncol=16, pf=8, splitk=1, rb=1, wk=1)
+    assert (lib.w4a16_gemm_ex(Q, S, Z, X, C, 64, 4, 256, 128, B.LAYOUT_TOKEN, ctypes.byref(nr), NULL, 0, NULL)
+            == WORKSPACE)
+    # dimension and pointer checks are the same as w4a16_gemm's
+    assert lib.w4a16_gemm_ex(Q, S, Z, X, C, 64, 0, 256, 128, B.LAYOUT_TOKEN, None, NULL, 0, NULL) == INVALID
+    assert lib.w4a16_gemm_ex(NULL, S, Z, X, C, 64, 1, 256, 128, B.LAYOUT_TOKEN, None, NULL, 0, NULL) == INVALID
+    assert (lib.w4a16_gemm_ex(Q, S, Z, ctypes.c_void_p(0x400008), C, 64, 1, 256, 128, B.LAYOUT_TOKEN, None,
+                              NULL, 0, NULL) == MISALIGNED)
