@@ -6,6 +6,8 @@ leg use this module.  It imports numpy and nothing else.
 Notation follows the PerfXLLM page (3532n.com/d/2322131), §3.3 item 1: the
 product is C[m, n] = A[m, k] . B[k, n], where A is the dequantized weight
 matrix (called W or Wdeq below) and B the fp16 activations (called X).
+The residual add + RMS normalization that feeds the projections (§3.2, first
+fusion) is at the end of the module, with its tolerance.
 """
 
 import numpy as np
@@ -208,3 +210,44 @@ def format_bytes(M, K):
     """
     G = _groups(K)
     return {"q": M * K // 2, "s": 2 * M * G, "z": M * G // 2, "fp16": 2 * M * K}
+
+
+def add_rmsnorm(x, r, gamma, eps):
+    """Residual add followed by RMS normalization, token-major, in float64.
+
+    §3.2 of the PerfXLLM page (operator fusion, first part) runs the residual
+    network's addition and the normalization that follows it as one
+    operator.  The page does not name the normalization; LLaMA's is RMSNorm,
+    the reading taken here: per token, no mean subtraction, no bias, a
+    learned gain per hidden channel.
+
+      h[n, k] = x[n, k] + r[n, k]
+      y[n, k] = h[n, k] / sqrt(mean_k h[n, k]^2 + eps) * gamma[k]
+
+    x, r: [N, K] (fp16 or float), gamma: [K], eps >= 0.  Returns (y, h) in
+    float64.  The residual stream is stored in fp16: ``residual_fp16`` gives
+    the stored h, and the normalization of the stored stream is
+    ``add_rmsnorm(h16, 0, gamma, eps)``.
+    """
+    h = np.asarray(x, dtype=np.float64) + np.asarray(r, dtype=np.float64)
+    if h.ndim != 2:
+        raise ValueError("x and r must be [N, K]")
+    ms = np.mean(h * h, axis=1)
+    y = h / np.sqrt(ms + float(eps))[:, None] * np.asarray(gamma, dtype=np.float64)[None, :]
+    return y, h
+
+
+def residual_fp16(x, r):
+    """The stored residual stream fp16(x + r): the exact sum (float64 holds
+    the sum of two fp16 values exactly) rounded to nearest, ties to even."""
+    return (np.asarray(x, dtype=np.float64) + np.asarray(r, dtype=np.float64)).astype(np.float16)
+
+
+def norm_tolerance(y_ref):
+    """Per-element bound on a normalized fp16 output: 2e-3 * |y| + 1e-6.
+
+    Budget (relative): fp16 rounding of the stored stream h (2^-11), of the
+    output (2^-11), a float32 mean of squares and reciprocal square root
+    (below 1e-6 at K <= 2^16): about 1.0e-3, doubled; the absolute floor
+    covers outputs in the fp16 subnormal range (spacing 6e-8)."""
+    return 2e-3 * np.abs(np.asarray(y_ref, dtype=np.float64)) + 1e-6

@@ -346,4 +346,103 @@ def pin_quantizer_exact_grid(ora):
     assert np.array_equal(s, s0) and np.array_equal(z, z0) and np.array_equal(q, q0)
 
 
+
+# ----------------------------------------------------------------------------
+# residual add + RMS normalization (§3.2 of the PerfXLLM page, first fusion)
+
+def _norm_case(N, K, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((N, K)) * 2).astype(np.float16)
+    r = (rng.standard_normal((N, K)) * 3).astype(np.float16)
+    gamma = rng.uniform(0.5, 1.5, K).astype(np.float16)
+    return x, r, gamma
+
+
+def pin_norm_unit_rms(ora):
+    """With unit gain and eps = 0 every output row has mean square 1 and
+    keeps the signs of h."""
+    x, r, _ = _norm_case(4, 384, 90)
+    y, h = ora.add_rmsnorm(x, r, np.ones(384), 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-12, atol=0)
+    assert np.array_equal(np.sign(y), np.sign(h))
+
+
+def pin_norm_one_hot(ora):
+    """h = a e_j: mean square a^2 / K, so y_j = sqrt(K) sign(a) gamma_j and
+    every other output is 0 (eps = 0)."""
+    K = 256
+    gamma = np.linspace(0.25, 2.0, K)
+    for j, a in ((0, 3.0), (17, -0.5), (255, 1024.0)):
+        x = np.zeros((1, K))
+        x[0, j] = a
+        y, _ = ora.add_rmsnorm(x, np.zeros((1, K)), gamma, 0.0)
+        want = np.zeros(K)
+        want[j] = np.sqrt(K) * np.sign(a) * gamma[j]
+        assert np.allclose(y[0], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_norm_constant_row(ora):
+    """h = c everywhere: y = gamma c / sqrt(c^2 + eps)."""
+    K = 128
+    gamma = np.arange(1, K + 1) / 64.0
+    for c, eps in ((0.5, 1e-6), (-2.0, 0.25), (1e-3, 1e-6)):
+        x = np.full((1, K), c / 2)
+        r = np.full((1, K), c / 2)
+        y, h = ora.add_rmsnorm(x, r, gamma, eps)
+        assert np.allclose(h, c, rtol=0, atol=0)
+        assert np.allclose(y[0], gamma * c / np.sqrt(c * c + eps), rtol=1e-12, atol=0)
+
+
+def pin_norm_scale_invariance(ora):
+    """eps = 0: scaling x and r by c > 0 leaves y unchanged; c < 0 flips it."""
+    x, r, gamma = _norm_case(3, 256, 91)
+    y, _ = ora.add_rmsnorm(x, r, gamma, 0.0)
+    for c in (4.0, 1.0 / 8, -2.0):
+        yc, _ = ora.add_rmsnorm(x.astype(np.float64) * c, r.astype(np.float64) * c, gamma, 0.0)
+        assert np.allclose(yc, np.sign(c) * y, rtol=1e-12, atol=1e-15)
+
+
+def pin_norm_zero_row(ora):
+    """An all-zero stream with eps > 0 normalizes to zeros (no NaN)."""
+    y, h = ora.add_rmsnorm(np.zeros((2, 128)), np.zeros((2, 128)), np.ones(128), 1e-6)
+    assert np.all(y == 0) and np.all(h == 0)
+
+
+def pin_norm_library(ora):
+    """torch's float64 rms_norm on the summed stream (an independent
+    implementation of the same definition), rows of different scales."""
+    import torch
+    x, r, gamma = _norm_case(5, 640, 92)
+    x[3] *= np.float16(0.01)
+    r[3] *= np.float16(0.01)
+    h = torch.from_numpy(x).double().add(torch.from_numpy(r).double())
+    for eps in (1e-6, 1e-5, 0.5):
+        want = torch.nn.functional.rms_norm(h, (640,), torch.from_numpy(gamma).double(), eps).numpy()
+        y, hh = ora.add_rmsnorm(x, r, gamma, eps)
+        assert np.array_equal(hh, h.numpy())
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-14)
+
+
+def pin_residual_rounding(ora):
+    """fp16 rounding of the stream: ties go to the even neighbour, other
+    sums to the nearest fp16 (1 + 2^-11 is half an fp16 step above 1)."""
+    x = np.array([[1.0, 1.0 + 2.0 ** -10, 1.0, -3.0, 1024.0]], dtype=np.float16)
+    r = np.array([[2.0 ** -11, 2.0 ** -11, 2.0 ** -11 + 2.0 ** -20, 0.5, 0.5]], dtype=np.float16)
+    want = np.array([[1.0, 1.0 + 2.0 ** -9, 1.0 + 2.0 ** -10, -2.5, 1024.0]])
+    got = ora.residual_fp16(x, r)
+    assert got.dtype == np.float16
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def pin_norm_tolerance(ora):
+    """The normalized-output bound admits one fp16 rounding of the exact
+    value twice over and rejects a 1% error."""
+    x, r, gamma = _norm_case(3, 512, 93)
+    y, _ = ora.add_rmsnorm(x, r, gamma, 1e-6)
+    tol = ora.norm_tolerance(y)
+    assert np.all(np.abs(y.astype(np.float16).astype(np.float64) - y) <= 0.5 * tol)
+    big = np.abs(y) > 0.1
+    assert not np.any((np.abs(y * 1.01 - y) <= tol)[big])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,20 @@ MUTATIONS = {
     "quantizer_zero_range": ("lo = np.minimum(w.min(axis=2), np.float32(0.0))", "lo = w.min(axis=2)"),
     "quantizer_scale_16": ("s16 = (rng / np.float32(15.0))", "s16 = (rng / np.float32(16.0))"),
     "group_size_64": ("GROUP = 128", "GROUP = 64"),
+    "norm_sum_not_mean": ("ms = np.mean(h * h, axis=1)", "ms = np.sum(h * h, axis=1)"),
+    "norm_mean_over_tokens": ("ms = np.mean(h * h, axis=1)", "ms = np.mean(h * h, axis=0)[:h.shape[0]]"),
+    "norm_no_sqrt": ("h / np.sqrt(ms + float(eps))[:, None]", "h / (ms + float(eps))[:, None]"),
+    "norm_eps_outside_sqrt": ("h / np.sqrt(ms + float(eps))[:, None]", "h / (np.sqrt(ms) + float(eps))[:, None]"),
+    "norm_gain_dropped": ("* np.asarray(gamma, dtype=np.float64)[None, :]", "* 1.0"),
+    "norm_gain_reversed": ("* np.asarray(gamma, dtype=np.float64)[None, :]",
+                           "* np.asarray(gamma, dtype=np.float64)[None, ::-1]"),
+    "norm_residual_subtracted": ("h = np.asarray(x, dtype=np.float64) + np.asarray(r, dtype=np.float64)",
+                                 "h = np.asarray(x, dtype=np.float64) - np.asarray(r, dtype=np.float64)"),
+    "norm_mean_subtracted": ("ms = np.mean(h * h, axis=1)",
+                             "h = h - h.mean(axis=1, keepdims=True)\n    ms = np.mean(h * h, axis=1)"),
+    "residual_not_rounded": ("+ np.asarray(r, dtype=np.float64)).astype(np.float16)",
+                             "+ np.asarray(r, dtype=np.float64))"),
+    "norm_tolerance_loose": ("return 2e-3 * np.abs(", "return 2e-1 * np.abs("),
 }
 
 
