@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
-                             "quantize_12288x4096"])
+                             "quantize_12288x4096", "prologue"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -328,6 +328,47 @@ def extra(args):
                           "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel": "quantize_kernel"}), flush=True)
+        return
+    if args.workload == "prologue":
+        # residual add + RMS normalization feeding the QKV and gate/up
+        # projections (token-major), against the projection alone and the
+        # normalization alone; weight copies cycled through as in the GEMV
+        for name, M, K in (("qkv", 12288, 4096), ("gate_up", 22016, 4096)):
+            cps = max(8, int(1.1e9 // alg_bytes(M, K, 1)))
+            lay = Layer(M, K, 7, copies=cps)
+            for N in (1, 16, 128):
+                xh, rh, gh = inputs.hidden_states(N, K, wid=7)
+                x, r, gm = (torch.from_numpy(a).cuda() for a in (xh, rh, gh))
+                xs = [x.clone() for _ in range(cps)]
+                hs = [torch.empty_like(x) for _ in range(cps)]
+                ys = [torch.empty_like(x) for _ in range(cps)]
+                outs = [torch.empty((N, M), dtype=torch.float16, device="cuda") for _ in range(cps)]
+                variants = {
+                    "gemm": [(lambda c=c, o=o, xx=xx: B.gemm(c[0], c[1], c[2], xx, out=o, layout=B.LAYOUT_TOKEN))
+                             for c, o, xx in zip(lay.copies, outs, xs)],
+                    "add_rmsnorm": [(lambda xx=xx, h=h, y=y: B.add_rmsnorm(xx, r, gm, 1e-6, h=h, y=y))
+                                    for xx, h, y in zip(xs, hs, ys)],
+                    "fused": [(lambda c=c, o=o, xx=xx, h=h: B.gemm_add_rmsnorm(c[0], c[1], c[2], xx, r, gm, 1e-6,
+                                                                             h=h, out=o))
+                              for c, o, xx, h in zip(lay.copies, outs, xs, hs)],
+                }
+                res = {}
+                for vname, calls in variants.items():
+                    stream = torch.cuda.Stream()
+                    g = capture(calls, stream)
+                    time_graph(g, 2, stream)
+                    reps = max(2, args.steps // cps)
+                    res[vname] = time_graph(g, reps, stream) / (reps * cps) * 1e3
+                    del g
+                nb = 8 * N * K + 2 * K
+                print(json.dumps({"workload": "prologue_" + name, "M": M, "K": K, "N": N,
+                                  "gemm_us": round(res["gemm"], 3), "add_rmsnorm_us": round(res["add_rmsnorm"], 3),
+                                  "fused_us": round(res["fused"], 3),
+                                  "fused_over_gemm_us": round(res["fused"] - res["gemm"], 3),
+                                  "add_rmsnorm_GB/s": round(nb / (res["add_rmsnorm"] * 1e-6) / 1e9, 1),
+                                  "plan": B.plan_default(M, N, K, B.LAYOUT_TOKEN).as_dict()}), flush=True)
+            del lay
+            torch.cuda.empty_cache()
         return
     if args.workload == "gemv_4096x4096":
         ms, plan, steps, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup)

@@ -97,6 +97,14 @@ def load_library(path=None):
         lib.w4a16_plan_default_ex.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan)]
         lib.w4a16_workspace_size_ex.restype = sz
         lib.w4a16_workspace_size_ex.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan)]
+        f32 = ctypes.c_float
+        lib.w4a16_add_rmsnorm.restype = ctypes.c_int
+        lib.w4a16_add_rmsnorm.argtypes = [vp, vp, vp, f32, vp, vp, i64, i64, vp]
+        lib.w4a16_gemm_add_rmsnorm.restype = ctypes.c_int
+        lib.w4a16_gemm_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, vp, i64, i64, i64, i32,
+                                               ctypes.POINTER(Plan), vp, sz, vp]
+        lib.w4a16_gemm_add_rmsnorm_workspace_size.restype = sz
+        lib.w4a16_gemm_add_rmsnorm_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
         if path is None:
             _lib = lib
         return lib
@@ -302,3 +310,56 @@ def gemm(qpk, s, zpk, x, out=None, plan=None, workspace=None, layout=LAYOUT_KN):
         _check(lib().w4a16_gemm_plan(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP,
                                      ctypes.byref(plan), _p(ws), ws_bytes, _stream()))
     return out
+
+
+def add_rmsnorm(x, residual, gamma, eps=1e-6, h=None, y=None):
+    """h = fp16(x + residual), y = RMSNorm(h) * gamma, token-major [N, K].
+    Pass h=residual to update the residual stream in place.  Returns (y, h)."""
+    _need(x, "x", torch.float16)
+    if x.dim() != 2:
+        raise ValueError("x must be [N, K]")
+    N, K = x.shape
+    _need(residual, "residual", torch.float16, (N, K))
+    _need(gamma, "gamma", torch.float16, (K,))
+    if h is None:
+        h = torch.empty_like(x)
+    else:
+        _need(h, "h", torch.float16, (N, K))
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", torch.float16, (N, K))
+    _check(lib().w4a16_add_rmsnorm(_p(x), _p(residual), _p(gamma), float(eps), _p(h), _p(y), N, K, _stream()))
+    return y, h
+
+
+def gemm_add_rmsnorm(qpk, s, zpk, x, residual, gamma, eps=1e-6, h=None, out=None, plan=None, workspace=None):
+    """Token-major fused prologue + product: h = fp16(x + residual) and
+    out[N, M] = RMSNorm(h) * gamma . Wdeq^T.  Returns (out, h)."""
+    M, N, K = _dims(qpk, s, zpk, x, LAYOUT_TOKEN)
+    if x.dim() != 2:
+        raise ValueError("x must be [N, K]")
+    _need(residual, "residual", torch.float16, (N, K))
+    _need(gamma, "gamma", torch.float16, (K,))
+    if h is None:
+        h = torch.empty_like(x)
+    else:
+        _need(h, "h", torch.float16, (N, K))
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", torch.float16)
+        if out.numel() != M * N:
+            raise ValueError("out must hold M*N=%d values" % (M * N))
+    need = int(lib().w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, GROUP,
+                                                           None if plan is None else ctypes.byref(plan)))
+    if workspace is None:
+        ws = _workspace_for(x.device).get(max(need, 1))
+    else:
+        ws = workspace.get(max(need, 1)) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().w4a16_gemm_add_rmsnorm(_p(qpk), _p(s), _p(zpk), _p(x), _p(residual), _p(gamma), float(eps),
+                                        _p(h), _p(out), M, N, K, GROUP,
+                                        None if plan is None else ctypes.byref(plan), _p(ws), ws_bytes,
+                                        _stream()))
+    return out, h

@@ -302,6 +302,87 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
     return ok();
 }
 
+// Residual add + RMS normalization feeding the GEMM (token-major).  The
+// normalized activations go into the workspace's chunk region: in the chunk
+// layout for the tiled and narrow kernels (which then skip their own
+// rewrite), row-major [N, K] for the skinny kernel (which reads x directly).
+size_t norm_workspace_bytes(const GemmArgs& a, const w4a16_plan& p) { return chunks_offset(a, p) + xpack_bytes(a); }
+
+int check_eps(float eps) {
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(W4A16_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    return W4A16_OK;
+}
+
+// h may be the residual buffer itself (updated in place), never a partial overlap
+bool bad_stream_alias(const void* h, const void* r, size_t n) { return h != r && overlaps(h, n, r, n); }
+
+int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, const void* residual,
+                  const void* gamma, float eps, void* h, void* c, int64_t M, int64_t N, int64_t K,
+                  int32_t group_size, const w4a16_plan* plan_in, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    st = check_eps(eps);
+    if (st) return st;
+    if (!qpk || !scales || !zpk || !x || !residual || !gamma || !h || !c)
+        return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(qpk) || !aligned16(scales) || !aligned16(zpk) || !aligned16(x) || !aligned16(residual) ||
+        !aligned16(gamma) || !aligned16(h) || !aligned16(c))
+        return fail(W4A16_ERR_MISALIGNED, "every data pointer must be 16-byte aligned");
+    const int64_t G = groups_of(K);
+    const size_t nq = (size_t)M * (size_t)(K / 8) * 4, ns = (size_t)M * G * 2,
+                 nz = (size_t)M * zwords_of(K) * 4, nx = (size_t)K * N * 2, nc = (size_t)M * N * 2,
+                 ng = (size_t)K * 2;
+    if (overlaps(c, nc, qpk, nq) || overlaps(c, nc, scales, ns) || overlaps(c, nc, zpk, nz) ||
+        overlaps(c, nc, x, nx) || overlaps(c, nc, residual, nx) || overlaps(c, nc, gamma, ng) ||
+        overlaps(c, nc, h, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "output overlaps another buffer");
+    if (overlaps(h, nx, x, nx) || overlaps(h, nx, gamma, ng) || overlaps(h, nx, qpk, nq) ||
+        overlaps(h, nx, scales, ns) || overlaps(h, nx, zpk, nz) || bad_stream_alias(h, residual, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "h overlaps an input (only h == residual is allowed)");
+
+    GemmArgs a = make_args(M, N, K, W4A16_LAYOUT_TOKEN);
+    const w4a16_plan p = plan_in ? *plan_in : default_plan(M, N, K, W4A16_LAYOUT_TOKEN);
+    st = check_plan(a, p);
+    if (st) return st;
+    const size_t need = norm_workspace_bytes(a, p);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    if (overlaps(workspace, need, c, nc) || overlaps(workspace, need, qpk, nq) ||
+        overlaps(workspace, need, scales, ns) || overlaps(workspace, need, zpk, nz) ||
+        overlaps(workspace, need, x, nx) || overlaps(workspace, need, residual, nx) ||
+        overlaps(workspace, need, gamma, ng) || overlaps(workspace, need, h, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
+    uint16_t* y = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + chunks_offset(a, p));
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    a.qpk = qpk;
+    a.scales = static_cast<const uint16_t*>(scales);
+    a.zpk = zpk;
+    a.c = static_cast<uint16_t*>(c);
+    const bool chunks = p.kernel != W4A16_KERNEL_SKINNY;
+    if (chunks) {
+        a.xp = y;
+        a.xp_ready = 1;
+        a.x = y;   // unused: the chunks are ready
+    } else {
+        a.x = y;   // the skinny kernel reads the normalized rows [N, K]
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_add_rmsnorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(residual),
+                                      static_cast<const uint16_t*>(gamma), eps, static_cast<uint16_t*>(h), y, N, K,
+                                      chunks, s);
+    if (e == hipSuccess)
+        e = p.kernel == W4A16_KERNEL_SKINNY   ? launch_skinny(a, skinny_of(p), s)
+            : p.kernel == W4A16_KERNEL_NARROW ? launch_narrow(a, narrow_of(p), s)
+                                              : launch_tiled(a, tiled_of(p), s);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,6 +544,46 @@ size_t w4a16_workspace_size_ex(int64_t M, int64_t N, int64_t K, int32_t group_si
     const w4a16_plan p = plan ? *plan : default_plan(M, N, K, layout);
     if (check_plan(a, p)) return 0;
     return workspace_bytes_for(a, p);
+}
+
+int w4a16_add_rmsnorm(const void* x, const void* residual, const void* gamma, float eps, void* h, void* y,
+                      int64_t N, int64_t K, void* stream) {
+    if (N < 1 || N >= kMaxDim || K < 8 || K >= kMaxDim || K % 8)
+        return fail(W4A16_ERR_INVALID_ARG, "need N >= 1, K >= 8, K %% 8 == 0, both below 2^31 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    int st = check_eps(eps);
+    if (st) return st;
+    if (!x || !residual || !gamma || !h || !y) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(gamma) || !aligned16(h) || !aligned16(y))
+        return fail(W4A16_ERR_MISALIGNED, "every data pointer must be 16-byte aligned");
+    const size_t nx = (size_t)N * (size_t)K * 2, ng = (size_t)K * 2;
+    if (overlaps(y, nx, x, nx) || overlaps(y, nx, residual, nx) || overlaps(y, nx, gamma, ng) ||
+        overlaps(y, nx, h, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "y overlaps another buffer");
+    if (overlaps(h, nx, x, nx) || overlaps(h, nx, gamma, ng) || bad_stream_alias(h, residual, nx))
+        return fail(W4A16_ERR_INVALID_ARG, "h overlaps an input (only h == residual is allowed)");
+    hipError_t e = launch_add_rmsnorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(residual),
+                                      static_cast<const uint16_t*>(gamma), eps, static_cast<uint16_t*>(h),
+                                      static_cast<uint16_t*>(y), N, K, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t w4a16_gemm_add_rmsnorm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size,
+                                             const w4a16_plan* plan) {
+    if (check_dims(M, N, K, group_size)) return 0;
+    GemmArgs a = make_args(M, N, K, W4A16_LAYOUT_TOKEN);
+    const w4a16_plan p = plan ? *plan : default_plan(M, N, K, W4A16_LAYOUT_TOKEN);
+    if (check_plan(a, p)) return 0;
+    return norm_workspace_bytes(a, p);
+}
+
+int w4a16_gemm_add_rmsnorm(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x,
+                           const void* residual, const void* gamma, float eps, void* h, void* c, int64_t M,
+                           int64_t N, int64_t K, int32_t group_size, const w4a16_plan* plan, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return run_gemm_norm(q_packed, scales, z_packed, x, residual, gamma, eps, h, c, M, N, K, group_size, plan,
+                         workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

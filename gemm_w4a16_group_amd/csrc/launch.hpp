@@ -17,7 +17,8 @@ struct GemmArgs {
     uint32_t* counters;       // one arrival counter per output tile (splitk > 1)
     int64_t M, N, K;
     int32_t G, ZW;
-    int32_t tm;               // 1: token-major x [N, K] and c [N, M] (tiled and narrow kernels; skinny at N = 1)
+    int32_t tm;               // 1: token-major x [N, K] and c [N, M]
+    int32_t xp_ready;         // 1: a.xp already holds the activation chunks (no rewrite before the GEMM)
 };
 
 struct SkinnyShape {
@@ -60,6 +61,11 @@ hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t st
 
 // X [K, N] -> 16-byte chunks [K/8][N] in a.xp (the tiled and narrow kernels' B/A operand layout)
 hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream);
+
+// h = fp16(x + r), y = fp16(h * rsqrt(mean h^2 + eps) * gamma), token-major [N, K]; with chunks, y is
+// written in the activation-chunk layout [K/8][N] of the tiled and narrow kernels
+hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* gamma, float eps, uint16_t* h,
+                              uint16_t* y, int64_t N, int64_t K, bool chunks, hipStream_t stream);
 
 // fp16 W [M, K] -> q_packed, fp16 scales, z_packed (round to nearest per group)
 hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,

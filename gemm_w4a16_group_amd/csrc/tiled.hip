@@ -390,6 +390,7 @@ int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t) {
 size_t xpack_bytes(const GemmArgs& a) { return (size_t)a.K * (size_t)a.N * 2; }
 
 hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
+    if (a.xp_ready) return hipSuccess;
     if (a.tm) {
         const int64_t blocks = (a.K / 128) * ((a.N + 15) / 16);
         hipLaunchKernelGGL(xpack_tm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.x,

@@ -95,19 +95,33 @@ def uniform_codes(shape, seed):
     return np.random.default_rng(seed).integers(0, 16, shape, dtype=np.uint8)
 
 
-def fp16_weights(M, K, seed):
-    """Unquantized fp16 weights ~ N(0, 0.02^2), for the quantizer's tests."""
-    rng = np.random.default_rng([seed, 7])
-    return (0.02 * rng.standard_normal((M, K))).astype(np.float16)
-
-
 def fp16_weights(M, K, wid=0, layer=0, proj=0, sigma=0.02, outliers=1e-3):
     """Unquantized weights for the quantizer, fp16 [M, K]: normal with
     standard deviation sigma (drawn in float32, rounded to fp16), a fraction
     `outliers` of them scaled by 20 (the heavy tail of trained linears).
-    Stream 2 of the weight seed, so it is independent of the code draws."""
-    rng = np.random.default_rng([wid, layer, proj, 2])
+    Stream 3 of the weight seed, so it is independent of the code, scale
+    and zero draws."""
+    rng = np.random.default_rng([wid, layer, proj, 3])
     w = rng.standard_normal((M, K), dtype=np.float32) * np.float32(sigma)
     mask = rng.random((M, K)) < outliers
     w[mask] *= np.float32(20.0)
     return w.astype(np.float16)
+
+
+def hidden_states(N, K, wid=0, layer=0, outlier_channels=0.01):
+    """Inputs of the residual add + RMS normalization, token-major:
+    (x fp16 [N, K], residual fp16 [N, K], gamma fp16 [K]).
+
+    residual ~ N(0, 1) with a fixed fraction of channels 10x larger (the
+    outlier channels of LLaMA hidden states), x ~ N(0, 0.5^2) (a sublayer's
+    output), gamma uniform in [0.1, 1.2]; all drawn in float32 and rounded to
+    fp16.  Stream 4 of (wid, layer); tokens are rows, so a prefix of N rows
+    is the same for every larger N."""
+    rng = np.random.default_rng([wid, layer, 0, 4])
+    big = rng.random(K) < outlier_channels
+    gamma = rng.uniform(0.1, 1.2, K).astype(np.float32).astype(np.float16)
+    rows = np.random.default_rng([wid, layer, 1, 4])
+    res = rows.standard_normal((N, 2, K), dtype=np.float32)
+    residual = res[:, 0, :] * np.where(big, np.float32(10.0), np.float32(1.0))[None, :]
+    x = res[:, 1, :] * np.float32(0.5)
+    return x.astype(np.float16), residual.astype(np.float16), gamma

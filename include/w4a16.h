@@ -243,6 +243,52 @@ size_t w4a16_workspace_size_ex(int64_t M, int64_t N, int64_t K,
                                int32_t group_size, int32_t layout,
                                const w4a16_plan *plan);
 
+/*
+ * Residual add + RMS normalization, the first operator fusion of PerfXLLM
+ * §3.2 (the residual network's addition and the normalization as one
+ * operator; the normalization read as LLaMA's RMSNorm).  Token-major:
+ *   h[n, k] = fp16(x[n, k] + residual[n, k])            (round to nearest even)
+ *   y[n, k] = fp16(h[n, k] * rsqrt(mean_k h[n, k]^2 + eps) * gamma[k])
+ * with the mean of squares taken in float32 over the stored fp16 h.
+ *   x, residual : fp16 [N, K];  gamma : fp16 [K];  eps : finite, >= 0
+ *   h           : out, fp16 [N, K]; may be residual itself (in-place
+ *                 update of the stream), must not overlap it otherwise
+ *   y           : out, fp16 [N, K]; overlaps nothing
+ * Requires N >= 1, K >= 8, K % 8 == 0, 16-byte aligned pointers.  h is
+ * bit-exact; y is within 2e-3 |y| + 1e-6 of the float64 result.
+ */
+int w4a16_add_rmsnorm(const void *x, const void *residual, const void *gamma,
+                      float eps, void *h, void *y, int64_t N, int64_t K,
+                      void *stream);
+
+/*
+ * The same normalization feeding the W4A16 product, token-major (the fused
+ * prologue of a QKV or gate/up projection):
+ *   h = fp16(x + residual);  c[n, m] = sum_k Wdeq[m, k] * y[n, k]
+ * with y as in w4a16_add_rmsnorm and c fp16 [N, M].  y never reaches the
+ * caller: it is written into the workspace, in the activation layout the
+ * plan's kernel reads (the tiled and narrow kernels then skip their own
+ * rewrite of the activations; the skinny kernel, N <= 8, reads y rows).
+ * Two launches per call.  plan: NULL for the token-major default plan
+ * (w4a16_plan_default_ex with W4A16_LAYOUT_TOKEN).  workspace: at least
+ * w4a16_gemm_add_rmsnorm_workspace_size() bytes, with the rules of
+ * w4a16_gemm.  h may be residual itself; c overlaps nothing.  Other
+ * requirements and errors as w4a16_gemm_ex and w4a16_add_rmsnorm.
+ */
+int w4a16_gemm_add_rmsnorm(const uint32_t *q_packed, const void *scales,
+                           const uint32_t *z_packed, const void *x,
+                           const void *residual, const void *gamma, float eps,
+                           void *h, void *c, int64_t M, int64_t N, int64_t K,
+                           int32_t group_size, const w4a16_plan *plan,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Workspace bytes of w4a16_gemm_add_rmsnorm for a plan (NULL: the
+ * token-major default plan); 0 on invalid input. */
+size_t w4a16_gemm_add_rmsnorm_workspace_size(int64_t M, int64_t N, int64_t K,
+                                             int32_t group_size,
+                                             const w4a16_plan *plan);
+
 #ifdef __cplusplus
 }
 #endif

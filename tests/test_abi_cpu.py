@@ -247,3 +247,50 @@ def test_token_layout_plans_and_checks(lib):
     assert lib.w4a16_gemm_ex(NULL, S, Z, X, C, 64, 1, 256, 128, B.LAYOUT_TOKEN, None, NULL, 0, NULL) == INVALID
     assert (lib.w4a16_gemm_ex(Q, S, Z, ctypes.c_void_p(0x400008), C, 64, 1, 256, 128, B.LAYOUT_TOKEN, None,
                               NULL, 0, NULL) == MISALIGNED)
+
+
+def test_add_rmsnorm_checks(lib):
+    R, G_, H, Y = (ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(4))
+    f = lib.w4a16_add_rmsnorm
+    # dimensions, eps, pointers, alignment
+    assert f(X, R, G_, 1e-6, H, Y, 0, 4096, NULL) == INVALID
+    assert f(X, R, G_, 1e-6, H, Y, 2, 4, NULL) == INVALID
+    assert f(X, R, G_, 1e-6, H, Y, 2, 4100, NULL) == INVALID
+    assert f(X, R, G_, -1.0, H, Y, 2, 4096, NULL) == INVALID
+    assert f(X, R, G_, float("nan"), H, Y, 2, 4096, NULL) == INVALID
+    assert f(X, R, G_, float("inf"), H, Y, 2, 4096, NULL) == INVALID
+    assert b"eps" in lib.w4a16_last_error()
+    assert f(X, R, NULL, 1e-6, H, Y, 2, 4096, NULL) == INVALID
+    assert f(X, R, G_, 1e-6, ctypes.c_void_p(0x2000008), Y, 2, 4096, NULL) == MISALIGNED
+    # y overlapping an input; h partially overlapping the residual
+    assert f(X, R, G_, 1e-6, H, ctypes.c_void_p(0x1000000 + 4096), 2, 4096, NULL) == INVALID
+    assert f(X, R, G_, 1e-6, ctypes.c_void_p(0x1000000 + 16), Y, 2, 4096, NULL) == INVALID
+    assert b"h overlaps" in lib.w4a16_last_error()
+    assert f(X, R, G_, 1e-6, X, Y, 2, 4096, NULL) == INVALID
+
+
+def test_gemm_add_rmsnorm_checks(lib):
+    R, G_, H = (ctypes.c_void_p(0x10000000 * (i + 8)) for i in range(3))
+    q, s, z, x, c = (ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(5))
+    ws = ctypes.c_void_p(0x10000000 * 12)
+    M, N, K = 4096, 16, 4096
+
+    def call(eps=1e-6, h=H, cc=c, wsp=ws, wsb=1 << 26, plan=None, n=N):
+        return lib.w4a16_gemm_add_rmsnorm(q, s, z, x, R, G_, eps, h, cc, M, n, K, 128, plan, wsp, wsb, NULL)
+
+    for n in (1, 3, 8, 16, 32, 100, 4096):
+        need = lib.w4a16_gemm_add_rmsnorm_workspace_size(M, n, K, 128, None)
+        assert need >= K * n * 2, n    # the normalized rows always live in the workspace
+    need = lib.w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, 128, None)
+    assert call(wsp=NULL, wsb=0) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(eps=-1e-3) == INVALID
+    assert call(h=NULL) == INVALID
+    assert call(h=ctypes.c_void_p(0x10000000 * 8 + 16)) == INVALID      # partial overlap of the residual
+    assert call(h=x) == INVALID
+    assert call(cc=ctypes.c_void_p(0x10000000 * 9 + 64)) == INVALID     # c over gamma
+    assert call(wsp=ctypes.c_void_p(0x10000000 * 10 - 4096)) == INVALID  # workspace runs into h
+    sk = B.Plan.make(kernel=B.KERNEL_SKINNY, ncol=16, rb=1, wm=1, wk=4, splitk=1)
+    assert call(plan=ctypes.byref(sk)) == UNSUPPORTED                    # token-major skinny needs N <= 8
+    assert lib.w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, 128, ctypes.byref(sk)) == 0
+    assert lib.w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, 64, None) == 0
