@@ -251,3 +251,87 @@ def norm_tolerance(y_ref):
     (below 2e-5 at K <= 2^16): about 1.0e-3, doubled; the absolute floor
     covers outputs in the fp16 subnormal range (spacing 6e-8)."""
     return 2e-3 * np.abs(np.asarray(y_ref, dtype=np.float64)) + 1e-6
+
+
+def rope(x, pos, base=10000.0):
+    """Rotary position encoding of the last axis of x (length D, even).
+
+    §3.2 of the PerfXLLM page fuses the rotary encoding of Q and K into the
+    attention operator without defining it; read here as LLaMA's: the
+    channel pairs (2i, 2i + 1) of a head are rotated by the angle
+    pos * base^(-2i / D):
+
+      out[2i]     = x[2i] cos(a_i) - x[2i + 1] sin(a_i)
+      out[2i + 1] = x[2i] sin(a_i) + x[2i + 1] cos(a_i)
+
+    pos broadcasts against x[..., 0].  float64 throughout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % 2:
+        raise ValueError("the head dimension must be even")
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * i / D)
+    a = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(a), np.sin(a)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def decode_attention(qkv, k_cache, v_cache, pos, H, D, base=10000.0, scale=None):
+    """One decode step of multi-head attention per sequence, in float64.
+
+    §3.2 of the PerfXLLM page, third fusion: the rotary encoding of Q and K,
+    the two products QK^T and PV, and the softmax between them.  For each
+    sequence b with its new token at position p = pos[b] (0-based):
+
+      q, k, v = the head slices of qkv[b] = [q | k | v], each [H, D]
+      q' = rope(q, p);  k' = fp16(rope(k, p))    (k' is stored in the cache)
+      keys j = 0 .. p: K_j = k_cache[b, :, j] for j < p, K_p = k'
+                       V_j = v_cache[b, :, j] for j < p, V_p = fp16(v)
+      s_j = scale * q' . K_j  (scale = 1 / sqrt(D) by default)
+      out[b, h] = sum_j softmax(s)_j V_j
+
+    qkv: [B, 3 H D]; k_cache, v_cache: [B, H, S, D]; pos: [B] ints with
+    0 <= p < S.  Returns (out [B, H D], A [B, H D], k_new [B, H, D],
+    v_new [B, H, D]), where A = sum_j softmax(s)_j |V_j| bounds the error
+    of out, and k_new / v_new are the float64 entries the step stores at
+    position p (the stored values are their fp16 roundings).
+    """
+    qkv = np.asarray(qkv, dtype=np.float64)
+    B = qkv.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, H * D))
+    A = np.zeros((B, H * D))
+    k_new = np.zeros((B, H, D))
+    v_new = np.zeros((B, H, D))
+    for b in range(B):
+        p = int(pos[b])
+        q = qkv[b, 0:H * D].reshape(H, D)
+        k = qkv[b, H * D:2 * H * D].reshape(H, D)
+        v = qkv[b, 2 * H * D:3 * H * D].reshape(H, D)
+        qr = rope(q, p, base)
+        kr = rope(k, p, base)
+        k_new[b], v_new[b] = kr, v
+        Kc = np.asarray(k_cache[b, :, :p], dtype=np.float64)
+        Vc = np.asarray(v_cache[b, :, :p], dtype=np.float64)
+        Kall = np.concatenate([Kc, kr.astype(np.float16).astype(np.float64)[:, None, :]], axis=1)
+        Vall = np.concatenate([Vc, v.astype(np.float16).astype(np.float64)[:, None, :]], axis=1)
+        for h in range(H):
+            s = scale * (Kall[h] @ qr[h])
+            w = np.exp(s - s.max())
+            w /= w.sum()
+            out[b, h * D:(h + 1) * D] = w @ Vall[h]
+            A[b, h * D:(h + 1) * D] = w @ np.abs(Vall[h])
+    return out, A, k_new, v_new
+
+
+def rope_tolerance(ref, pair_norm):
+    """Bound on a stored fp16 rotated key: half an fp16 step (2^-11 |ref|),
+    float32 rotation of the pair (1e-6 of its norm) and the fp16 subnormal
+    half-spacing (6e-8)."""
+    return 2.0 ** -11 * np.abs(ref) + 1e-6 * pair_norm + 6e-8

@@ -445,4 +445,137 @@ def pin_norm_tolerance(ora):
     assert not np.any((np.abs(y * 1.01 - y) <= tol)[big])
 
 
+
+# ----------------------------------------------------------------------------
+# rotary encoding and decode attention (§3.2 of the PerfXLLM page, third fusion)
+
+def pin_rope_closed_form(ora):
+    """D = 2: the pair turns by pos radians; D = 4 with base 16: the second
+    pair turns by pos / 4; position 0 is the identity."""
+    for p in (0, 1, 3, 100):
+        assert np.allclose(ora.rope([1.0, 0.0], p), [np.cos(p), np.sin(p)], rtol=0, atol=1e-15)
+        assert np.allclose(ora.rope([0.0, 1.0], p), [-np.sin(p), np.cos(p)], rtol=0, atol=1e-15)
+        assert np.allclose(ora.rope([0.0, 0.0, 1.0, 0.0], p, base=16.0),
+                           [0.0, 0.0, np.cos(p / 4), np.sin(p / 4)], rtol=0, atol=1e-15)
+        assert np.allclose(ora.rope([0.0, 1.0, 0.0, 0.0], p, base=16.0),
+                           [-np.sin(p), np.cos(p), 0.0, 0.0], rtol=0, atol=1e-15)
+    x = np.random.default_rng(94).standard_normal((3, 128))
+    assert np.array_equal(ora.rope(x, 0), x)
+
+
+def pin_rope_complex(ora):
+    """The pairs as complex numbers x[2i] + i x[2i+1], multiplied by
+    exp(i pos base^(-2i/D)); pair norms are kept."""
+    rng = np.random.default_rng(95)
+    D = 128
+    x = rng.standard_normal((4, D))
+    pos = np.array([0, 1, 17, 2047])
+    z = x[:, 0::2] + 1j * x[:, 1::2]
+    ang = pos[:, None] * np.power(10000.0, -np.arange(0, D, 2) / D)[None, :]
+    w = z * np.exp(1j * ang)
+    got = ora.rope(x, pos)
+    assert np.allclose(got[:, 0::2], w.real, rtol=0, atol=1e-12)
+    assert np.allclose(got[:, 1::2], w.imag, rtol=0, atol=1e-12)
+    assert np.allclose(np.hypot(got[:, 0::2], got[:, 1::2]), np.abs(z), rtol=1e-13)
+
+
+def pin_rope_relative_position(ora):
+    """q . k after encoding depends on the positions only through their
+    difference."""
+    rng = np.random.default_rng(96)
+    q, k = rng.standard_normal((2, 128))
+    for m, n, t in ((5, 2, 100), (0, 9, 33), (700, 700, 1)):
+        a = ora.rope(q, m) @ ora.rope(k, n)
+        b = ora.rope(q, m + t) @ ora.rope(k, n + t)
+        assert abs(a - b) <= 1e-10 * (1 + abs(a))
+
+
+def _attn_case(B, H, D, S, seed):
+    rng = np.random.default_rng(seed)
+    qkv = rng.standard_normal((B, 3 * H * D)).astype(np.float16)
+    kc = rng.standard_normal((B, H, S, D)).astype(np.float16)
+    vc = rng.standard_normal((B, H, S, D)).astype(np.float16)
+    return qkv, kc, vc
+
+
+def pin_attention_first_token(ora):
+    """At position 0 the only key is the new one: out = fp16(v), whatever q
+    and k are; the stored key is rope(k, 0) = k."""
+    qkv, kc, vc = _attn_case(2, 3, 16, 4, 97)
+    out, A, kn, vn = ora.decode_attention(qkv, kc, vc, [0, 0], 3, 16)
+    v = qkv[:, 2 * 48:].astype(np.float64)
+    assert np.array_equal(out, v) and np.array_equal(A, np.abs(v))
+    assert np.array_equal(kn.reshape(2, 48), qkv[:, 48:96].astype(np.float64))
+
+
+def pin_attention_uniform(ora):
+    """q = 0: every score is 0, so out is the mean of the p + 1 values and A
+    the mean of their magnitudes."""
+    H, D, S = 2, 8, 12
+    qkv, kc, vc = _attn_case(3, H, D, S, 98)
+    qkv[:, :H * D] = 0
+    pos = [1, 7, 11]
+    out, A, _, _ = ora.decode_attention(qkv, kc, vc, pos, H, D)
+    for b, p in enumerate(pos):
+        V = np.concatenate([vc[b, :, :p].astype(np.float64),
+                            qkv[b, 2 * H * D:].astype(np.float64).reshape(H, 1, D)], axis=1)
+        assert np.allclose(out[b], V.mean(axis=1).reshape(-1), rtol=1e-13, atol=1e-15)
+        assert np.allclose(A[b], np.abs(V).mean(axis=1).reshape(-1), rtol=1e-13, atol=1e-15)
+
+
+def pin_attention_two_keys_closed_form(ora):
+    """D = 2, position 1: q = k = (1, 0) both turn by 1 radian, and the cached
+    key (cos 1, sin 1) equals the new one up to its fp16 rounding, so the two
+    scores match and out is the mean of the two values."""
+    c1 = np.float16(np.cos(1.0))
+    s1 = np.float16(np.sin(1.0))
+    qkv = np.array([[1.0, 0.0, 1.0, 0.0, 3.0, -1.0]], dtype=np.float16)
+    kc = np.array([[[[c1, s1], [0, 0]]]], dtype=np.float16)
+    vc = np.array([[[[1.0, 5.0], [0, 0]]]], dtype=np.float16)
+    out, _, kn, _ = ora.decode_attention(qkv, kc, vc, [1], 1, 2)
+    assert np.allclose(kn[0, 0], [np.cos(1.0), np.sin(1.0)], rtol=0, atol=1e-15)
+    assert np.allclose(out[0], [2.0, 2.0], rtol=0, atol=1e-12)
+
+
+def pin_attention_dominant_key(ora):
+    """A cached key along q, 40x longer than the others: its value wins."""
+    H, D, S = 1, 16, 9
+    qkv, kc, vc = _attn_case(1, H, D, S, 99)
+    p = 6
+    qr = ora.rope(qkv[0, :D].astype(np.float64), p)
+    kc[0, 0, 3] = (qr / np.linalg.norm(qr) * 40).astype(np.float16)
+    out, _, _, _ = ora.decode_attention(qkv, kc, vc, [p], H, D)
+    assert np.allclose(out[0], vc[0, 0, 3].astype(np.float64), rtol=0, atol=1e-6)
+
+
+def pin_attention_library(ora):
+    """torch's float64 scaled_dot_product_attention over the rotated query and
+    the keys and values the step attends to (default scale 1/sqrt(D))."""
+    import torch
+    H, D, S = 4, 32, 20
+    qkv, kc, vc = _attn_case(3, H, D, S, 100)
+    pos = [0, 9, 19]
+    out, _, kn, vn = ora.decode_attention(qkv, kc, vc, pos, H, D)
+    for b, p in enumerate(pos):
+        q = torch.from_numpy(ora.rope(qkv[b, :H * D].astype(np.float64).reshape(H, D), p))
+        K = torch.cat([torch.from_numpy(kc[b, :, :p].astype(np.float64)),
+                       torch.from_numpy(kn[b].astype(np.float16).astype(np.float64))[:, None, :]], dim=1)
+        V = torch.cat([torch.from_numpy(vc[b, :, :p].astype(np.float64)),
+                       torch.from_numpy(vn[b].astype(np.float16).astype(np.float64))[:, None, :]], dim=1)
+        want = torch.nn.functional.scaled_dot_product_attention(q[:, None, :], K, V)[:, 0, :].reshape(-1)
+        assert np.allclose(out[b], want.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def pin_rope_tolerance(ora):
+    """The stored-key bound admits one fp16 rounding and rejects 1%."""
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((64, 128))
+    y = ora.rope(x, 1234)
+    pn = np.repeat(np.hypot(y[:, 0::2], y[:, 1::2]), 2, axis=1)
+    tol = ora.rope_tolerance(y, pn)
+    assert np.all(np.abs(y.astype(np.float16).astype(np.float64) - y) <= tol)
+    big = np.abs(y) > 0.1
+    assert not np.any((np.abs(0.01 * y) <= tol)[big])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,20 @@ MUTATIONS = {
     "residual_not_rounded": ("+ np.asarray(r, dtype=np.float64)).astype(np.float16)",
                              "+ np.asarray(r, dtype=np.float64))"),
     "norm_tolerance_loose": ("return 2e-3 * np.abs(", "return 2e-1 * np.abs("),
+    "rope_sin_sign": ("out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
+    "rope_half_split_pairs": ("x0, x1 = x[..., 0::2], x[..., 1::2]", "x0, x1 = x[..., :D // 2], x[..., D // 2:]"),
+    "rope_frequency_exponent": ("theta = float(base) ** (-2.0 * i / D)", "theta = float(base) ** (-1.0 * i / D)"),
+    "rope_query_position_shifted": ("qr = rope(q, p, base)", "qr = rope(q, p + 1, base)"),
+    "rope_key_not_rotated": ("kr = rope(k, p, base)", "kr = rope(k, 0, base)"),
+    "attention_cache_shifted": ("Kc = np.asarray(k_cache[b, :, :p], dtype=np.float64)",
+                                "Kc = np.asarray(k_cache[b, :, 1:p + 1], dtype=np.float64)"),
+    "attention_new_value_dropped": ("Vall = np.concatenate([Vc, v.astype(np.float16)",
+                                    "Vall = np.concatenate([Vc, 0 * v.astype(np.float16)"),
+    "attention_scale_1_over_d": ("scale = 1.0 / np.sqrt(D)", "scale = 1.0 / D"),
+    "attention_bound_wrong": ("A[b, h * D:(h + 1) * D] = w @ np.abs(Vall[h])",
+                              "A[b, h * D:(h + 1) * D] = np.abs(w @ Vall[h])"),
+    "attention_head_slices_swapped": ("q = qkv[b, 0:H * D].reshape(H, D)", "q = qkv[b, H * D:2 * H * D].reshape(H, D)"),
+    "rope_tolerance_loose": ("return 2.0 ** -11 * np.abs(ref)", "return 2.0 ** -5 * np.abs(ref)"),
 }
 
 
