@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
-                             "quantize_12288x4096", "prologue"])
+                             "quantize_12288x4096", "prologue", "attention"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -297,6 +297,7 @@ def copy_calib():
 
 def extra(args):
     """Other workloads, one JSON line each (for tuning and the design notes)."""
+    import numpy as np
     import torch
     from gemm_w4a16_group_amd import binding as B
     from gemm_w4a16_group_amd import inputs
@@ -328,6 +329,41 @@ def extra(args):
                           "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel": "quantize_kernel"}), flush=True)
+        return
+    if args.workload == "attention":
+        # one decode step of LLaMA-7B attention (32 heads of 128) over a KV
+        # cache of capacity S; copies of the caches cycled through so that
+        # they are read from HBM
+        H, D = 32, 128
+        for Bn, S, lens, bound in ((1, 4096, [512], "tight"), (1, 4096, [2048], "tight"),
+                                   (1, 4096, [4096], "tight"), (1, 4096, [512], "capacity"),
+                                   (8, 2048, [int(v) for v in np.random.default_rng(8).integers(1, 2049, 8)], "tight"),
+                                   (32, 1024, [1024] * 32, "tight")):
+            pos = np.array(lens, dtype=np.int32) - 1
+            max_len = int(pos.max()) + 1 if bound == "tight" else S
+            qkv_h, kc_h, vc_h = inputs.attention_inputs(Bn, H, D, S, wid=9)
+            rd = 2 * int(pos.sum()) * H * D * 2
+            b_alg = rd + Bn * 3 * H * D * 2 + Bn * H * D * 2 + 2 * Bn * H * D * 2
+            cps = max(4, int(1.1e9 // max(rd, 1)))
+            cps = min(cps, max(4, int(8e9 // (2 * kc_h.nbytes))))
+            qkv = torch.from_numpy(qkv_h).cuda()
+            pos_d = torch.from_numpy(pos).cuda()
+            kcs = [torch.from_numpy(kc_h).cuda() for _ in range(cps)]
+            vcs = [torch.from_numpy(vc_h).cuda() for _ in range(cps)]
+            outs = [torch.empty((Bn, H * D), dtype=torch.float16, device="cuda") for _ in range(cps)]
+            calls = [(lambda k=k, v=v, o=o: B.decode_attention(qkv, k, v, pos_d, max_len=max_len, out=o))
+                     for k, v, o in zip(kcs, vcs, outs)]
+            stream = torch.cuda.Stream()
+            g = capture(calls, stream)
+            time_graph(g, 2, stream)
+            reps = max(2, args.steps // cps)
+            us = time_graph(g, reps, stream) / (reps * cps) * 1e3
+            print(json.dumps({"workload": "decode_attention", "B": Bn, "H": H, "D": D, "S": S,
+                              "lengths": lens if Bn <= 8 else "%d x %d" % (Bn, lens[0]), "max_len": max_len,
+                              "us": round(us, 3), "bytes": b_alg, "GB/s": round(b_alg / (us * 1e-6) / 1e9, 1),
+                              "frac_hbm": round(b_alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+            del g, calls, kcs, vcs, outs
+            torch.cuda.empty_cache()
         return
     if args.workload == "prologue":
         # residual add + RMS normalization feeding the QKV and gate/up

@@ -105,6 +105,10 @@ def load_library(path=None):
                                                ctypes.POINTER(Plan), vp, sz, vp]
         lib.w4a16_gemm_add_rmsnorm_workspace_size.restype = sz
         lib.w4a16_gemm_add_rmsnorm_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        lib.w4a16_decode_attention.restype = ctypes.c_int
+        lib.w4a16_decode_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, f32, vp, sz, vp]
+        lib.w4a16_decode_attention_workspace_size.restype = sz
+        lib.w4a16_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64]
         if path is None:
             _lib = lib
         return lib
@@ -363,3 +367,37 @@ def gemm_add_rmsnorm(qpk, s, zpk, x, residual, gamma, eps=1e-6, h=None, out=None
                                         None if plan is None else ctypes.byref(plan), _p(ws), ws_bytes,
                                         _stream()))
     return out, h
+
+
+def decode_attention(qkv, k_cache, v_cache, pos, max_len=None, rope_base=10000.0, scale=None, out=None,
+                     workspace=None):
+    """One decode step of multi-head attention with rotary encoding:
+    qkv fp16 [B, 3 H D] (q | k | v of each sequence's new token), caches fp16
+    [B, H, S, D] (updated at each sequence's position), pos int32 [B] on the
+    device, max_len a bound on pos + 1 (default S).  Returns out [B, H D]."""
+    _need(k_cache, "k_cache", torch.float16)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, H, S, D]")
+    Bn, H, S, D = k_cache.shape
+    _need(v_cache, "v_cache", torch.float16, (Bn, H, S, D))
+    _need(qkv, "qkv", torch.float16, (Bn, 3 * H * D))
+    _need(pos, "pos", torch.int32, (Bn,))
+    if max_len is None:
+        max_len = S
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((Bn, H * D), dtype=torch.float16, device=qkv.device)
+    else:
+        _need(out, "out", torch.float16, (Bn, H * D))
+    need = int(lib().w4a16_decode_attention_workspace_size(Bn, H, D, S, max_len))
+    ws = None
+    if need:
+        if workspace is None:
+            ws = _workspace_for(qkv.device).get(need)
+        else:
+            ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().w4a16_decode_attention(_p(qkv), _p(k_cache), _p(v_cache), _p(pos), _p(out), Bn, H, D, S, max_len,
+                                        float(rope_base), float(scale), _p(ws), ws_bytes, _stream()))
+    return out

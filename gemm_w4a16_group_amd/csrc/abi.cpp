@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <math.h>
 #include <string>
 
 #include "../../include/w4a16.h"
@@ -383,6 +384,44 @@ int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, 
     return ok();
 }
 
+// Decode attention: the head dimension is fixed at 128 (LLaMA-7B); a split
+// along the keys needs the workspace's counters and per-split partials.
+constexpr int64_t kAttnHeadDim = 128;
+
+size_t attn_workspace_bytes(const AttnArgs& a) {
+    const int64_t splits = attn_splits(a, attn_keys_per_wave(a));
+    if (splits <= 1) return 0;
+    return kCounterBytes + (size_t)a.B * (size_t)a.H * (size_t)splits * (kAttnHeadDim + 2) * 4;
+}
+
+int make_attn(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len, float rope_base, float scale,
+              AttnArgs& a) {
+    if (D != kAttnHeadDim) return fail(W4A16_ERR_UNSUPPORTED, "head dimension must be 128, got %lld", (long long)D);
+    if (B < 1 || B > 65535 || H < 1 || H > 65535)
+        return fail(W4A16_ERR_INVALID_ARG, "need 1 <= B, H <= 65535 (B=%lld H=%lld)", (long long)B, (long long)H);
+    if (S < 1 || max_len < 1 || max_len > S || S >= kMaxDim)
+        return fail(W4A16_ERR_INVALID_ARG, "need 1 <= max_len <= S < 2^31 (S=%lld max_len=%lld)", (long long)S,
+                    (long long)max_len);
+    if ((double)B * (double)H * (double)S * (double)D * 2.0 > 9.0e18)
+        return fail(W4A16_ERR_INVALID_ARG, "cache size overflows");
+    if (!(rope_base > 0.f) || rope_base > 3.0e38f)
+        return fail(W4A16_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+    if (!(scale > 0.f) || scale > 3.0e38f) return fail(W4A16_ERR_INVALID_ARG, "scale must be finite and > 0");
+    memset(&a, 0, sizeof(a));
+    a.B = (int32_t)B;
+    a.H = (int32_t)H;
+    a.S = S;
+    a.max_len = max_len;
+    a.theta1 = pow((double)rope_base, -2.0 / (double)D);
+    a.scale = scale;
+    if (attn_splits(a, attn_keys_per_wave(a)) > kAttnMaxSplits)
+        return fail(W4A16_ERR_UNSUPPORTED, "max_len above %lld", (long long)kAttnMaxSplits * 256);
+    if (attn_splits(a, attn_keys_per_wave(a)) > 1 && B * H > kCounterSlots)
+        return fail(W4A16_ERR_UNSUPPORTED, "split attention supports at most %lld (sequence, head) pairs",
+                    (long long)kCounterSlots);
+    return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -584,6 +623,55 @@ int w4a16_gemm_add_rmsnorm(const uint32_t* q_packed, const void* scales, const u
                            size_t workspace_bytes, void* stream) {
     return run_gemm_norm(q_packed, scales, z_packed, x, residual, gamma, eps, h, c, M, N, K, group_size, plan,
                          workspace, workspace_bytes, stream);
+}
+
+size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len) {
+    AttnArgs a;
+    const std::string saved = g_err;
+    const int st = make_attn(B, H, D, S, max_len, 10000.f, 1.f, a);
+    g_err = saved;
+    return st ? 0 : attn_workspace_bytes(a);
+}
+
+int w4a16_decode_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out, int64_t B,
+                           int64_t H, int64_t D, int64_t S, int64_t max_len, float rope_base, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    AttnArgs a;
+    int st = make_attn(B, H, D, S, max_len, rope_base, scale, a);
+    if (st) return st;
+    if (!qkv || !k_cache || !v_cache || !pos || !out) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (((uintptr_t)pos) & 3))
+        return fail(W4A16_ERR_MISALIGNED, "qkv, caches and out must be 16-byte aligned, pos 4-byte aligned");
+    const size_t nq = (size_t)B * 3 * H * D * 2, nc = (size_t)B * H * S * D * 2, no = (size_t)B * H * D * 2,
+                 np = (size_t)B * 4;
+    if (overlaps(out, no, qkv, nq) || overlaps(out, no, k_cache, nc) || overlaps(out, no, v_cache, nc) ||
+        overlaps(out, no, pos, np))
+        return fail(W4A16_ERR_INVALID_ARG, "out overlaps another buffer");
+    if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, qkv, nq) || overlaps(v_cache, nc, qkv, nq) ||
+        overlaps(k_cache, nc, pos, np) || overlaps(v_cache, nc, pos, np))
+        return fail(W4A16_ERR_INVALID_ARG, "a cache overlaps another buffer");
+    const size_t need = attn_workspace_bytes(a);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+        if (overlaps(workspace, need, qkv, nq) || overlaps(workspace, need, k_cache, nc) ||
+            overlaps(workspace, need, v_cache, nc) || overlaps(workspace, need, out, no) ||
+            overlaps(workspace, need, pos, np))
+            return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
+        a.counters = static_cast<uint32_t*>(workspace);
+        a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    }
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.pos = pos;
+    a.out = static_cast<uint16_t*>(out);
+    hipError_t e = launch_decode_attn(a, attn_keys_per_wave(a), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

@@ -1,0 +1,323 @@
+// Fused decode attention: one step of multi-head attention per sequence,
+// with the rotary encoding of q and k, QK^T, the softmax and PV in one
+// kernel (the third fusion of §3.2 of the PerfXLLM page; the rotary
+// encoding read as LLaMA's: channel pairs (2i, 2i + 1) of a head turned by
+// pos * base^(-2i / D)).
+//
+// Layouts (fp16 unless stated):
+//   qkv      [B, 3 H D]     the new token of each sequence, q | k | v
+//   k_cache  [B, H, S, D]   positions 0 .. p - 1 hold earlier keys (rotated)
+//   v_cache  [B, H, S, D]
+//   pos      int32 [B]      position p of the new token
+//   out      [B, H D]
+// The step stores fp16(rope(k, p)) and fp16(v) at position p and attends
+// over keys 0 .. p.  D = 128.
+//
+// HBM-bound on the cache: 2 * 2 D bytes per key.  Grid (splits, H, B): a
+// workgroup of four waves takes 4 * KPW consecutive keys of one head (flash-
+// decoding split along the keys, so that one sequence fills the chip); each
+// wave KPW keys in rounds of 8: lane (key slot lane / 8, channel block
+// lane % 8) owns 16 channels of one key.  A wave issues all of its K and V
+// loads (16 bytes per lane per load, each key's 256 bytes read by 8 adjacent
+// lanes) before any arithmetic, then rotates q while they are in flight.
+// Scores: 16 fp32 FMAs per lane and a 3-step butterfly over the channel
+// blocks.  Softmax with the wave's maximum; values weighted in fp32; partial
+// sums reduced over key slots (butterfly), then over the four waves in LDS.
+// With several splits, each writes (max, sum, o[D]) with agent-coherent
+// stores and the last one of a head to arrive (an arrival counter in the
+// workspace) merges them in split order.
+//
+// Angles: theta_i = theta_1^i from theta_1 = base^(-2/D) (double, from the
+// host), p * theta_i in double, reduced modulo 2 pi in double (two-part
+// constant), then sine and cosine in float32: the rotation is float32-exact
+// to about 1e-7 of the pair's norm at any position.
+#include <math.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr double kTwoPiHi = 6.283185307179586;
+constexpr double kTwoPiLo = 2.4492935982947064e-16;
+constexpr double kInvTwoPi = 0.15915494309189535;
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return (float)as_h2(w)[1]; }
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ uint32_t word_of(const u32x4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// wave-then-workgroup reductions over the 256 threads (every thread gets the result)
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int KPW>
+__global__ void __launch_bounds__(256) decode_attn_kernel(AttnArgs a) {
+    constexpr int R = KPW / 8;   // rounds of 8 keys per wave
+    constexpr int D = kHeadDim;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int part = lane & 7, kslot = lane >> 3;
+    const int H = a.H;
+    const int64_t S = a.S;
+    const int p = a.pos[b];
+    const bool valid = p >= 0 && (int64_t)p < a.max_len;
+    const int64_t slab = ((int64_t)b * H + h) * S * D;
+    const int64_t wg0 = (int64_t)split * 4 * KPW;
+    const int64_t j0 = wg0 + (int64_t)wave * KPW;
+    // a workgroup whose keys all lie past p has nothing to read
+    const bool live = valid && wg0 <= (int64_t)p;
+
+    __shared__ float so[4][D];
+    __shared__ float sm[4], sl[4];
+    __shared__ float red[4];
+    __shared__ int last_flag;
+    float M = -INFINITY, L = 0.f, O = 0.f;   // this workgroup's (max, sum, o[tid])
+
+    if (live) {
+        // ---- 1. every K and V load of the wave; rows past p read row p
+        // (cached, masked below)
+        u32x4 kr[R][2], vr[R][2];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t j = j0 + 8 * r + kslot;
+            j = j < (int64_t)p ? j : (int64_t)p;
+            const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + slab + j * D + 16 * part);
+            kr[r][0] = kp[0];
+            kr[r][1] = kp[1];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t j = j0 + 8 * r + kslot;
+            j = j < (int64_t)p ? j : (int64_t)p;
+            const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + slab + j * D + 16 * part);
+            vr[r][0] = vp[0];
+            vr[r][1] = vp[1];
+        }
+        const uint16_t* row = a.qkv + (int64_t)b * 3 * H * D + (int64_t)h * D + 16 * part;
+        const u32x4 q0 = reinterpret_cast<const u32x4*>(row)[0], q1 = reinterpret_cast<const u32x4*>(row)[1];
+        const u32x4 k0 = reinterpret_cast<const u32x4*>(row + H * D)[0],
+                    k1 = reinterpret_cast<const u32x4*>(row + H * D)[1];
+        const u32x4 v0 = reinterpret_cast<const u32x4*>(row + 2 * H * D)[0],
+                    v1 = reinterpret_cast<const u32x4*>(row + 2 * H * D)[1];
+
+        // ---- 2. rotation of this lane's 8 channel pairs (pairs 8 part .. + 7)
+        float qf[16];
+        uint32_t kn[8];   // the new key, rotated, as stored (fp16 pairs)
+        {
+            const double pd = (double)p;
+            double th = 1.0, pw = a.theta1;
+            for (int e = 8 * part; e; e >>= 1) {   // theta_1^(8 part)
+                if (e & 1) th *= pw;
+                pw *= pw;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const double ang = pd * th;
+                const double kq = rint(ang * kInvTwoPi);
+                double rr = fma(-kq, kTwoPiHi, ang);
+                rr = fma(-kq, kTwoPiLo, rr);
+                float sn, cs;
+                sincosf((float)rr, &sn, &cs);
+                const uint32_t qw = word_of(t < 4 ? q0 : q1, t & 3), kw = word_of(t < 4 ? k0 : k1, t & 3);
+                const float x0 = h2f_lo(qw), x1 = h2f_hi(qw);
+                qf[2 * t] = (x0 * cs - x1 * sn) * a.scale;
+                qf[2 * t + 1] = (x0 * sn + x1 * cs) * a.scale;
+                const float y0 = h2f_lo(kw), y1 = h2f_hi(kw);
+                kn[t] = pack_h2(y0 * cs - y1 * sn, y0 * sn + y1 * cs);
+                th *= a.theta1;
+            }
+        }
+
+        // ---- 3. scores (the new key replaces cache row p)
+        float sc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t j = j0 + 8 * r + kslot;
+            const bool is_new = j == (int64_t)p;
+            float d = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t w = is_new ? kn[t] : word_of(t < 4 ? kr[r][0] : kr[r][1], t & 3);
+                d = fmaf(qf[2 * t], h2f_lo(w), d);
+                d = fmaf(qf[2 * t + 1], h2f_hi(w), d);
+            }
+            d += __shfl_xor(d, 1);
+            d += __shfl_xor(d, 2);
+            d += __shfl_xor(d, 4);
+            sc[r] = j <= (int64_t)p ? d : -INFINITY;
+        }
+        float m = sc[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) m = fmaxf(m, sc[r]);
+        m = fmaxf(m, __shfl_xor(m, 8));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+
+        // ---- 4. weighted values
+        float l = 0.f, o[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t j = j0 + 8 * r + kslot;
+            const bool is_new = j == (int64_t)p;
+            const float w = sc[r] == -INFINITY ? 0.f : __expf(sc[r] - m);
+            l += w;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t vw =
+                    is_new ? word_of(t < 4 ? v0 : v1, t & 3) : word_of(t < 4 ? vr[r][0] : vr[r][1], t & 3);
+                o[2 * t] = fmaf(w, h2f_lo(vw), o[2 * t]);
+                o[2 * t + 1] = fmaf(w, h2f_hi(vw), o[2 * t + 1]);
+            }
+        }
+        // over the eight key slots (lanes of equal part)
+#pragma unroll
+        for (int mk = 8; mk <= 32; mk <<= 1) {
+            l += __shfl_xor(l, mk);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] += __shfl_xor(o[i], mk);
+        }
+
+        // ---- 5. the new token's key and value go into the cache (the eight
+        // lanes of one key slot of one wave)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (j0 + 8 * r + kslot == (int64_t)p) {
+                u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + slab + (int64_t)p * D + 16 * part);
+                u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + slab + (int64_t)p * D + 16 * part);
+                kd[0] = u32x4{kn[0], kn[1], kn[2], kn[3]};
+                kd[1] = u32x4{kn[4], kn[5], kn[6], kn[7]};
+                vd[0] = v0;
+                vd[1] = v1;
+            }
+        }
+
+        // ---- 6. the four waves meet in LDS
+        if (kslot == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) so[wave][16 * part + i] = o[i];
+        }
+        if (lane == 0) {
+            sm[wave] = m;
+            sl[wave] = l;
+        }
+        __syncthreads();
+        M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        float ew[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ew[w] = sm[w] == -INFINITY ? 0.f : __expf(sm[w] - M);
+        L = ((ew[0] * sl[0] + ew[1] * sl[1]) + ew[2] * sl[2]) + ew[3] * sl[3];
+        if (tid < D) O = ((ew[0] * so[0][tid] + ew[1] * so[1][tid]) + ew[2] * so[2][tid]) + ew[3] * so[3][tid];
+    }
+
+    uint16_t* outp = a.out + (int64_t)b * H * D + (int64_t)h * D;
+    const int splits = gridDim.x;
+    if (splits == 1) {
+        // an invalid position leaves L = 0: the output is NaN
+        if (tid < D) outp[tid] = (uint16_t)f32_to_h16_bits(O / L);
+        return;
+    }
+
+    // ---- 7. several splits: partials, then the last arrival merges them
+    const int64_t head = (int64_t)b * H + h;
+    float* part_base = a.part + (head * splits + split) * (D + 2);
+    if (tid < D) __hip_atomic_store(part_base + tid, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == D) __hip_atomic_store(part_base + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == D + 1) __hip_atomic_store(part_base + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == (unsigned)(splits - 1);
+        if (last) __hip_atomic_store(a.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = last;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+
+    // (a) the largest split maximum, (b) the split weights and the total sum,
+    // (c) the weighted values: thread (channel tid % 128, parity tid / 128)
+    // takes every other split, eight loads in flight at a time
+    __shared__ float es[kAttnMaxSplits];
+    __shared__ float oh[2][D];
+    const float* pb = a.part + head * splits * (D + 2);
+    float mx = -INFINITY;
+    for (int s = tid; s < splits; s += 256)
+        mx = fmaxf(mx, __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    mx = block_max(mx, red);
+    float ls = 0.f;
+    for (int s = tid; s < splits; s += 256) {
+        const float ms = __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float ll = __hip_atomic_load(pb + s * (D + 2) + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float e = ms == -INFINITY ? 0.f : __expf(ms - mx);
+        es[s] = e;
+        ls += e * ll;
+    }
+    ls = block_sum(ls, red);   // its barriers also publish es
+    const int ch = tid & (D - 1), par = tid >> 7;
+    float acc = 0.f;
+    for (int s0 = par; s0 < splits; s0 += 16) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = s0 + 2 * i < splits ? s0 + 2 * i : par;
+            v[i] = __hip_atomic_load(pb + s * (D + 2) + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (s0 + 2 * i < splits) acc = fmaf(es[s0 + 2 * i], v[i], acc);
+    }
+    oh[par][ch] = acc;
+    __syncthreads();
+    if (tid < D) outp[tid] = (uint16_t)f32_to_h16_bits((oh[0][tid] + oh[1][tid]) / ls);
+}
+
+}  // namespace
+
+int attn_keys_per_wave(const AttnArgs& a) {
+    // the largest workgroup span that still gives 512 workgroups, at least 16
+    for (int kpw = 64; kpw >= 16; kpw /= 2) {
+        const int64_t splits = (a.max_len + 4 * kpw - 1) / (4 * kpw);
+        if ((int64_t)a.B * a.H * splits >= 512) return kpw;
+    }
+    return 16;
+}
+
+int64_t attn_splits(const AttnArgs& a, int kpw) { return (a.max_len + 4 * kpw - 1) / (4 * kpw); }
+
+hipError_t launch_decode_attn(const AttnArgs& a, int kpw, hipStream_t stream) {
+    const dim3 grid((unsigned)attn_splits(a, kpw), (unsigned)a.H, (unsigned)a.B);
+    switch (kpw) {
+        case 16: hipLaunchKernelGGL(decode_attn_kernel<16>, grid, dim3(256), 0, stream, a); break;
+        case 32: hipLaunchKernelGGL(decode_attn_kernel<32>, grid, dim3(256), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(256), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

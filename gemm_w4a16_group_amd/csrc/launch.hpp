@@ -21,6 +21,21 @@ struct GemmArgs {
     int32_t xp_ready;         // 1: a.xp already holds the activation chunks (no rewrite before the GEMM)
 };
 
+// One decode step of multi-head attention (head dimension 128).
+struct AttnArgs {
+    const uint16_t* qkv;      // [B, 3 H D]: q | k | v of each sequence's new token
+    uint16_t* k_cache;        // [B, H, S, D]
+    uint16_t* v_cache;        // [B, H, S, D]
+    const int32_t* pos;       // [B] position of the new token
+    uint16_t* out;            // [B, H D]
+    float* part;              // [B H, splits, D + 2] partial (o, max, sum) per split
+    uint32_t* counters;       // one arrival counter per (sequence, head)
+    int64_t S, max_len;       // cache capacity; bound on pos + 1 (<= S)
+    int32_t B, H;
+    double theta1;            // base^(-2 / D)
+    float scale;              // softmax scale (1 / sqrt(D) in LLaMA)
+};
+
 struct SkinnyShape {
     int ncol, rb, wm, wk, splitk;
 };
@@ -66,6 +81,13 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream);
 // written in the activation-chunk layout [K/8][N] of the tiled and narrow kernels
 hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* gamma, float eps, uint16_t* h,
                               uint16_t* y, int64_t N, int64_t K, bool chunks, hipStream_t stream);
+
+// decode attention: keys per wave (16, 32 or 64) for the shape, splits along the keys (at most
+// kAttnMaxSplits), launch
+constexpr int kAttnMaxSplits = 1024;
+int attn_keys_per_wave(const AttnArgs& a);
+int64_t attn_splits(const AttnArgs& a, int kpw);
+hipError_t launch_decode_attn(const AttnArgs& a, int kpw, hipStream_t stream);
 
 // fp16 W [M, K] -> q_packed, fp16 scales, z_packed (round to nearest per group)
 hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,

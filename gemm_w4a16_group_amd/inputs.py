@@ -125,3 +125,15 @@ def hidden_states(N, K, wid=0, layer=0, outlier_channels=0.01):
     residual = res[:, 0, :] * np.where(big, np.float32(10.0), np.float32(1.0))[None, :]
     x = res[:, 1, :] * np.float32(0.5)
     return x.astype(np.float16), residual.astype(np.float16), gamma
+
+
+def attention_inputs(B, H, D, S, wid=0, layer=0):
+    """Inputs of one decode step of attention: (qkv fp16 [B, 3 H D],
+    k_cache fp16 [B, H, S, D], v_cache fp16 [B, H, S, D]), all standard
+    normal (drawn in float32, rounded to fp16), so that scores q.k / sqrt(D)
+    have unit spread.  Stream 5 of (wid, layer)."""
+    rng = np.random.default_rng([wid, layer, 0, 5])
+    qkv = rng.standard_normal((B, 3 * H * D), dtype=np.float32).astype(np.float16)
+    kc = rng.standard_normal((B, H, S, D), dtype=np.float32).astype(np.float16)
+    vc = rng.standard_normal((B, H, S, D), dtype=np.float32).astype(np.float16)
+    return qkv, kc, vc

@@ -294,3 +294,31 @@ def test_gemm_add_rmsnorm_checks(lib):
     assert call(plan=ctypes.byref(sk)) == UNSUPPORTED                    # token-major skinny needs N <= 8
     assert lib.w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, 128, ctypes.byref(sk)) == 0
     assert lib.w4a16_gemm_add_rmsnorm_workspace_size(M, N, K, 64, None) == 0
+
+
+def test_decode_attention_checks(lib):
+    qkv, kc, vc, pos, out = (ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(5))
+    ws = ctypes.c_void_p(0x10000000 * 9)
+
+    def call(B=1, H=32, D=128, S=2048, L=2048, base=10000.0, scale=0.088, o=out, k=kc, p=pos, w=ws, wb=1 << 24):
+        return lib.w4a16_decode_attention(qkv, k, vc, p, o, B, H, D, S, L, base, scale, w, wb, NULL)
+
+    assert call(D=64) == UNSUPPORTED
+    assert call(S=300000, L=300000) == UNSUPPORTED   # more than 1024 splits along the keys
+    assert call(B=0) == INVALID
+    assert call(H=70000) == INVALID
+    assert call(L=4096) == INVALID           # max_len above the capacity
+    assert call(L=0) == INVALID
+    assert call(base=0.0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(o=NULL) == INVALID
+    assert call(p=ctypes.c_void_p(0x40000002)) == MISALIGNED
+    assert call(o=ctypes.c_void_p(0x10000000 * 2 + 256)) == INVALID   # out inside the key cache
+    assert call(k=ctypes.c_void_p(0x10000000 * 3 - 4096)) == INVALID  # key cache runs into the value cache
+    need = lib.w4a16_decode_attention_workspace_size(1, 32, 128, 2048, 2048)
+    assert need > 0                          # one sequence: split along the keys
+    assert call(w=NULL, wb=0) == WORKSPACE
+    assert call(wb=need - 1) == WORKSPACE
+    # many sequences fill the chip without a split: no workspace
+    assert lib.w4a16_decode_attention_workspace_size(64, 32, 128, 64, 64) == 0
+    assert lib.w4a16_decode_attention_workspace_size(1, 32, 64, 2048, 2048) == 0   # unsupported D
