@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
-                             "quantize_12288x4096", "prologue", "attention"])
+                             "quantize_12288x4096", "prologue", "attention", "tune_table"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -329,6 +329,40 @@ def extra(args):
                           "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel": "quantize_kernel"}), flush=True)
+        return
+    if args.workload == "tune_table":
+        # the tuner's choice per N for the 12288x4096 projection (cold-cache
+        # timing inside the tuner), then the tuned and the default plan timed
+        # the same way as small_n / large_n (graph of calls over 40 weight
+        # copies), both layouts
+        M, K = 12288, 4096
+        cps = 40
+        lay = Layer(M, K, 10, copies=cps)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for layout in (B.LAYOUT_KN, B.LAYOUT_TOKEN):
+            for N in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 4096):
+                xh = inputs.activations(K, N, wid=10)
+                x = torch.from_numpy(xh.T.copy() if layout == B.LAYOUT_TOKEN else xh).cuda()
+                qpk, sd, zpk = lay.copies[0]
+                tuned, tuner_us, tried = B.tune(qpk, sd, zpk, x, layout=layout, iters=5, flush=flush)
+                shape = (N, M) if layout == B.LAYOUT_TOKEN else (M, N)
+                ncalls = cps if N <= 256 else 4
+                outs = [torch.empty(shape, dtype=torch.float16, device="cuda") for _ in range(ncalls)]
+                res = {}
+                for name, plan in (("default", None), ("tuned", tuned)):
+                    calls = [(lambda c=c, o=o, pl=plan: B.gemm(c[0], c[1], c[2], x, out=o, plan=pl, layout=layout))
+                             for c, o in zip(lay.copies[:ncalls], outs)]
+                    stream = torch.cuda.Stream()
+                    g = capture(calls, stream)
+                    reps = max(2, (args.steps // ncalls) if N <= 256 else 5)
+                    time_graph(g, 2, stream)
+                    res[name] = time_graph(g, reps, stream) / (reps * ncalls) * 1e3
+                    del g
+                print(json.dumps({"workload": "tune_table_12288x4096", "layout": "token" if layout else "kn",
+                                  "N": N, "plans_timed": tried, "tuner_us": round(tuner_us, 3),
+                                  "default_us": round(res["default"], 3), "tuned_us": round(res["tuned"], 3),
+                                  "default": B.plan_default(M, N, K, layout).as_dict(),
+                                  "tuned": tuned.as_dict()}), flush=True)
         return
     if args.workload == "attention":
         # one decode step of LLaMA-7B attention (32 heads of 128) over a KV

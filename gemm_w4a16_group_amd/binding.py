@@ -109,6 +109,10 @@ def load_library(path=None):
         lib.w4a16_decode_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, f32, vp, sz, vp]
         lib.w4a16_decode_attention_workspace_size.restype = sz
         lib.w4a16_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+        lib.w4a16_tune.restype = ctypes.c_int
+        lib.w4a16_tune.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp, sz, i32,
+                                   ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_float),
+                                   ctypes.POINTER(ctypes.c_int32), vp]
         if path is None:
             _lib = lib
         return lib
@@ -401,3 +405,24 @@ def decode_attention(qkv, k_cache, v_cache, pos, max_len=None, rope_base=10000.0
     _check(lib().w4a16_decode_attention(_p(qkv), _p(k_cache), _p(v_cache), _p(pos), _p(out), Bn, H, D, S, max_len,
                                         float(rope_base), float(scale), _p(ws), ws_bytes, _stream()))
     return out
+
+
+def tune(qpk, s, zpk, x, layout=LAYOUT_KN, iters=20, flush=None, workspace_bytes=None):
+    """Time the candidate plans of this call's shape on the device (the
+    library's tuner) and return (plan, microseconds per call, plans timed).
+    flush: an optional device tensor overwritten before every timed call
+    (cold-cache timing).  The workspace is the stream's default one, grown
+    to the largest candidate's need (or to workspace_bytes)."""
+    M, N, K = _dims(qpk, s, zpk, x, layout)
+    out = torch.empty((N, M) if layout == LAYOUT_TOKEN else (M, N), dtype=torch.float16, device=x.device)
+    if workspace_bytes is None:
+        workspace_bytes = (64 << 10) + 8 * M * N * 4 + 2 * K * N + 4096
+    ws = _workspace_for(x.device).get(workspace_bytes)
+    best = Plan()
+    us = ctypes.c_float()
+    n = ctypes.c_int32()
+    fb = 0 if flush is None else flush.numel() * flush.element_size()
+    _check(lib().w4a16_tune(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP, layout, _p(ws),
+                            ws.numel() * ws.element_size(), _p(flush), fb, int(iters), ctypes.byref(best),
+                            ctypes.byref(us), ctypes.byref(n), _stream()))
+    return best, float(us.value), int(n.value)

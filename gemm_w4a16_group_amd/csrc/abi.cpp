@@ -12,6 +12,7 @@
 
 #include <math.h>
 #include <string>
+#include <vector>
 
 #include "../../include/w4a16.h"
 #include "launch.hpp"
@@ -301,6 +302,69 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
                                                      : launch_tiled(a, tiled_of(p), s);
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+// Candidate plans for the tuner: every kernel family that can take the
+// shape, over the plan fields that matter (the default plan first).
+std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
+    std::vector<w4a16_plan> out;
+    auto add = [&](w4a16_plan p) {
+        const std::string saved = g_err;
+        const int st = check_plan(a, p);
+        g_err = saved;
+        if (st == W4A16_OK) out.push_back(p);
+    };
+    w4a16_plan p;
+    memset(&p, 0, sizeof(p));
+    add(default_plan(a.M, a.N, a.K, a.tm ? W4A16_LAYOUT_TOKEN : W4A16_LAYOUT_KN));
+    const int64_t N = a.N;
+    if (skinny_columns(N)) {
+        for (int wm : {1, 2, 4})
+            for (int wk : {1, 2, 4, 8, 16})
+                for (int splitk : {1, 2, 3, 4}) {
+                    if (wm * wk > 16) continue;
+                    memset(&p, 0, sizeof(p));
+                    p.kernel = W4A16_KERNEL_SKINNY;
+                    p.ncol = (int32_t)N;
+                    p.rb = 1;
+                    p.wm = wm;
+                    p.wk = wk;
+                    p.splitk = splitk;
+                    add(p);
+                }
+    }
+    if (N <= 64) {
+        for (int ncol : {16, 32, 64})
+            for (int pf : {8, 16})
+                for (int rb : {1, 2})
+                    for (int wk : {1, 2, 4})
+                        for (int splitk : {1, 2, 3, 4, 6, 8}) {
+                            if (ncol < N) continue;
+                            memset(&p, 0, sizeof(p));
+                            p.kernel = W4A16_KERNEL_NARROW;
+                            p.ncol = ncol;
+                            p.pf = pf;
+                            p.rb = rb;
+                            p.wk = wk;
+                            p.splitk = splitk;
+                            add(p);
+                        }
+    }
+    if (N >= 8) {
+        for (int bm : {128, 256})
+            for (int bn : {64, 128, 256})
+                for (int wm : {4, 2})
+                    for (int splitk : {1, 2, 4}) {
+                        memset(&p, 0, sizeof(p));
+                        p.kernel = W4A16_KERNEL_TILED;
+                        p.bm = bm;
+                        p.bn = bn;
+                        p.wm = wm;
+                        p.splitk = splitk;
+                        add(p);
+                    }
+    }
+    return out;
 }
 
 // Residual add + RMS normalization feeding the GEMM (token-major).  The
@@ -671,6 +735,70 @@ int w4a16_decode_attention(const void* qkv, void* k_cache, void* v_cache, const 
     a.out = static_cast<uint16_t*>(out);
     hipError_t e = launch_decode_attn(a, attn_keys_per_wave(a), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int w4a16_tune(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x, void* c,
+               int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, void* workspace,
+               size_t workspace_bytes, void* flush, size_t flush_bytes, int32_t iters, w4a16_plan* best,
+               float* best_us, int32_t* n_tried, void* stream) {
+    int st = check_dims(M, N, K, group_size);
+    if (st) return st;
+    st = check_layout(layout);
+    if (st) return st;
+    if (!best) return fail(W4A16_ERR_INVALID_ARG, "best is NULL");
+    if (iters < 1 || iters > 100000) return fail(W4A16_ERR_INVALID_ARG, "iters must be in 1..100000");
+    if (flush && (flush_bytes == 0 || !aligned16(flush)))
+        return fail(W4A16_ERR_INVALID_ARG, "flush buffer must be 16-byte aligned and non-empty");
+    const GemmArgs a = make_args(M, N, K, layout);
+    const std::vector<w4a16_plan> cands = candidate_plans(a);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return fail(W4A16_ERR_HIP, "hipEventCreate failed");
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        hipEventDestroy(ev[0]);
+        return fail(W4A16_ERR_HIP, "hipEventCreate failed");
+    }
+    float best_t = 0.f;
+    int tried = 0;
+    w4a16_plan winner;
+    memset(&winner, 0, sizeof(winner));
+    int status = W4A16_OK;
+    for (const w4a16_plan& p : cands) {
+        if (workspace_bytes_for(a, p) > (workspace ? workspace_bytes : 0)) continue;
+        // one untimed call (also validates every argument)
+        status = run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, layout, &p, workspace,
+                          workspace_bytes, stream);
+        if (status) break;
+        float total = 0.f;
+        for (int i = 0; i < iters && !status; ++i) {
+            if (flush && hipMemsetAsync(flush, i & 0xFF, flush_bytes, s) != hipSuccess)
+                status = fail(W4A16_ERR_HIP, "flush failed");
+            if (!status && hipEventRecord(ev[0], s) != hipSuccess) status = fail(W4A16_ERR_HIP, "event record failed");
+            if (!status)
+                status = run_gemm(q_packed, scales, z_packed, x, c, M, N, K, group_size, layout, &p, workspace,
+                                  workspace_bytes, stream);
+            if (!status && hipEventRecord(ev[1], s) != hipSuccess) status = fail(W4A16_ERR_HIP, "event record failed");
+            float ms = 0.f;
+            if (!status && (hipEventSynchronize(ev[1]) != hipSuccess || hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess))
+                status = fail(W4A16_ERR_HIP, "event timing failed");
+            total += ms;
+        }
+        if (status) break;
+        const float us = total * 1e3f / (float)iters;
+        if (tried == 0 || us < best_t) {
+            best_t = us;
+            winner = p;
+        }
+        ++tried;
+    }
+    hipEventDestroy(ev[0]);
+    hipEventDestroy(ev[1]);
+    if (status) return status;
+    if (tried == 0) return fail(W4A16_ERR_WORKSPACE, "no candidate plan fits the %zu-byte workspace", workspace_bytes);
+    *best = winner;
+    if (best_us) *best_us = best_t;
+    if (n_tried) *n_tried = tried;
     return ok();
 }
 

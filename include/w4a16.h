@@ -203,6 +203,32 @@ int w4a16_gemm_plan(const uint32_t *q_packed, const void *scales,
                     size_t workspace_bytes, void *stream);
 
 /*
+ * Plan tuner, the "parameter tuning" of PerfXLLM §3.3 item 1: times the
+ * candidate plans of this shape and layout on the caller's buffers and
+ * returns the fastest.  Candidates: the default plan first, then skinny,
+ * narrow and tiled plans over their fields (those the shape admits); plans
+ * needing more than workspace_bytes are skipped.  Each candidate runs once
+ * untimed, then iters times, each timed call bracketed by HIP events on
+ * `stream`.  flush (optional, device memory, 16-byte aligned): flush_bytes
+ * of it are overwritten before every timed call, so that the weights come
+ * from HBM and not from the last-level cache (give more than 256 MB on
+ * MI355X); NULL times warm calls.
+ *   best    : out, the fastest plan
+ *   best_us : out, its mean microseconds per call (may be NULL)
+ *   n_tried : out, the number of plans timed (may be NULL)
+ * Unlike every other entry point this one synchronizes the stream, writes c
+ * and the workspace many times, and must not be called during graph
+ * capture.  W4A16_ERR_WORKSPACE if no candidate fits the workspace; other
+ * checks as w4a16_gemm_ex.
+ */
+int w4a16_tune(const uint32_t *q_packed, const void *scales,
+               const uint32_t *z_packed, const void *x, void *c, int64_t M,
+               int64_t N, int64_t K, int32_t group_size, int32_t layout,
+               void *workspace, size_t workspace_bytes, void *flush,
+               size_t flush_bytes, int32_t iters, w4a16_plan *best,
+               float *best_us, int32_t *n_tried, void *stream);
+
+/*
  * Activation and output layouts for the _ex entry points.
  *   W4A16_LAYOUT_KN    : x fp16 [K, N] and c fp16 [M, N] (the product of
  *                        PerfXLLM §3.3 item 1 as written; what w4a16_gemm

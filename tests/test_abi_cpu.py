@@ -322,3 +322,20 @@ def test_decode_attention_checks(lib):
     # many sequences fill the chip without a split: no workspace
     assert lib.w4a16_decode_attention_workspace_size(64, 32, 128, 64, 64) == 0
     assert lib.w4a16_decode_attention_workspace_size(1, 32, 64, 2048, 2048) == 0   # unsupported D
+
+
+def test_tune_checks(lib):
+    best = B.Plan()
+    us = ctypes.c_float()
+    n = ctypes.c_int32()
+
+    def call(iters=5, bp=ctypes.byref(best), layout=0, flush=NULL, fb=0, g=128):
+        return lib.w4a16_tune(Q, S, Z, X, C, 64, 4, 256, g, layout, WS, 1 << 20, flush, fb, iters, bp,
+                              ctypes.byref(us), ctypes.byref(n), NULL)
+
+    assert call(iters=0) == INVALID
+    assert call(bp=None) == INVALID
+    assert call(layout=5) == INVALID
+    assert call(g=64) == UNSUPPORTED
+    assert call(flush=ctypes.c_void_p(0x700008), fb=4096) == INVALID
+    assert call(flush=ctypes.c_void_p(0x700000), fb=0) == INVALID
