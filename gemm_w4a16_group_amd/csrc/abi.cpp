@@ -106,8 +106,8 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // so that all of a wave's weight loads are in flight at once, and a split
 // across workgroups only when the staged activations would not fit in LDS.
 //
-// Tiled kernel otherwise: 256 x 128 tiles from N = 4096 on, 128 x 128 from
-// N = 512, 128 x 64 below; a split along K only when there are too few
+// Tiled kernel otherwise: 256 x 128 tiles from N = 4096 on (from N = 1024
+// when that still gives 256 tiles), 128 x 128 from N = 512, 128 x 64 below; a split along K only when there are too few
 // tiles to fill the chip (N <= 32: two-way, four-way under 64 tiles; larger
 // N: two-way for long rows, K >= 8192).
 //
@@ -148,8 +148,13 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
             int64_t wk = (ngs + 4) / 8;
             if (wk < 1) wk = 1;
             while (wk * p.wm > 16) wk /= 2;
-            // small grids: more waves along K (at least two groups each)
-            while (wk * 2 * p.wm <= 16 && tiles * splitk * p.wm * wk < 2048 && ngs >= 4 * wk) wk *= 2;
+            // small grids: more waves along K (at least two groups each);
+            // from three columns on, up to twice as many while every wave
+            // keeps four groups (measured at 12288x4096)
+            while (wk * 2 * p.wm <= 16 && ngs >= 4 * wk &&
+                   (tiles * splitk * p.wm * wk < 2048 ||
+                    (N >= 3 && tiles * splitk * p.wm * wk < 4096 && ngs >= 8 * wk)))
+                wk *= 2;
             p.wk = (int32_t)wk;
             p.splitk = (int32_t)splitk;
             if (splitk > 1 && tiles > kCounterSlots) break;
@@ -162,7 +167,8 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     }
     p.kernel = W4A16_KERNEL_TILED;
     p.wm = 4;
-    p.bm = N >= 4096 ? 256 : 128;
+    // 256-row tiles from N = 1024 on when they still give 256 tiles
+    p.bm = (N >= 4096 || (N >= 1024 && ((M + 255) / 256) * ((N + 127) / 128) >= 256)) ? 256 : 128;
     p.bn = N >= 512 ? 128 : 64;
     const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     int64_t splitk = 1;

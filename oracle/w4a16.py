@@ -335,3 +335,27 @@ def rope_tolerance(ref, pair_norm):
     float32 rotation of the pair (1e-6 of its norm) and the fp16 subnormal
     half-spacing (6e-8)."""
     return 2.0 ** -11 * np.abs(ref) + 1e-6 * pair_norm + 6e-8
+
+
+def silu_mul(gu):
+    """The gated activation of LLaMA's MLP on the fused gate/up projection's
+    output, in float64: gu is [N, 2 I] with the gate in columns 0 .. I - 1
+    and the up projection in I .. 2 I - 1 (the fused 22016 = 2 x 11008 rows
+    of the gate/up weight, gate rows first);
+
+      act[n, i] = silu(g) * u,  silu(g) = g / (1 + exp(-g)).
+
+    The pages do not describe the MLP; this is the LLaMA-7B reading.
+    """
+    gu = np.asarray(gu, dtype=np.float64)
+    I = gu.shape[1] // 2
+    if gu.shape[1] != 2 * I:
+        raise ValueError("gu must have an even number of columns")
+    g, u = gu[:, :I], gu[:, I:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def silu_mul_tolerance(ref):
+    """Bound on an fp16 activation: one fp16 rounding (2^-11 |ref|), float32
+    exp and divide (below 1e-6 relative), doubled; absolute floor 1e-6."""
+    return 1e-3 * np.abs(np.asarray(ref, dtype=np.float64)) + 1e-6

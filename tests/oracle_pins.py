@@ -578,4 +578,44 @@ def pin_rope_tolerance(ora):
     assert not np.any((np.abs(0.01 * y) <= tol)[big])
 
 
+
+# ----------------------------------------------------------------------------
+# gated MLP activation (the decoder layer's silu(gate) * up)
+
+def pin_silu_mul_closed_forms(ora):
+    """silu(0) = 0, silu(g) - silu(-g) = g (the logistic function's symmetry),
+    silu(g) -> g for large g and -> 0 for very negative g; gate and up are the
+    first and second halves of a row."""
+    g = np.array([0.0, 1.0, -1.0, 2.5, 40.0, -40.0])
+    one = np.ones_like(g)
+    gu = np.stack([np.concatenate([g, one]), np.concatenate([-g, one])])
+    a = ora.silu_mul(gu)
+    assert a[0, 0] == 0.0
+    assert np.allclose(a[0] - a[1], g, rtol=0, atol=1e-12)
+    assert abs(a[0, 4] - 40.0) < 1e-12 and abs(a[0, 5]) < 1e-15
+    assert abs(a[0, 1] - 1.0 / (1.0 + np.exp(-1.0))) < 1e-15
+    up = np.arange(1.0, 7.0)
+    a2 = ora.silu_mul(np.concatenate([np.full(6, 1.0), up])[None, :])
+    assert np.allclose(a2[0], up / (1.0 + np.exp(-1.0)), rtol=1e-15)
+
+
+def pin_silu_mul_library(ora):
+    """torch's float64 silu times the up half."""
+    import torch
+    rng = np.random.default_rng(102)
+    gu = (rng.standard_normal((3, 512)) * 4).astype(np.float16)
+    t = torch.from_numpy(gu.astype(np.float64))
+    want = (torch.nn.functional.silu(t[:, :256]) * t[:, 256:]).numpy()
+    assert np.allclose(ora.silu_mul(gu), want, rtol=1e-14, atol=1e-300)
+
+
+def pin_silu_mul_tolerance(ora):
+    rng = np.random.default_rng(103)
+    ref = ora.silu_mul(rng.standard_normal((4, 256)) * 3)
+    tol = ora.silu_mul_tolerance(ref)
+    assert np.all(np.abs(ref.astype(np.float16).astype(np.float64) - ref) <= tol)
+    big = np.abs(ref) > 0.1
+    assert not np.any((np.abs(0.01 * ref) <= tol)[big])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -70,6 +70,10 @@ MUTATIONS = {
                               "A[b, h * D:(h + 1) * D] = np.abs(w @ Vall[h])"),
     "attention_head_slices_swapped": ("q = qkv[b, 0:H * D].reshape(H, D)", "q = qkv[b, H * D:2 * H * D].reshape(H, D)"),
     "rope_tolerance_loose": ("return 2.0 ** -11 * np.abs(ref)", "return 2.0 ** -5 * np.abs(ref)"),
+    "silu_sigmoid_sign": ("return g / (1.0 + np.exp(-g)) * u", "return g / (1.0 + np.exp(g)) * u"),
+    "silu_halves_swapped": ("g, u = gu[:, :I], gu[:, I:]", "u, g = gu[:, :I], gu[:, I:]"),
+    "silu_no_gate": ("return g / (1.0 + np.exp(-g)) * u", "return 1.0 / (1.0 + np.exp(-g)) * u"),
+    "silu_tolerance_loose": ("return 1e-3 * np.abs(np.asarray(ref", "return 1e-1 * np.abs(np.asarray(ref"),
 }
 
 
