@@ -53,6 +53,16 @@ class Plan(ctypes.Structure):
         return p
 
 
+class Linear(ctypes.Structure):
+    _fields_ = [("q_packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("z_packed", ctypes.c_void_p)]
+
+
+class DecoderLayer(ctypes.Structure):
+    _fields_ = [("qkv", Linear), ("o", Linear), ("gate_up", Linear), ("down", Linear),
+                ("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
 def load_library(path=None):
     """Load (once) and return the ctypes handle of libw4a16.so."""
     global _lib
@@ -113,6 +123,13 @@ def load_library(path=None):
         lib.w4a16_tune.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp, sz, i32,
                                    ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_float),
                                    ctypes.POINTER(ctypes.c_int32), vp]
+        lib.w4a16_silu_mul.restype = ctypes.c_int
+        lib.w4a16_silu_mul.argtypes = [vp, vp, i64, i64, vp]
+        lib.w4a16_decode_layer.restype = ctypes.c_int
+        lib.w4a16_decode_layer.argtypes = [ctypes.POINTER(DecoderLayer), i64, i64, i64, i64, i64, i64, vp, f32, f32,
+                                           vp, vp, vp, sz, vp]
+        lib.w4a16_decode_layer_workspace_size.restype = sz
+        lib.w4a16_decode_layer_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
         if path is None:
             _lib = lib
         return lib
@@ -426,3 +443,54 @@ def tune(qpk, s, zpk, x, layout=LAYOUT_KN, iters=20, flush=None, workspace_bytes
                             ws.numel() * ws.element_size(), _p(flush), fb, int(iters), ctypes.byref(best),
                             ctypes.byref(us), ctypes.byref(n), _stream()))
     return best, float(us.value), int(n.value)
+
+
+def silu_mul(gu, out=None):
+    """act[N, I] = silu(gu[:, :I]) * gu[:, I:] (fp16, token-major)."""
+    _need(gu, "gu", torch.float16)
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [N, 2 I]")
+    N, I = gu.shape[0], gu.shape[1] // 2
+    if out is None:
+        out = torch.empty((N, I), dtype=torch.float16, device=gu.device)
+    else:
+        _need(out, "out", torch.float16, (N, I))
+    _check(lib().w4a16_silu_mul(_p(gu), _p(out), N, I, _stream()))
+    return out
+
+
+def decode_layer_workspace_size(B, H, D, I, S, max_len):
+    return int(lib().w4a16_decode_layer_workspace_size(B, H, D, I, S, max_len))
+
+
+def _linear(w):
+    qpk, s, zpk = w
+    _need(qpk, "q_packed", torch.int32)
+    _need(s, "scales", torch.float16)
+    _need(zpk, "z_packed", torch.int32)
+    return Linear(_p(qpk), _p(s), _p(zpk))
+
+
+def decode_layer(layer, pos, residual, x, workspace, max_len=None, eps=1e-6, rope_base=10000.0):
+    """One decode step of one decoder layer (w4a16_decode_layer).  layer: a
+    dict with "qkv", "o", "gate_up", "down" (each (q_packed, scales,
+    z_packed)), "attn_norm", "mlp_norm", "k_cache", "v_cache".  residual and
+    x (fp16 [B, H D]) are updated in place; workspace is a zero-initialised
+    uint8 device tensor of at least decode_layer_workspace_size() bytes."""
+    kc = layer["k_cache"]
+    _need(kc, "k_cache", torch.float16)
+    Bn, H, S, D = kc.shape
+    _need(layer["v_cache"], "v_cache", torch.float16, (Bn, H, S, D))
+    gu_rows = layer["gate_up"][0].shape[0]
+    I = gu_rows // 2
+    _need(layer["attn_norm"], "attn_norm", torch.float16, (H * D,))
+    _need(layer["mlp_norm"], "mlp_norm", torch.float16, (H * D,))
+    _need(residual, "residual", torch.float16, (Bn, H * D))
+    _need(x, "x", torch.float16, (Bn, H * D))
+    _need(pos, "pos", torch.int32, (Bn,))
+    _need(workspace, "workspace", torch.uint8)
+    st = DecoderLayer(_linear(layer["qkv"]), _linear(layer["o"]), _linear(layer["gate_up"]), _linear(layer["down"]),
+                      _p(layer["attn_norm"]), _p(layer["mlp_norm"]), _p(kc), _p(layer["v_cache"]))
+    _check(lib().w4a16_decode_layer(ctypes.byref(st), Bn, H, D, I, S, S if max_len is None else max_len, _p(pos),
+                                    float(eps), float(rope_base), _p(residual), _p(x), _p(workspace),
+                                    workspace.numel(), _stream()))

@@ -259,9 +259,11 @@ int check_layout(int32_t layout) {
     return W4A16_OK;
 }
 
+// dry: check everything, launch nothing (a composite call validates all of
+// its steps before it enqueues the first one)
 int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, void* c,
              int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, const w4a16_plan* plan_in,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream, bool dry = false) {
     int st = check_dims(M, N, K, group_size);
     if (st) return st;
     st = check_layout(layout);
@@ -301,6 +303,7 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
     a.zpk = zpk;
     a.x = static_cast<const uint16_t*>(x);
     a.c = static_cast<uint16_t*>(c);
+    if (dry) return ok();
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = p.kernel == W4A16_KERNEL_SKINNY   ? launch_skinny(a, skinny_of(p), s)
@@ -390,7 +393,7 @@ bool bad_stream_alias(const void* h, const void* r, size_t n) { return h != r &&
 int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, const void* residual,
                   const void* gamma, float eps, void* h, void* c, int64_t M, int64_t N, int64_t K,
                   int32_t group_size, const w4a16_plan* plan_in, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, bool dry = false) {
     int st = check_dims(M, N, K, group_size);
     if (st) return st;
     st = check_eps(eps);
@@ -441,6 +444,7 @@ int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, 
     } else {
         a.x = y;   // the skinny kernel reads the normalized rows [N, K]
     }
+    if (dry) return ok();
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_add_rmsnorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(residual),
@@ -490,6 +494,160 @@ int make_attn(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len, float
         return fail(W4A16_ERR_UNSUPPORTED, "split attention supports at most %lld (sequence, head) pairs",
                     (long long)kCounterSlots);
     return W4A16_OK;
+}
+
+int run_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out, int64_t B, int64_t H,
+                  int64_t D, int64_t S, int64_t max_len, float rope_base, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream, bool dry = false) {
+    AttnArgs a;
+    int st = make_attn(B, H, D, S, max_len, rope_base, scale, a);
+    if (st) return st;
+    if (!qkv || !k_cache || !v_cache || !pos || !out) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (((uintptr_t)pos) & 3))
+        return fail(W4A16_ERR_MISALIGNED, "qkv, caches and out must be 16-byte aligned, pos 4-byte aligned");
+    const size_t nq = (size_t)B * 3 * H * D * 2, nc = (size_t)B * H * S * D * 2, no = (size_t)B * H * D * 2,
+                 np = (size_t)B * 4;
+    if (overlaps(out, no, qkv, nq) || overlaps(out, no, k_cache, nc) || overlaps(out, no, v_cache, nc) ||
+        overlaps(out, no, pos, np))
+        return fail(W4A16_ERR_INVALID_ARG, "out overlaps another buffer");
+    if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, qkv, nq) || overlaps(v_cache, nc, qkv, nq) ||
+        overlaps(k_cache, nc, pos, np) || overlaps(v_cache, nc, pos, np))
+        return fail(W4A16_ERR_INVALID_ARG, "a cache overlaps another buffer");
+    const size_t need = attn_workspace_bytes(a);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+        if (overlaps(workspace, need, qkv, nq) || overlaps(workspace, need, k_cache, nc) ||
+            overlaps(workspace, need, v_cache, nc) || overlaps(workspace, need, out, no) ||
+            overlaps(workspace, need, pos, np))
+            return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
+        a.counters = static_cast<uint32_t*>(workspace);
+        a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    }
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.pos = pos;
+    a.out = static_cast<uint16_t*>(out);
+    if (dry) return ok();
+    hipError_t e = launch_decode_attn(a, attn_keys_per_wave(a), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+
+int run_silu_mul(const void* gu, void* act, int64_t N, int64_t I, void* stream, bool dry = false) {
+    if (N < 1 || N >= kMaxDim || I < 8 || I % 8 || I >= kMaxDim / 2)
+        return fail(W4A16_ERR_INVALID_ARG, "need N >= 1, I >= 8, I %% 8 == 0 (N=%lld I=%lld)", (long long)N,
+                    (long long)I);
+    if (!gu || !act) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    if (!aligned16(gu) || !aligned16(act)) return fail(W4A16_ERR_MISALIGNED, "gu and act must be 16-byte aligned");
+    if (overlaps(gu, (size_t)N * I * 4, act, (size_t)N * I * 2))
+        return fail(W4A16_ERR_INVALID_ARG, "act overlaps gu");
+    if (dry) return ok();
+    hipError_t e = launch_silu_mul(static_cast<const uint16_t*>(gu), static_cast<uint16_t*>(act), N, I,
+                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Decoder layer workspace: [shared region: the largest workspace any step
+// needs, steps run one after another][qkv][attention output][gate/up][act],
+// each at a 256-byte boundary.
+struct LayerLayout {
+    size_t shared, qkv, attn, gu, act, total;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int layer_layout(int64_t B, int64_t H, int64_t D, int64_t I, int64_t S, int64_t max_len, LayerLayout& L) {
+    AttnArgs aa;
+    int st = make_attn(B, H, D, S, max_len, 10000.f, 1.f, aa);
+    if (st) return st;
+    if (I < 128 || I % 128 || I >= kMaxDim / 2)
+        return fail(W4A16_ERR_INVALID_ARG, "I must be a positive multiple of 128, got %lld", (long long)I);
+    const int64_t HD = H * D;
+    st = check_dims(3 * HD, B, HD, kGroupSize);
+    if (!st) st = check_dims(2 * I, B, HD, kGroupSize);
+    if (!st) st = check_dims(HD, B, I, kGroupSize);
+    if (st) return st;
+    size_t shared = attn_workspace_bytes(aa);
+    auto grow = [&](size_t v) { shared = v > shared ? v : shared; };
+    {
+        const GemmArgs a = make_args(3 * HD, B, HD, W4A16_LAYOUT_TOKEN);
+        grow(norm_workspace_bytes(a, default_plan(3 * HD, B, HD, W4A16_LAYOUT_TOKEN)));
+    }
+    {
+        const GemmArgs a = make_args(HD, B, HD, W4A16_LAYOUT_TOKEN);
+        grow(workspace_bytes_for(a, default_plan(HD, B, HD, W4A16_LAYOUT_TOKEN)));
+    }
+    {
+        const GemmArgs a = make_args(2 * I, B, HD, W4A16_LAYOUT_TOKEN);
+        grow(norm_workspace_bytes(a, default_plan(2 * I, B, HD, W4A16_LAYOUT_TOKEN)));
+    }
+    {
+        const GemmArgs a = make_args(HD, B, I, W4A16_LAYOUT_TOKEN);
+        grow(workspace_bytes_for(a, default_plan(HD, B, I, W4A16_LAYOUT_TOKEN)));
+    }
+    grow(kCounterBytes);
+    L.shared = round256(shared);
+    L.qkv = L.shared;
+    L.attn = L.qkv + round256((size_t)B * 3 * HD * 2);
+    L.gu = L.attn + round256((size_t)B * HD * 2);
+    L.act = L.gu + round256((size_t)B * 2 * I * 2);
+    L.total = L.act + round256((size_t)B * I * 2);
+    return W4A16_OK;
+}
+
+int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_t D, int64_t I, int64_t S,
+                     int64_t max_len, const int32_t* pos, float eps, float rope_base, void* residual, void* x,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!ly) return fail(W4A16_ERR_INVALID_ARG, "layer is NULL");
+    LayerLayout L;
+    int st = layer_layout(B, H, D, I, S, max_len, L);
+    if (st) return st;
+    if (!workspace || workspace_bytes < L.total)
+        return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    if (!residual || !x) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
+    const size_t nh = (size_t)B * H * D * 2;
+    if (overlaps(residual, nh, x, nh)) return fail(W4A16_ERR_INVALID_ARG, "residual overlaps x");
+    if (overlaps(workspace, L.total, residual, nh) || overlaps(workspace, L.total, x, nh))
+        return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps residual or x");
+    char* w = static_cast<char*>(workspace);
+    void* shared = w;
+    void* qkv = w + L.qkv;
+    void* attn = w + L.attn;
+    void* gu = w + L.gu;
+    void* act = w + L.act;
+    const int64_t HD = H * D;
+    const float scale = (float)(1.0 / sqrt((double)D));
+    // every step checked first (dry), then enqueued
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool dry = pass == 0;
+        st = run_gemm_norm(ly->qkv.q_packed, ly->qkv.scales, ly->qkv.z_packed, x, residual, ly->attn_norm, eps,
+                           residual, qkv, 3 * HD, B, HD, kGroupSize, nullptr, shared, L.shared, stream, dry);
+        if (!st)
+            st = run_attention(qkv, ly->k_cache, ly->v_cache, pos, attn, B, H, D, S, max_len, rope_base, scale,
+                               shared, L.shared, stream, dry);
+        if (!st)
+            st = run_gemm(ly->o.q_packed, ly->o.scales, ly->o.z_packed, attn, x, HD, B, HD, kGroupSize,
+                          W4A16_LAYOUT_TOKEN, nullptr, shared, L.shared, stream, dry);
+        if (!st)
+            st = run_gemm_norm(ly->gate_up.q_packed, ly->gate_up.scales, ly->gate_up.z_packed, x, residual,
+                               ly->mlp_norm, eps, residual, gu, 2 * I, B, HD, kGroupSize, nullptr, shared, L.shared,
+                               stream, dry);
+        if (!st) st = run_silu_mul(gu, act, B, I, stream, dry);
+        if (!st)
+            st = run_gemm(ly->down.q_packed, ly->down.scales, ly->down.z_packed, act, x, HD, B, I, kGroupSize,
+                          W4A16_LAYOUT_TOKEN, nullptr, shared, L.shared, stream, dry);
+        if (st) return st;
+    }
+    return ok();
 }
 
 }  // namespace
@@ -706,42 +864,27 @@ size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D, in
 int w4a16_decode_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out, int64_t B,
                            int64_t H, int64_t D, int64_t S, int64_t max_len, float rope_base, float scale,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    AttnArgs a;
-    int st = make_attn(B, H, D, S, max_len, rope_base, scale, a);
-    if (st) return st;
-    if (!qkv || !k_cache || !v_cache || !pos || !out) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
-    if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        (((uintptr_t)pos) & 3))
-        return fail(W4A16_ERR_MISALIGNED, "qkv, caches and out must be 16-byte aligned, pos 4-byte aligned");
-    const size_t nq = (size_t)B * 3 * H * D * 2, nc = (size_t)B * H * S * D * 2, no = (size_t)B * H * D * 2,
-                 np = (size_t)B * 4;
-    if (overlaps(out, no, qkv, nq) || overlaps(out, no, k_cache, nc) || overlaps(out, no, v_cache, nc) ||
-        overlaps(out, no, pos, np))
-        return fail(W4A16_ERR_INVALID_ARG, "out overlaps another buffer");
-    if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, qkv, nq) || overlaps(v_cache, nc, qkv, nq) ||
-        overlaps(k_cache, nc, pos, np) || overlaps(v_cache, nc, pos, np))
-        return fail(W4A16_ERR_INVALID_ARG, "a cache overlaps another buffer");
-    const size_t need = attn_workspace_bytes(a);
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need)
-            return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                        workspace ? workspace_bytes : (size_t)0);
-        if (!aligned16(workspace)) return fail(W4A16_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-        if (overlaps(workspace, need, qkv, nq) || overlaps(workspace, need, k_cache, nc) ||
-            overlaps(workspace, need, v_cache, nc) || overlaps(workspace, need, out, no) ||
-            overlaps(workspace, need, pos, np))
-            return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
-        a.counters = static_cast<uint32_t*>(workspace);
-        a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-    }
-    a.qkv = static_cast<const uint16_t*>(qkv);
-    a.k_cache = static_cast<uint16_t*>(k_cache);
-    a.v_cache = static_cast<uint16_t*>(v_cache);
-    a.pos = pos;
-    a.out = static_cast<uint16_t*>(out);
-    hipError_t e = launch_decode_attn(a, attn_keys_per_wave(a), static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return run_attention(qkv, k_cache, v_cache, pos, out, B, H, D, S, max_len, rope_base, scale, workspace,
+                         workspace_bytes, stream);
+}
+
+int w4a16_silu_mul(const void* gu, void* act, int64_t N, int64_t I, void* stream) {
+    return run_silu_mul(gu, act, N, I, stream);
+}
+
+size_t w4a16_decode_layer_workspace_size(int64_t B, int64_t H, int64_t D, int64_t I, int64_t S, int64_t max_len) {
+    LayerLayout L;
+    const std::string saved = g_err;
+    const int st = layer_layout(B, H, D, I, S, max_len, L);
+    g_err = saved;
+    return st ? 0 : L.total;
+}
+
+int w4a16_decode_layer(const w4a16_decoder_layer* layer, int64_t B, int64_t H, int64_t D, int64_t I, int64_t S,
+                       int64_t max_len, const int32_t* pos, float eps, float rope_base, void* residual, void* x,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return run_decode_layer(layer, B, H, D, I, S, max_len, pos, eps, rope_base, residual, x, workspace,
+                            workspace_bytes, stream);
 }
 
 int w4a16_tune(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* x, void* c,

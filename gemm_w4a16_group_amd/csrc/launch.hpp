@@ -89,6 +89,9 @@ int attn_keys_per_wave(const AttnArgs& a);
 int64_t attn_splits(const AttnArgs& a, int kpw);
 hipError_t launch_decode_attn(const AttnArgs& a, int kpw, hipStream_t stream);
 
+// act [N, I] = fp16(silu(gate) * up) from gu [N, 2 I] (gate columns first); I % 8 == 0
+hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* act, int64_t N, int64_t I, hipStream_t stream);
+
 // fp16 W [M, K] -> q_packed, fp16 scales, z_packed (round to nearest per group)
 hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,
                            hipStream_t stream);

@@ -315,6 +315,106 @@ size_t w4a16_gemm_add_rmsnorm_workspace_size(int64_t M, int64_t N, int64_t K,
                                              int32_t group_size,
                                              const w4a16_plan *plan);
 
+/*
+ * One decode step of multi-head attention per sequence, the third fusion of
+ * PerfXLLM §3.2 (the rotary encoding of Q and K, QK^T, the softmax and the
+ * product with V in one operator; the rotary encoding read as LLaMA's:
+ * channel pairs (2i, 2i + 1) turned by p * rope_base^(-2i / D)).  For each
+ * sequence b with its new token at position p = pos[b]:
+ *   q, k, v = the head slices of qkv[b] = [q | k | v]
+ *   stores fp16(rope(k, p)) and v at position p of the caches, then
+ *   out[b, h] = sum_{j <= p} softmax_j(scale * rope(q, p) . K[b, h, j]) V[b, h, j]
+ *   qkv     : fp16 [B, 3 H D] (the QKV projection's token-major output)
+ *   k_cache, v_cache : fp16 [B, H, S, D], updated at each sequence's p
+ *   pos     : int32 [B] in device memory
+ *   out     : fp16 [B, H D]
+ *   max_len : a bound on p + 1 over the batch (1 <= max_len <= S): the
+ *             work is split along it, so a tight bound is faster; a position
+ *             outside [0, max_len) gives NaN outputs for its sequence and
+ *             leaves its cache entries alone
+ *   scale   : softmax scale, finite and > 0 (1 / sqrt(D) in LLaMA)
+ * Requires D == 128 (W4A16_ERR_UNSUPPORTED otherwise), 1 <= B, H <= 65535,
+ * max_len <= 262144, 16-byte aligned qkv, caches and out, and no overlap
+ * between out, qkv, the caches and pos.  workspace: at least
+ * w4a16_decode_attention_workspace_size() bytes (0 when the keys are not
+ * split), with the zero-filled-counter rule of w4a16_gemm.  Results are
+ * bitwise repeatable.
+ */
+int w4a16_decode_attention(const void *qkv, void *k_cache, void *v_cache,
+                           const int32_t *pos, void *out, int64_t B, int64_t H,
+                           int64_t D, int64_t S, int64_t max_len,
+                           float rope_base, float scale, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of w4a16_decode_attention (0 if none or on invalid
+ * input). */
+size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D,
+                                             int64_t S, int64_t max_len);
+
+/*
+ * The gated activation of LLaMA's MLP on the fused gate/up projection's
+ * output (the pages do not describe the MLP; this is the LLaMA-7B reading):
+ *   act[n, i] = fp16(silu(gu[n, i]) * gu[n, I + i]),  silu(g) = g / (1 + e^-g)
+ *   gu  : fp16 [N, 2 I], gate in columns 0 .. I - 1 (gate rows first in the
+ *         fused weight), up in I .. 2 I - 1
+ *   act : fp16 [N, I], overlapping nothing
+ * Requires N >= 1, I >= 8, I % 8 == 0, 16-byte aligned pointers.  Within
+ * 1e-3 |act| + 1e-6 of the float64 result.
+ */
+int w4a16_silu_mul(const void *gu, void *act, int64_t N, int64_t I,
+                   void *stream);
+
+/* One W4A16 linear layer's weights, as w4a16_gemm takes them. */
+typedef struct {
+    const uint32_t *q_packed;
+    const void *scales;
+    const uint32_t *z_packed;
+} w4a16_linear;
+
+/* The weights and caches of one LLaMA decoder layer (hidden size H D,
+ * MLP width I). */
+typedef struct {
+    w4a16_linear qkv;       /* [3 H D, H D]: q rows, then k, then v      */
+    w4a16_linear o;         /* [H D, H D]                                 */
+    w4a16_linear gate_up;   /* [2 I, H D]: gate rows, then up rows        */
+    w4a16_linear down;      /* [H D, I]                                   */
+    const void *attn_norm;  /* fp16 [H D] gain of the attention's norm    */
+    const void *mlp_norm;   /* fp16 [H D] gain of the MLP's norm          */
+    void *k_cache;          /* fp16 [B, H, S, D]                          */
+    void *v_cache;          /* fp16 [B, H, S, D]                          */
+} w4a16_decoder_layer;
+
+/*
+ * One decode step of one LLaMA decoder layer, token-major, all on `stream`
+ * (the generation phase of PerfXLLM §3.3, one input token per sequence,
+ * with the fusions of §3.2):
+ *   r   = fp16(x + r);  y = rmsnorm(r) * attn_norm          (w4a16_gemm_add_rmsnorm
+ *   qkv = y . Wqkv^T                                           with the QKV weights)
+ *   a   = decode attention(qkv, caches, pos)                  (w4a16_decode_attention)
+ *   x   = a . Wo^T                                             (w4a16_gemm_ex)
+ *   r   = fp16(x + r);  y = rmsnorm(r) * mlp_norm;  gu = y . Wgu^T
+ *   act = silu(gate) * up                                       (w4a16_silu_mul)
+ *   x   = act . Wdown^T                                         (w4a16_gemm_ex)
+ * residual (r) and x are fp16 [B, H D], both read and overwritten: on entry
+ * x is the previous layer's output still to be added to the stream, on exit
+ * this layer's.  Default plans, scale 1 / sqrt(D).  Every step is checked
+ * before the first is enqueued; nothing allocates or synchronizes, so a
+ * whole model's step can be captured in one graph.  workspace: at least
+ * w4a16_decode_layer_workspace_size() bytes, 16-byte aligned, first 64 KB
+ * zero before first use (kept zero).  Requirements of the steps above;
+ * I % 128 == 0.
+ */
+int w4a16_decode_layer(const w4a16_decoder_layer *layer, int64_t B, int64_t H,
+                       int64_t D, int64_t I, int64_t S, int64_t max_len,
+                       const int32_t *pos, float eps, float rope_base,
+                       void *residual, void *x, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of w4a16_decode_layer (0 on invalid input). */
+size_t w4a16_decode_layer_workspace_size(int64_t B, int64_t H, int64_t D,
+                                         int64_t I, int64_t S,
+                                         int64_t max_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -339,3 +339,34 @@ def test_tune_checks(lib):
     assert call(g=64) == UNSUPPORTED
     assert call(flush=ctypes.c_void_p(0x700008), fb=4096) == INVALID
     assert call(flush=ctypes.c_void_p(0x700000), fb=0) == INVALID
+
+
+def test_every_export_is_declared():
+    """The library exports no w4a16_ function that the header does not declare."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if ln.split() and ln.split()[-1].startswith("w4a16_")})
+    assert exported == B.header_functions()
+
+
+def test_decode_layer_and_silu_checks(lib):
+    assert lib.w4a16_silu_mul(X, C, 0, 64, NULL) == INVALID
+    assert lib.w4a16_silu_mul(X, C, 4, 12, NULL) == INVALID
+    assert lib.w4a16_silu_mul(X, ctypes.c_void_p(0x400008), 4, 64, NULL) == MISALIGNED
+    assert lib.w4a16_silu_mul(X, ctypes.c_void_p(0x400000 + 64), 4, 64, NULL) == INVALID   # act inside gu
+    # workspace sizes: valid shapes give a size, invalid ones 0
+    assert lib.w4a16_decode_layer_workspace_size(1, 32, 128, 11008, 2048, 2048) > 0
+    assert lib.w4a16_decode_layer_workspace_size(1, 32, 128, 11000, 2048, 2048) == 0   # I % 128
+    assert lib.w4a16_decode_layer_workspace_size(1, 32, 64, 11008, 2048, 2048) == 0    # D
+    layer = B.DecoderLayer()
+    assert lib.w4a16_decode_layer(None, 1, 4, 128, 1024, 64, 64, X, 1e-6, 1e4, Q, S, WS, 1 << 30, NULL) == INVALID
+    # a layer of null pointers fails its first step's checks before anything is enqueued
+    need = lib.w4a16_decode_layer_workspace_size(1, 4, 128, 1024, 64, 64)
+    assert (lib.w4a16_decode_layer(ctypes.byref(layer), 1, 4, 128, 1024, 64, 64, X, 1e-6, 1e4, Q, S, WS, need, NULL)
+            == INVALID)
+    assert (lib.w4a16_decode_layer(ctypes.byref(layer), 1, 4, 128, 1024, 64, 64, X, 1e-6, 1e4, Q, S, WS, need - 1,
+                                   NULL) == WORKSPACE)

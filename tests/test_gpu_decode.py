@@ -1,0 +1,162 @@
+"""The decoder layer's gated activation against the oracle; the decode-layer
+entry point against the same steps called one by one (bit for bit) and
+against the oracle composed step by step; the captured decode graph against
+eager steps, replay after replay."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.w4a16 as ora
+from gemm_w4a16_group_amd import binding as B
+from gemm_w4a16_group_amd import inputs
+from gemm_w4a16_group_amd.decode import DecodeGraph
+from gpu_util import Problem, dev, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("shape", [(1, 11008), (5, 8), (33, 1000), (128, 11008)], ids=lambda s: "N%d_I%d" % s)
+def test_silu_mul(shape):
+    N, I = shape
+    log("silu_mul %s" % (shape,))
+    rng = np.random.default_rng(N * 7 + I)
+    gu = (rng.standard_normal((N, 2 * I), dtype=np.float32) * 3).astype(np.float16)
+    gu[0, :4] = np.array([0.0, 30.0, -30.0, -0.0], dtype=np.float16)
+    act = B.silu_mul(dev(gu)).cpu().numpy()
+    ref = ora.silu_mul(gu)
+    err = np.abs(act.astype(np.float64) - ref)
+    assert np.all(err <= ora.silu_mul_tolerance(ref)), float(np.max(err / ora.silu_mul_tolerance(ref)))
+
+
+H, D, I, S = 4, 128, 1024, 64
+HD = H * D
+
+
+def make_layer(seed, Bn):
+    """A small LLaMA-shaped layer: random int4 weights packed on the device,
+    gains, caches filled with random history."""
+    projs = {"qkv": (3 * HD, HD), "o": (HD, HD), "gate_up": (2 * I, HD), "down": (HD, I)}
+    layer, host = {}, {}
+    for i, (name, (M, K)) in enumerate(projs.items()):
+        p = Problem(M, K, seed=200 + 10 * seed + i)
+        layer[name] = (p.qpk, p.s_d, p.zpk)
+        host[name] = p
+    _, _, g1 = inputs.hidden_states(1, HD, wid=800 + seed)
+    _, _, g2 = inputs.hidden_states(1, HD, wid=900 + seed)
+    _, kc, vc = inputs.attention_inputs(Bn, H, D, S, wid=1000 + seed)
+    layer.update(attn_norm=dev(g1), mlp_norm=dev(g2), k_cache=dev(kc), v_cache=dev(vc))
+    host.update(attn_norm=g1, mlp_norm=g2, k_cache=kc, v_cache=vc)
+    return layer, host
+
+
+def clone_layer(layer):
+    out = dict(layer)
+    out["k_cache"] = layer["k_cache"].clone()
+    out["v_cache"] = layer["v_cache"].clone()
+    return out
+
+
+def oracle_layer(host, x, r, pos, eps=1e-6):
+    """The layer composed from the oracle's steps, every stored tensor
+    rounded to fp16 as the library stores it.  Returns (x_out, r_out,
+    A_down) with A_down = |Wdown| |act| bounding the last product."""
+    def proj(name, act):
+        p = host[name]
+        C, A = ora.reference(p.qpk_ref, p.s, p.zpk_ref, np.asarray(act, dtype=np.float64).T)
+        return C.T, A.T
+
+    h = ora.residual_fp16(x, r)
+    y, _ = ora.add_rmsnorm(h, np.zeros_like(h), host["attn_norm"], eps)
+    qkv = proj("qkv", y)[0].astype(np.float16)
+    a, _, _, _ = ora.decode_attention(qkv, host["k_cache"], host["v_cache"], pos, H, D)
+    o = proj("o", a.astype(np.float16))[0].astype(np.float16)
+    h2 = ora.residual_fp16(o, h)
+    y2, _ = ora.add_rmsnorm(h2, np.zeros_like(h2), host["mlp_norm"], eps)
+    gu = proj("gate_up", y2)[0].astype(np.float16)
+    act = ora.silu_mul(gu).astype(np.float16)
+    xo, A = proj("down", act)
+    return xo, h2, A
+
+
+def stream_inputs(Bn, seed):
+    x, r, _ = inputs.hidden_states(Bn, HD, wid=1100 + seed)
+    return x, r
+
+
+def test_decode_layer_matches_its_steps_bitwise():
+    Bn = 3
+    layer, _ = make_layer(0, Bn)
+    pos = dev(np.array([0, 17, 63], dtype=np.int32))
+    x, r = stream_inputs(Bn, 0)
+    # the entry point
+    la = clone_layer(layer)
+    xa, ra = dev(x), dev(r)
+    ws = torch.zeros(B.decode_layer_workspace_size(Bn, H, D, I, S, S), dtype=torch.uint8, device="cuda")
+    B.decode_layer(la, pos, ra, xa, ws)
+    # the same steps one by one through the public calls
+    lb = clone_layer(layer)
+    xb, rb = dev(x), dev(r)
+    qkv, _ = B.gemm_add_rmsnorm(*lb["qkv"], xb, rb, lb["attn_norm"], 1e-6, h=rb)
+    att = B.decode_attention(qkv, lb["k_cache"], lb["v_cache"], pos)
+    B.gemm(*lb["o"], att, out=xb, layout=B.LAYOUT_TOKEN)
+    gu, _ = B.gemm_add_rmsnorm(*lb["gate_up"], xb, rb, lb["mlp_norm"], 1e-6, h=rb)
+    act = B.silu_mul(gu)
+    B.gemm(*lb["down"], act, out=xb, layout=B.LAYOUT_TOKEN)
+    torch.cuda.synchronize()
+    for name, u, v in (("x", xa, xb), ("residual", ra, rb), ("k_cache", la["k_cache"], lb["k_cache"]),
+                       ("v_cache", la["v_cache"], lb["v_cache"])):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16)), name
+
+
+def test_decode_layer_against_oracle():
+    """End to end through one layer.  Each step meets its own bound in its
+    own tests; composed, the upstream errors pass through the softmax and
+    the gated activation, so the composite bound is the down projection's
+    rule widened tenfold: |x - x_ref| <= 5e-2 sum|Wdown||act| + 1e-2, and a
+    relative 2-norm error below 2e-2; the residual stream within 1e-2 of its
+    scale."""
+    Bn = 2
+    layer, host = make_layer(1, Bn)
+    pos = np.array([5, 40], dtype=np.int32)
+    x, r = stream_inputs(Bn, 1)
+    xd, rd = dev(x), dev(r)
+    ws = torch.zeros(B.decode_layer_workspace_size(Bn, H, D, I, S, S), dtype=torch.uint8, device="cuda")
+    B.decode_layer(layer, dev(pos), rd, xd, ws)
+    torch.cuda.synchronize()
+    xo, h2, A = oracle_layer(host, x, r, pos)
+    xg = xd.cpu().numpy().astype(np.float64)
+    err = np.abs(xg - xo)
+    assert np.all(err <= 5e-2 * A + 1e-2), float(np.max(err / (5e-2 * A + 1e-2)))
+    assert np.linalg.norm(xg - xo) <= 2e-2 * np.linalg.norm(xo)
+    rg = rd.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(rg - h2)) <= 1e-2 * np.max(np.abs(h2))
+
+
+def test_decode_graph_replays_match_eager():
+    """Two layers, four steps: graph replays (with eager work and
+    synchronisations between them) equal eager steps bit for bit."""
+    Bn = 2
+    layers = [make_layer(2 + i, Bn)[0] for i in range(2)]
+    pos0 = [3, 30]
+    x, r = stream_inputs(Bn, 2)
+    g = DecodeGraph([clone_layer(l) for l in layers], pos0)
+    e = DecodeGraph([clone_layer(l) for l in layers], pos0)
+    for d in (g, e):
+        d.x.copy_(dev(x))
+        d.residual.copy_(dev(r))
+    torch.cuda.synchronize()
+    for step in range(4):
+        log("decode graph step %d" % step)
+        g.step()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        e.eager_step()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        assert torch.equal(g.pos, e.pos)
+        assert torch.equal(g.x.view(torch.int16), e.x.view(torch.int16)), step
+        assert torch.equal(g.residual.view(torch.int16), e.residual.view(torch.int16)), step
+        for lg, le in zip(g.layers, e.layers):
+            assert torch.equal(lg["k_cache"].view(torch.int16), le["k_cache"].view(torch.int16)), step
+    assert g.graph is not None
