@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
-                             "quantize_12288x4096", "prologue", "attention", "tune_table"])
+                             "quantize_12288x4096", "prologue", "attention", "tune_table", "decode_step"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -329,6 +329,57 @@ def extra(args):
                           "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "kernel": "quantize_kernel"}), flush=True)
+        return
+    if args.workload == "decode_step":
+        # a LLaMA-7B decode step: 32 decoder layers (QKV, attention, o_proj,
+        # gate/up, down, with the normalizations and the gated activation),
+        # one HIP graph per step, B sequences at context ~1024 in a 2048-slot
+        # cache; embeddings and the output head are not part of it
+        from gemm_w4a16_group_amd.decode import DecodeGraph
+        H, D, I, S, L = 32, 128, 11008, 2048, 32
+        for Bn in (1, 8):
+            layers = []
+            for layer in range(L):
+                ly = {}
+                for proj, (name, M, K) in enumerate((("qkv", 3 * H * D, H * D), ("o", H * D, H * D),
+                                                     ("gate_up", 2 * I, H * D), ("down", H * D, I))):
+                    w = torch.from_numpy(inputs.raw_q_words(M, K, wid=11, layer=layer, proj=proj).view("int32")).cuda()
+                    sc, z = inputs.scales_zeros(M, K, wid=11, layer=layer, proj=proj)
+                    _, zd = B.pack(None, torch.from_numpy(z).cuda())
+                    ly[name] = (w, torch.from_numpy(sc).cuda(), zd)
+                _, _, g1 = inputs.hidden_states(1, H * D, wid=11, layer=2 * layer)
+                _, _, g2 = inputs.hidden_states(1, H * D, wid=11, layer=2 * layer + 1)
+                ly["attn_norm"], ly["mlp_norm"] = torch.from_numpy(g1).cuda(), torch.from_numpy(g2).cuda()
+                ly["k_cache"] = torch.randn((Bn, H, S, D), dtype=torch.float16, device="cuda",
+                                            generator=torch.Generator(device="cuda").manual_seed(layer))
+                ly["v_cache"] = torch.randn((Bn, H, S, D), dtype=torch.float16, device="cuda",
+                                            generator=torch.Generator(device="cuda").manual_seed(1000 + layer))
+                layers.append(ly)
+            pos0 = [1023] * Bn
+            dg = DecodeGraph(layers, pos0, max_len=S)
+            _, emb, _ = inputs.hidden_states(Bn, H * D, wid=11, layer=99)
+            dg.embed.copy_(torch.from_numpy(emb).cuda())   # the same token embedding every step
+            dg.step()            # eager (loads the kernels)
+            dg.step()            # capture + first replay
+            torch.cuda.synchronize()
+            steps = 50
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(steps):
+                dg.step()
+            end.record()
+            end.synchronize()
+            ms = start.elapsed_time(end) / steps
+            wbytes = L * sum(alg_bytes(M, K, Bn) for M, K in ((3 * H * D, H * D), (H * D, H * D), (2 * I, H * D),
+                                                             (H * D, I)))
+            kv = L * 2 * Bn * H * D * 2 * (1024 + 2 + steps // 2)
+            print(json.dumps({"workload": "llama7b_decode_step", "B": Bn, "layers": L, "context": "1025-%d" % (1026 + steps),
+                              "ms_per_step": round(ms, 4), "tokens_per_s": round(Bn * 1e3 / ms, 1),
+                              "weights_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                              "weights_plus_kv_GB/s": round((wbytes + kv) / (ms * 1e-3) / 1e9, 1),
+                              "finite": bool(torch.isfinite(dg.hidden()).all().item())}), flush=True)
+            del dg, layers
+            torch.cuda.empty_cache()
         return
     if args.workload == "tune_table":
         # the tuner's choice per N for the 12288x4096 projection (cold-cache

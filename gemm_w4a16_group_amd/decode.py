@@ -15,11 +15,13 @@ from . import binding as B
 class DecodeGraph:
     """Decode steps over `layers` (dicts as `binding.decode_layer` takes
     them) for B sequences whose next positions are `pos0` (int32, one per
-    sequence).  State: `residual` and `x` (fp16 [B, H D]; x holds the last
-    layer's output after a step), `pos` (advanced by one per step), the
-    layers' KV caches.  The first `step()` runs eagerly (it also loads the
-    kernels); the second captures the step as a graph and replays it; later
-    ones replay."""
+    sequence).  A step starts from `embed` (fp16 [B, H D], the new tokens'
+    embeddings, written by the caller before the step): the residual stream
+    is set to it and x to zero, the layers run, and the positions advance by
+    one.  After a step the last hidden state is residual + x (`hidden()`),
+    and the layers' KV caches hold the new tokens.  The first `step()` runs
+    eagerly (it also loads the kernels); the second captures the step as a
+    graph and replays it; later ones replay."""
 
     def __init__(self, layers, pos0, max_len=None, eps=1e-6, rope_base=10000.0):
         kc = layers[0]["k_cache"]
@@ -30,6 +32,7 @@ class DecodeGraph:
         self.eps, self.rope_base = eps, rope_base
         dev = kc.device
         hd = self.H * self.D
+        self.embed = torch.zeros((self.B, hd), dtype=torch.float16, device=dev)
         self.residual = torch.zeros((self.B, hd), dtype=torch.float16, device=dev)
         self.x = torch.zeros((self.B, hd), dtype=torch.float16, device=dev)
         self.pos = torch.as_tensor(pos0, dtype=torch.int32).to(dev).contiguous()
@@ -42,6 +45,8 @@ class DecodeGraph:
         self.stream = torch.cuda.Stream(device=dev)
 
     def _enqueue(self):
+        self.residual.copy_(self.embed)
+        self.x.zero_()   # a fill kernel (no memset node in the graph)
         for layer in self.layers:
             B.decode_layer(layer, self.pos, self.residual, self.x, self.workspace, max_len=self.max_len,
                            eps=self.eps, rope_base=self.rope_base)
@@ -63,3 +68,7 @@ class DecodeGraph:
                 self._enqueue()
         self.graph.replay()
         self.steps += 1
+
+    def hidden(self):
+        """The last layer's output added to the stream (fp32 on the device)."""
+        return self.residual.float() + self.x.float()

@@ -139,15 +139,14 @@ def test_decode_graph_replays_match_eager():
     Bn = 2
     layers = [make_layer(2 + i, Bn)[0] for i in range(2)]
     pos0 = [3, 30]
-    x, r = stream_inputs(Bn, 2)
     g = DecodeGraph([clone_layer(l) for l in layers], pos0)
     e = DecodeGraph([clone_layer(l) for l in layers], pos0)
-    for d in (g, e):
-        d.x.copy_(dev(x))
-        d.residual.copy_(dev(r))
     torch.cuda.synchronize()
     for step in range(4):
         log("decode graph step %d" % step)
+        emb = dev(stream_inputs(Bn, 10 + step)[1])
+        for d in (g, e):
+            d.embed.copy_(emb)
         g.step()
         torch.cuda.synchronize()
         scratch = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
@@ -157,6 +156,7 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(g.pos, e.pos)
         assert torch.equal(g.x.view(torch.int16), e.x.view(torch.int16)), step
         assert torch.equal(g.residual.view(torch.int16), e.residual.view(torch.int16)), step
+        assert torch.isfinite(g.hidden()).all()
         for lg, le in zip(g.layers, e.layers):
             assert torch.equal(lg["k_cache"].view(torch.int16), le["k_cache"].view(torch.int16)), step
     assert g.graph is not None
