@@ -119,6 +119,11 @@ def load_library(path=None):
         lib.w4a16_decode_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, f32, vp, sz, vp]
         lib.w4a16_decode_attention_workspace_size.restype = sz
         lib.w4a16_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+        lib.w4a16_decode_attention_plan.restype = ctypes.c_int
+        lib.w4a16_decode_attention_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, f32, i32, i32,
+                                                    vp, sz, vp]
+        lib.w4a16_decode_attention_workspace_size_plan.restype = sz
+        lib.w4a16_decode_attention_workspace_size_plan.argtypes = [i64, i64, i64, i64, i64, i32, i32]
         lib.w4a16_tune.restype = ctypes.c_int
         lib.w4a16_tune.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp, sz, i32,
                                    ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_float),
@@ -391,11 +396,12 @@ def gemm_add_rmsnorm(qpk, s, zpk, x, residual, gamma, eps=1e-6, h=None, out=None
 
 
 def decode_attention(qkv, k_cache, v_cache, pos, max_len=None, rope_base=10000.0, scale=None, out=None,
-                     workspace=None):
+                     workspace=None, shape=None):
     """One decode step of multi-head attention with rotary encoding:
     qkv fp16 [B, 3 H D] (q | k | v of each sequence's new token), caches fp16
     [B, H, S, D] (updated at each sequence's position), pos int32 [B] on the
-    device, max_len a bound on pos + 1 (default S).  Returns out [B, H D]."""
+    device, max_len a bound on pos + 1 (default S); shape (keys per wave,
+    waves) or None for the default.  Returns out [B, H D]."""
     _need(k_cache, "k_cache", torch.float16)
     if k_cache.dim() != 4:
         raise ValueError("k_cache must be [B, H, S, D]")
@@ -411,7 +417,8 @@ def decode_attention(qkv, k_cache, v_cache, pos, max_len=None, rope_base=10000.0
         out = torch.empty((Bn, H * D), dtype=torch.float16, device=qkv.device)
     else:
         _need(out, "out", torch.float16, (Bn, H * D))
-    need = int(lib().w4a16_decode_attention_workspace_size(Bn, H, D, S, max_len))
+    kpw, waves = (0, 0) if shape is None else shape
+    need = int(lib().w4a16_decode_attention_workspace_size_plan(Bn, H, D, S, max_len, kpw, waves))
     ws = None
     if need:
         if workspace is None:
@@ -419,8 +426,9 @@ def decode_attention(qkv, k_cache, v_cache, pos, max_len=None, rope_base=10000.0
         else:
             ws = workspace.get(need) if isinstance(workspace, Workspace) else workspace
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().w4a16_decode_attention(_p(qkv), _p(k_cache), _p(v_cache), _p(pos), _p(out), Bn, H, D, S, max_len,
-                                        float(rope_base), float(scale), _p(ws), ws_bytes, _stream()))
+    _check(lib().w4a16_decode_attention_plan(_p(qkv), _p(k_cache), _p(v_cache), _p(pos), _p(out), Bn, H, D, S,
+                                             max_len, float(rope_base), float(scale), kpw, waves, _p(ws), ws_bytes,
+                                             _stream()))
     return out
 
 

@@ -462,8 +462,8 @@ int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, 
 // along the keys needs the workspace's counters and per-split partials.
 constexpr int64_t kAttnHeadDim = 128;
 
-size_t attn_workspace_bytes(const AttnArgs& a) {
-    const int64_t splits = attn_splits(a, attn_keys_per_wave(a));
+size_t attn_workspace_bytes(const AttnArgs& a, const AttnShape& sh) {
+    const int64_t splits = attn_splits(a, sh);
     if (splits <= 1) return 0;
     return kCounterBytes + (size_t)a.B * (size_t)a.H * (size_t)splits * (kAttnHeadDim + 2) * 4;
 }
@@ -488,19 +488,36 @@ int make_attn(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len, float
     a.max_len = max_len;
     a.theta1 = pow((double)rope_base, -2.0 / (double)D);
     a.scale = scale;
-    if (attn_splits(a, attn_keys_per_wave(a)) > kAttnMaxSplits)
-        return fail(W4A16_ERR_UNSUPPORTED, "max_len above %lld", (long long)kAttnMaxSplits * 256);
-    if (attn_splits(a, attn_keys_per_wave(a)) > 1 && B * H > kCounterSlots)
+    return W4A16_OK;
+}
+
+// A workgroup shape for these arguments: supported, at most kAttnMaxSplits
+// splits, and a counter per (sequence, head) when it splits.
+int check_attn_shape(const AttnArgs& a, const AttnShape& sh) {
+    if (!attn_shape_supported(sh))
+        return fail(W4A16_ERR_UNSUPPORTED, "keys per wave must be 16, 32 or 64 and waves 4, 8 or 16 (got %d, %d)",
+                    sh.kpw, sh.waves);
+    if (attn_splits(a, sh) > kAttnMaxSplits)
+        return fail(W4A16_ERR_UNSUPPORTED, "more than %d splits along the keys (max_len %lld)", kAttnMaxSplits,
+                    (long long)a.max_len);
+    if (attn_splits(a, sh) > 1 && (int64_t)a.B * a.H > kCounterSlots)
         return fail(W4A16_ERR_UNSUPPORTED, "split attention supports at most %lld (sequence, head) pairs",
                     (long long)kCounterSlots);
     return W4A16_OK;
 }
 
+AttnShape shape_or_default(const AttnArgs& a, int32_t kpw, int32_t waves) {
+    return (kpw == 0 && waves == 0) ? attn_default_shape(a) : AttnShape{kpw, waves};
+}
+
 int run_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out, int64_t B, int64_t H,
                   int64_t D, int64_t S, int64_t max_len, float rope_base, float scale, void* workspace,
-                  size_t workspace_bytes, void* stream, bool dry = false) {
+                  size_t workspace_bytes, void* stream, bool dry = false, int32_t kpw = 0, int32_t waves = 0) {
     AttnArgs a;
     int st = make_attn(B, H, D, S, max_len, rope_base, scale, a);
+    if (st) return st;
+    const AttnShape sh = shape_or_default(a, kpw, waves);
+    st = check_attn_shape(a, sh);
     if (st) return st;
     if (!qkv || !k_cache || !v_cache || !pos || !out) return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
     if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -514,7 +531,7 @@ int run_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* 
     if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, qkv, nq) || overlaps(v_cache, nc, qkv, nq) ||
         overlaps(k_cache, nc, pos, np) || overlaps(v_cache, nc, pos, np))
         return fail(W4A16_ERR_INVALID_ARG, "a cache overlaps another buffer");
-    const size_t need = attn_workspace_bytes(a);
+    const size_t need = attn_workspace_bytes(a, sh);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(W4A16_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -533,7 +550,7 @@ int run_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* 
     a.pos = pos;
     a.out = static_cast<uint16_t*>(out);
     if (dry) return ok();
-    hipError_t e = launch_decode_attn(a, attn_keys_per_wave(a), static_cast<hipStream_t>(stream));
+    hipError_t e = launch_decode_attn(a, sh, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -574,7 +591,9 @@ int layer_layout(int64_t B, int64_t H, int64_t D, int64_t I, int64_t S, int64_t 
     if (!st) st = check_dims(2 * I, B, HD, kGroupSize);
     if (!st) st = check_dims(HD, B, I, kGroupSize);
     if (st) return st;
-    size_t shared = attn_workspace_bytes(aa);
+    st = check_attn_shape(aa, attn_default_shape(aa));
+    if (st) return st;
+    size_t shared = attn_workspace_bytes(aa, attn_default_shape(aa));
     auto grow = [&](size_t v) { shared = v > shared ? v : shared; };
     {
         const GemmArgs a = make_args(3 * HD, B, HD, W4A16_LAYOUT_TOKEN);
@@ -853,12 +872,27 @@ int w4a16_gemm_add_rmsnorm(const uint32_t* q_packed, const void* scales, const u
                          workspace, workspace_bytes, stream);
 }
 
-size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len) {
+size_t w4a16_decode_attention_workspace_size_plan(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len,
+                                                  int32_t keys_per_wave, int32_t waves) {
     AttnArgs a;
     const std::string saved = g_err;
-    const int st = make_attn(B, H, D, S, max_len, 10000.f, 1.f, a);
+    int st = make_attn(B, H, D, S, max_len, 10000.f, 1.f, a);
+    const AttnShape sh = shape_or_default(a, keys_per_wave, waves);
+    if (!st) st = check_attn_shape(a, sh);
     g_err = saved;
-    return st ? 0 : attn_workspace_bytes(a);
+    return st ? 0 : attn_workspace_bytes(a, sh);
+}
+
+size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len) {
+    return w4a16_decode_attention_workspace_size_plan(B, H, D, S, max_len, 0, 0);
+}
+
+int w4a16_decode_attention_plan(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out,
+                                int64_t B, int64_t H, int64_t D, int64_t S, int64_t max_len, float rope_base,
+                                float scale, int32_t keys_per_wave, int32_t waves, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return run_attention(qkv, k_cache, v_cache, pos, out, B, H, D, S, max_len, rope_base, scale, workspace,
+                         workspace_bytes, stream, false, keys_per_wave, waves);
 }
 
 int w4a16_decode_attention(const void* qkv, void* k_cache, void* v_cache, const int32_t* pos, void* out, int64_t B,

@@ -55,28 +55,38 @@ __device__ __forceinline__ uint32_t word_of(const u32x4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// wave-then-workgroup reductions over the 256 threads (every thread gets the result)
+// wave-then-workgroup reductions over the W waves (every thread gets the
+// result; the waves' values are combined in wave order)
+template <int W>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) r = fmaxf(r, red[w]);
+    return r;
 }
+template <int W>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) r += red[w];
+    return r;
 }
 
-template <int KPW>
-__global__ void __launch_bounds__(256) decode_attn_kernel(AttnArgs a) {
+template <int KPW, int W>
+__global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     constexpr int R = KPW / 8;   // rounds of 8 keys per wave
     constexpr int D = kHeadDim;
+    constexpr int NT = 64 * W;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int part = lane & 7, kslot = lane >> 3;
@@ -85,14 +95,14 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(AttnArgs a) {
     const int p = a.pos[b];
     const bool valid = p >= 0 && (int64_t)p < a.max_len;
     const int64_t slab = ((int64_t)b * H + h) * S * D;
-    const int64_t wg0 = (int64_t)split * 4 * KPW;
+    const int64_t wg0 = (int64_t)split * W * KPW;
     const int64_t j0 = wg0 + (int64_t)wave * KPW;
     // a workgroup whose keys all lie past p has nothing to read
     const bool live = valid && wg0 <= (int64_t)p;
 
-    __shared__ float so[4][D];
-    __shared__ float sm[4], sl[4];
-    __shared__ float red[4];
+    __shared__ float so[W][D];
+    __shared__ float sm[W], sl[W];
+    __shared__ float red[W];
     __shared__ int last_flag;
     float M = -INFINITY, L = 0.f, O = 0.f;   // this workgroup's (max, sum, o[tid])
 
@@ -226,12 +236,19 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(AttnArgs a) {
             sl[wave] = l;
         }
         __syncthreads();
-        M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-        float ew[4];
+        M = sm[0];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) ew[w] = sm[w] == -INFINITY ? 0.f : __expf(sm[w] - M);
-        L = ((ew[0] * sl[0] + ew[1] * sl[1]) + ew[2] * sl[2]) + ew[3] * sl[3];
-        if (tid < D) O = ((ew[0] * so[0][tid] + ew[1] * so[1][tid]) + ew[2] * so[2][tid]) + ew[3] * so[3][tid];
+        for (int w = 1; w < W; ++w) M = fmaxf(M, sm[w]);
+        float ew[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) ew[w] = sm[w] == -INFINITY ? 0.f : __expf(sm[w] - M);
+        L = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) L = fmaf(ew[w], sl[w], L);
+        if (tid < D) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) O = fmaf(ew[w], so[w][tid], O);
+        }
     }
 
     uint16_t* outp = a.out + (int64_t)b * H * D + (int64_t)h * D;
@@ -260,64 +277,95 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(AttnArgs a) {
     if (!last_flag) return;
 
     // (a) the largest split maximum, (b) the split weights and the total sum,
-    // (c) the weighted values: thread (channel tid % 128, parity tid / 128)
-    // takes every other split, eight loads in flight at a time
+    // (c) the weighted values: thread (channel tid % 128, class tid / 128)
+    // takes the splits of its class modulo NC, eight loads in flight at a time
+    constexpr int NC = NT / D;
     __shared__ float es[kAttnMaxSplits];
-    __shared__ float oh[2][D];
+    __shared__ float oh[NC][D];
     const float* pb = a.part + head * splits * (D + 2);
     float mx = -INFINITY;
-    for (int s = tid; s < splits; s += 256)
+    for (int s = tid; s < splits; s += NT)
         mx = fmaxf(mx, __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    mx = block_max(mx, red);
+    mx = block_max<W>(mx, red);
     float ls = 0.f;
-    for (int s = tid; s < splits; s += 256) {
+    for (int s = tid; s < splits; s += NT) {
         const float ms = __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float ll = __hip_atomic_load(pb + s * (D + 2) + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float e = ms == -INFINITY ? 0.f : __expf(ms - mx);
         es[s] = e;
         ls += e * ll;
     }
-    ls = block_sum(ls, red);   // its barriers also publish es
-    const int ch = tid & (D - 1), par = tid >> 7;
+    ls = block_sum<W>(ls, red);   // its barriers also publish es
+    const int ch = tid & (D - 1), cls = tid / D;
     float acc = 0.f;
-    for (int s0 = par; s0 < splits; s0 += 16) {
+    for (int s0 = cls; s0 < splits; s0 += 8 * NC) {
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int s = s0 + 2 * i < splits ? s0 + 2 * i : par;
+            const int s = s0 + NC * i < splits ? s0 + NC * i : 0;
             v[i] = __hip_atomic_load(pb + s * (D + 2) + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (s0 + 2 * i < splits) acc = fmaf(es[s0 + 2 * i], v[i], acc);
+            if (s0 + NC * i < splits) acc = fmaf(es[s0 + NC * i], v[i], acc);
     }
-    oh[par][ch] = acc;
+    oh[cls][ch] = acc;
     __syncthreads();
-    if (tid < D) outp[tid] = (uint16_t)f32_to_h16_bits((oh[0][tid] + oh[1][tid]) / ls);
+    if (tid < D) {
+        float o = oh[0][tid];
+#pragma unroll
+        for (int c = 1; c < NC; ++c) o += oh[c][tid];
+        outp[tid] = (uint16_t)f32_to_h16_bits(o / ls);
+    }
 }
 
 }  // namespace
 
-int attn_keys_per_wave(const AttnArgs& a) {
-    // the largest workgroup span that still gives 512 workgroups, at least 16
-    for (int kpw = 64; kpw >= 16; kpw /= 2) {
-        const int64_t splits = (a.max_len + 4 * kpw - 1) / (4 * kpw);
-        if ((int64_t)a.B * a.H * splits >= 512) return kpw;
-    }
-    return 16;
+// Sixteen waves (1024 threads, at most 128 registers each) only with 16 keys
+// per wave: more would spill.
+bool attn_shape_supported(const AttnShape& sh) {
+    return ((sh.kpw == 16 || sh.kpw == 32 || sh.kpw == 64) && (sh.waves == 4 || sh.waves == 8)) ||
+           (sh.kpw == 16 && sh.waves == 16);
 }
 
-int64_t attn_splits(const AttnArgs& a, int kpw) { return (a.max_len + 4 * kpw - 1) / (4 * kpw); }
+AttnShape attn_default_shape(const AttnArgs& a) {
+    // four waves; the largest span that still gives 512 workgroups, at least 16 keys per wave
+    for (int kpw = 64; kpw >= 16; kpw /= 2) {
+        const AttnShape sh{kpw, 4};
+        if ((int64_t)a.B * a.H * attn_splits(a, sh) >= 512) return sh;
+    }
+    return AttnShape{16, 4};
+}
 
-hipError_t launch_decode_attn(const AttnArgs& a, int kpw, hipStream_t stream) {
-    const dim3 grid((unsigned)attn_splits(a, kpw), (unsigned)a.H, (unsigned)a.B);
-    switch (kpw) {
-        case 16: hipLaunchKernelGGL(decode_attn_kernel<16>, grid, dim3(256), 0, stream, a); break;
-        case 32: hipLaunchKernelGGL(decode_attn_kernel<32>, grid, dim3(256), 0, stream, a); break;
-        case 64: hipLaunchKernelGGL(decode_attn_kernel<64>, grid, dim3(256), 0, stream, a); break;
+int64_t attn_splits(const AttnArgs& a, const AttnShape& sh) {
+    const int64_t span = (int64_t)sh.kpw * sh.waves;
+    return (a.max_len + span - 1) / span;
+}
+
+template <int KPW, int W>
+hipError_t launch_attn_t(const AttnArgs& a, const dim3& grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_attn_kernel<KPW, W>), grid, dim3(64 * W), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int KPW>
+hipError_t launch_attn_w(const AttnArgs& a, int waves, const dim3& grid, hipStream_t stream) {
+    switch (waves) {
+        case 4: return launch_attn_t<KPW, 4>(a, grid, stream);
+        case 8: return launch_attn_t<KPW, 8>(a, grid, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const AttnArgs& a, const AttnShape& sh, hipStream_t stream) {
+    const dim3 grid((unsigned)attn_splits(a, sh), (unsigned)a.H, (unsigned)a.B);
+    if (sh.kpw == 16 && sh.waves == 16) return launch_attn_t<16, 16>(a, grid, stream);
+    switch (sh.kpw) {
+        case 16: return launch_attn_w<16>(a, sh.waves, grid, stream);
+        case 32: return launch_attn_w<32>(a, sh.waves, grid, stream);
+        case 64: return launch_attn_w<64>(a, sh.waves, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4a16

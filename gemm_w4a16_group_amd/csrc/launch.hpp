@@ -82,12 +82,16 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* gamma, float eps, uint16_t* h,
                               uint16_t* y, int64_t N, int64_t K, bool chunks, hipStream_t stream);
 
-// decode attention: keys per wave (16, 32 or 64) for the shape, splits along the keys (at most
-// kAttnMaxSplits), launch
+// decode attention: a workgroup of `waves` waves (4 or 8; 16 with kpw 16) takes waves * kpw
+// consecutive keys (kpw = 16, 32 or 64 keys per wave); splits along the keys at most kAttnMaxSplits
+struct AttnShape {
+    int kpw, waves;
+};
 constexpr int kAttnMaxSplits = 1024;
-int attn_keys_per_wave(const AttnArgs& a);
-int64_t attn_splits(const AttnArgs& a, int kpw);
-hipError_t launch_decode_attn(const AttnArgs& a, int kpw, hipStream_t stream);
+bool attn_shape_supported(const AttnShape& sh);
+AttnShape attn_default_shape(const AttnArgs& a);
+int64_t attn_splits(const AttnArgs& a, const AttnShape& sh);
+hipError_t launch_decode_attn(const AttnArgs& a, const AttnShape& sh, hipStream_t stream);
 
 // act [N, I] = fp16(silu(gate) * up) from gu [N, 2 I] (gate columns first); I % 8 == 0
 hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* act, int64_t N, int64_t I, hipStream_t stream);

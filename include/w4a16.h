@@ -334,7 +334,8 @@ size_t w4a16_gemm_add_rmsnorm_workspace_size(int64_t M, int64_t N, int64_t K,
  *             leaves its cache entries alone
  *   scale   : softmax scale, finite and > 0 (1 / sqrt(D) in LLaMA)
  * Requires D == 128 (W4A16_ERR_UNSUPPORTED otherwise), 1 <= B, H <= 65535,
- * max_len <= 262144, 16-byte aligned qkv, caches and out, and no overlap
+ * max_len <= 262144 (the keys are split at most 1024 ways), 16-byte
+ * aligned qkv, caches and out, and no overlap
  * between out, qkv, the caches and pos.  workspace: at least
  * w4a16_decode_attention_workspace_size() bytes (0 when the keys are not
  * split), with the zero-filled-counter rule of w4a16_gemm.  Results are
@@ -350,6 +351,31 @@ int w4a16_decode_attention(const void *qkv, void *k_cache, void *v_cache,
  * input). */
 size_t w4a16_decode_attention_workspace_size(int64_t B, int64_t H, int64_t D,
                                              int64_t S, int64_t max_len);
+
+/*
+ * w4a16_decode_attention with an explicit workgroup shape (for tests and
+ * tuning; results are the same up to the summation order of the split
+ * merge): a workgroup of `waves` waves (4 or 8; 16 with 16 keys per wave)
+ * takes waves * keys_per_wave consecutive keys of one head (keys_per_wave
+ * 16, 32 or 64);
+ * 0, 0 selects the default shape.  W4A16_ERR_UNSUPPORTED for other values,
+ * or for a shape that splits the keys more than 1024 ways.
+ */
+int w4a16_decode_attention_plan(const void *qkv, void *k_cache, void *v_cache,
+                                const int32_t *pos, void *out, int64_t B,
+                                int64_t H, int64_t D, int64_t S,
+                                int64_t max_len, float rope_base, float scale,
+                                int32_t keys_per_wave, int32_t waves,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Workspace bytes of w4a16_decode_attention_plan for a shape (0, 0: the
+ * default); 0 if none is needed or on invalid input. */
+size_t w4a16_decode_attention_workspace_size_plan(int64_t B, int64_t H,
+                                                  int64_t D, int64_t S,
+                                                  int64_t max_len,
+                                                  int32_t keys_per_wave,
+                                                  int32_t waves);
 
 /*
  * The gated activation of LLaMA's MLP on the fused gate/up projection's

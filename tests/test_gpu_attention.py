@@ -105,3 +105,19 @@ def test_decode_attention_two_steps():
     for o, r, a, name in ((o1, ref1, A1, "step 1"), (o2, ref2, A2, "step 2")):
         err = np.abs(o.astype(np.float64) - r)
         assert np.all(err <= ora.tolerance(a)), name
+
+
+SHAPES = [(16, 4), (32, 4), (64, 4), (16, 8), (32, 8), (64, 8), (16, 16)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "kpw%d_w%d" % s)
+def test_decode_attention_shapes(shape):
+    """Every workgroup shape on a split case and a single-workgroup case."""
+    for Bn, H, S, pos in ((2, 8, 1500, [1499, 700]), (1, 4, 40, [39]), (3, 2, 3000, [2999, 0, 1024])):
+        log("decode_attention shape %s B=%d S=%d" % (shape, Bn, S))
+        qkv, kc, vc = inputs.attention_inputs(Bn, H, D, S, wid=660 + S)
+        kd, vd = dev(kc), dev(vc)
+        out = B.decode_attention(dev(qkv), kd, vd, dev(np.asarray(pos, dtype=np.int32)), shape=shape)
+        torch.cuda.synchronize()
+        check_step(qkv, kc, vc, pos, kd.cpu().numpy(), vd.cpu().numpy(), out.cpu().numpy(), H,
+                   "shape %s B=%d" % (shape, Bn))
