@@ -25,7 +25,8 @@
 // sums reduced over key slots (butterfly), then over the four waves in LDS.
 // With several splits, each writes (max, sum, o[D]) with agent-coherent
 // stores and the last one of a head to arrive (an arrival counter in the
-// workspace) merges them in split order.
+// workspace) merges them in split order, with all of the merge's loads in
+// flight at once.
 //
 // Angles: theta_i = theta_1^i from theta_1 = base^(-2/D) (double, from the
 // host), p * theta_i in double, reduced modulo 2 pi in double (two-part
@@ -55,33 +56,6 @@ __device__ __forceinline__ uint32_t word_of(const u32x4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// wave-then-workgroup reductions over the W waves (every thread gets the
-// result; the waves' values are combined in wave order)
-template <int W>
-__device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) r = fmaxf(r, red[w]);
-    return r;
-}
-template <int W>
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) r += red[w];
-    return r;
-}
-
 template <int KPW, int W>
 __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     constexpr int R = KPW / 8;   // rounds of 8 keys per wave
@@ -102,7 +76,6 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
 
     __shared__ float so[W][D];
     __shared__ float sm[W], sl[W];
-    __shared__ float red[W];
     __shared__ int last_flag;
     float M = -INFINITY, L = 0.f, O = 0.f;   // this workgroup's (max, sum, o[tid])
 
@@ -276,30 +249,44 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     __syncthreads();
     if (!last_flag) return;
 
-    // (a) the largest split maximum, (b) the split weights and the total sum,
-    // (c) the weighted values: thread (channel tid % 128, class tid / 128)
-    // takes the splits of its class modulo NC, eight loads in flight at a time
+    // The merge issues all of its loads before it uses any: every split's
+    // maximum and sum (into LDS), and this thread's first eight value
+    // partials (thread = (channel tid % 128, class tid / 128), class c takes
+    // splits c, c + NC, ...).  Every thread then forms the weights and the
+    // total sum over all splits in split order, so the result is the same
+    // whichever workgroup merges.
     constexpr int NC = NT / D;
-    __shared__ float es[kAttnMaxSplits];
+    __shared__ float sms[kAttnMaxSplits], sls[kAttnMaxSplits];
     __shared__ float oh[NC][D];
     const float* pb = a.part + head * splits * (D + 2);
-    float mx = -INFINITY;
-    for (int s = tid; s < splits; s += NT)
-        mx = fmaxf(mx, __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    mx = block_max<W>(mx, red);
-    float ls = 0.f;
-    for (int s = tid; s < splits; s += NT) {
-        const float ms = __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float ll = __hip_atomic_load(pb + s * (D + 2) + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float e = ms == -INFINITY ? 0.f : __expf(ms - mx);
-        es[s] = e;
-        ls += e * ll;
-    }
-    ls = block_sum<W>(ls, red);   // its barriers also publish es
     const int ch = tid & (D - 1), cls = tid / D;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int s = cls + NC * i < splits ? cls + NC * i : 0;
+        v[i] = __hip_atomic_load(pb + s * (D + 2) + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int s = tid; s < splits; s += NT) {
+        sms[s] = __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sls[s] = __hip_atomic_load(pb + s * (D + 2) + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, sms[s]);
+    float ls = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const float ms = sms[s];
+        ls = fmaf(ms == -INFINITY ? 0.f : __expf(ms - mx), sls[s], ls);
+    }
+    auto weight = [&](int s) {
+        const float ms = sms[s];
+        return ms == -INFINITY ? 0.f : __expf(ms - mx);
+    };
     float acc = 0.f;
-    for (int s0 = cls; s0 < splits; s0 += 8 * NC) {
-        float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (cls + NC * i < splits) acc = fmaf(weight(cls + NC * i), v[i], acc);
+    for (int s0 = cls + 8 * NC; s0 < splits; s0 += 8 * NC) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = s0 + NC * i < splits ? s0 + NC * i : 0;
@@ -307,7 +294,7 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (s0 + NC * i < splits) acc = fmaf(es[s0 + NC * i], v[i], acc);
+            if (s0 + NC * i < splits) acc = fmaf(weight(s0 + NC * i), v[i], acc);
     }
     oh[cls][ch] = acc;
     __syncthreads();
