@@ -135,6 +135,8 @@ def load_library(path=None):
                                            vp, vp, vp, sz, vp]
         lib.w4a16_decode_layer_workspace_size.restype = sz
         lib.w4a16_decode_layer_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
+        lib.w4a16_gemm_silu.restype = ctypes.c_int
+        lib.w4a16_gemm_silu.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.POINTER(Plan), vp, sz, vp]
         if path is None:
             _lib = lib
         return lib
@@ -502,3 +504,32 @@ def decode_layer(layer, pos, residual, x, workspace, max_len=None, eps=1e-6, rop
     _check(lib().w4a16_decode_layer(ctypes.byref(st), Bn, H, D, I, S, S if max_len is None else max_len, _p(pos),
                                     float(eps), float(rope_base), _p(residual), _p(x), _p(workspace),
                                     workspace.numel(), _stream()))
+
+
+def gemm_silu(qpk, s, zpk, gu, out=None, plan=None, workspace=None):
+    """Down projection with the gated activation as its prologue:
+    out[N, M] = (silu(gu[:, :K]) * gu[:, K:]) . Wdeq^T (token-major)."""
+    _need(qpk, "q_packed", torch.int32)
+    M, K = qpk.shape[0], qpk.shape[1] * 8
+    _need(gu, "gu", torch.float16)
+    if gu.dim() != 2 or gu.shape[1] != 2 * K:
+        raise ValueError("gu must be [N, 2K=%d], got %s" % (2 * K, tuple(gu.shape)))
+    N = gu.shape[0]
+    G = K // GROUP
+    _need(s, "scales", torch.float16, (M, G))
+    _need(zpk, "z_packed", torch.int32, (M, (G + 7) // 8))
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float16, device=gu.device)
+    else:
+        _need(out, "out", torch.float16)
+        if out.numel() != M * N:
+            raise ValueError("out must hold M*N=%d values" % (M * N))
+    need = workspace_size(M, N, K, plan, LAYOUT_TOKEN)
+    ws = None
+    if need:
+        ws = _workspace_for(gu.device).get(need) if workspace is None else (
+            workspace.get(need) if isinstance(workspace, Workspace) else workspace)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().w4a16_gemm_silu(_p(qpk), _p(s), _p(zpk), _p(gu), _p(out), M, N, K, GROUP,
+                                 None if plan is None else ctypes.byref(plan), _p(ws), ws_bytes, _stream()))
+    return out

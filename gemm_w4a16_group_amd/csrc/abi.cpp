@@ -264,23 +264,26 @@ int check_layout(int32_t layout) {
 // its steps before it enqueues the first one)
 int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const void* x, void* c,
              int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t layout, const w4a16_plan* plan_in,
-             void* workspace, size_t workspace_bytes, void* stream, bool dry = false) {
+             void* workspace, size_t workspace_bytes, void* stream, bool dry = false, int32_t act = 0) {
     int st = check_dims(M, N, K, group_size);
     if (st) return st;
     st = check_layout(layout);
     if (st) return st;
+    if (act && layout != W4A16_LAYOUT_TOKEN)
+        return fail(W4A16_ERR_INVALID_ARG, "the gated activation prologue takes token-major activations");
     if (!qpk || !scales || !zpk || !x || !c)
         return fail(W4A16_ERR_INVALID_ARG, "null data pointer");
     if (!aligned16(qpk) || !aligned16(scales) || !aligned16(zpk) || !aligned16(x) || !aligned16(c))
         return fail(W4A16_ERR_MISALIGNED, "every data pointer must be 16-byte aligned");
     const int64_t G = groups_of(K);
     const size_t nq = (size_t)M * (size_t)(K / 8) * 4, ns = (size_t)M * G * 2,
-                 nz = (size_t)M * zwords_of(K) * 4, nx = (size_t)K * N * 2, nc = (size_t)M * N * 2;
+                 nz = (size_t)M * zwords_of(K) * 4, nx = (size_t)K * N * 2 * (act ? 2 : 1), nc = (size_t)M * N * 2;
     if (overlaps(c, nc, qpk, nq) || overlaps(c, nc, scales, ns) || overlaps(c, nc, zpk, nz) ||
         overlaps(c, nc, x, nx))
         return fail(W4A16_ERR_INVALID_ARG, "output overlaps an input");
 
     GemmArgs a = make_args(M, N, K, layout);
+    a.act = act ? 1 : 0;
     const w4a16_plan p = plan_in ? *plan_in : default_plan(M, N, K, layout);
     st = check_plan(a, p);
     if (st) return st;
@@ -573,10 +576,10 @@ int run_silu_mul(const void* gu, void* act, int64_t N, int64_t I, void* stream, 
 }
 
 // Decoder layer workspace: [shared region: the largest workspace any step
-// needs, steps run one after another][qkv][attention output][gate/up][act],
-// each at a 256-byte boundary.
+// needs, steps run one after another][qkv][attention output][gate/up], each
+// at a 256-byte boundary.  The down projection forms silu(gate) * up itself.
 struct LayerLayout {
-    size_t shared, qkv, attn, gu, act, total;
+    size_t shared, qkv, attn, gu, total;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -617,8 +620,7 @@ int layer_layout(int64_t B, int64_t H, int64_t D, int64_t I, int64_t S, int64_t 
     L.qkv = L.shared;
     L.attn = L.qkv + round256((size_t)B * 3 * HD * 2);
     L.gu = L.attn + round256((size_t)B * HD * 2);
-    L.act = L.gu + round256((size_t)B * 2 * I * 2);
-    L.total = L.act + round256((size_t)B * I * 2);
+    L.total = L.gu + round256((size_t)B * 2 * I * 2);
     return W4A16_OK;
 }
 
@@ -643,7 +645,6 @@ int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_
     void* qkv = w + L.qkv;
     void* attn = w + L.attn;
     void* gu = w + L.gu;
-    void* act = w + L.act;
     const int64_t HD = H * D;
     const float scale = (float)(1.0 / sqrt((double)D));
     // every step checked first (dry), then enqueued
@@ -661,10 +662,9 @@ int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_
             st = run_gemm_norm(ly->gate_up.q_packed, ly->gate_up.scales, ly->gate_up.z_packed, x, residual,
                                ly->mlp_norm, eps, residual, gu, 2 * I, B, HD, kGroupSize, nullptr, shared, L.shared,
                                stream, dry);
-        if (!st) st = run_silu_mul(gu, act, B, I, stream, dry);
         if (!st)
-            st = run_gemm(ly->down.q_packed, ly->down.scales, ly->down.z_packed, act, x, HD, B, I, kGroupSize,
-                          W4A16_LAYOUT_TOKEN, nullptr, shared, L.shared, stream, dry);
+            st = run_gemm(ly->down.q_packed, ly->down.scales, ly->down.z_packed, gu, x, HD, B, I, kGroupSize,
+                          W4A16_LAYOUT_TOKEN, nullptr, shared, L.shared, stream, dry, 1);
         if (st) return st;
     }
     return ok();
@@ -984,6 +984,13 @@ int w4a16_tune(const uint32_t* q_packed, const void* scales, const uint32_t* z_p
     if (best_us) *best_us = best_t;
     if (n_tried) *n_tried = tried;
     return ok();
+}
+
+int w4a16_gemm_silu(const uint32_t* q_packed, const void* scales, const uint32_t* z_packed, const void* gu, void* c,
+                    int64_t M, int64_t N, int64_t K, int32_t group_size, const w4a16_plan* plan, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    return run_gemm(q_packed, scales, z_packed, gu, c, M, N, K, group_size, W4A16_LAYOUT_TOKEN, plan, workspace,
+                    workspace_bytes, stream, false, 1);
 }
 
 }  // extern "C"

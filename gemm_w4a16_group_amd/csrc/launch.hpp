@@ -19,6 +19,8 @@ struct GemmArgs {
     int32_t G, ZW;
     int32_t tm;               // 1: token-major x [N, K] and c [N, M]
     int32_t xp_ready;         // 1: a.xp already holds the activation chunks (no rewrite before the GEMM)
+    int32_t act;              // 1: x is a gate/up output [N, 2K] (token-major); the activations are
+                              //    silu(gate) * up, formed while staging or rewriting them
 };
 
 // One decode step of multi-head attention (head dimension 128).

@@ -151,14 +151,35 @@ __device__ __forceinline__ half8 unscale_ones() {
 // one 16-byte load per column, which is already that column's octet.  It becomes T8 LDS chunks, one per column, each
 // holding the octet in the order 0, 4, 1, 5, 2, 6, 3, 7, with k 1, 5, 3, 7
 // divided by 16 (exact unless the quotient is subnormal: then rounded once).
+// silu(g) * u of two fp16 pairs, float32, rounded once to fp16 (the
+// decoder layer's gated activation, computed while staging)
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g, uint32_t u) {
+    const half2v gh = as_h2(g), uh = as_h2(u);
+    const float g0 = (float)gh[0], g1 = (float)gh[1];
+    const _Float16 lo = (_Float16)(g0 / (1.0f + expf(-g0)) * (float)uh[0]);
+    const _Float16 hi = (_Float16)(g1 / (1.0f + expf(-g1)) * (float)uh[1]);
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
 template <int NT>
 struct XStage {
     static constexpr int T8 = NT < 8 ? NT : 8;
     static constexpr int NB8 = NT <= 8 ? 1 : NT / 8;   // column octets
     u32x4 v[T8];
 
+    template <bool ACT>
     __device__ __forceinline__ void load(const uint16_t* x, int64_t k0, int nb8, bool tm, int64_t K) {
-        if (NT <= 8) {
+        if (ACT && NT <= 8) {
+            // x is the gate/up output [NT, 2K]: the octet is silu(gate) * up,
+            // in float32, rounded once to fp16
+#pragma unroll
+            for (int t = 0; t < T8; ++t) {
+                const u32x4 g = *reinterpret_cast<const u32x4*>(x + (int64_t)t * 2 * K + k0);
+                const u32x4 u = *reinterpret_cast<const u32x4*>(x + (int64_t)t * 2 * K + K + k0);
+                v[t] = u32x4{silu_mul_pair(g.x, u.x), silu_mul_pair(g.y, u.y), silu_mul_pair(g.z, u.z),
+                             silu_mul_pair(g.w, u.w)};
+            }
+        } else if (NT <= 8) {
 #pragma unroll
             for (int t = 0; t < T8; ++t) {
                 const uint16_t* src = tm ? x + (int64_t)t * K + k0 : x + k0 * NT + 8 * t;
@@ -227,8 +248,10 @@ __device__ __forceinline__ void group_sums_one_column(const u32x4& v, int b, int
     if ((b & 15) == 0 && b < nxb) stab[b >> 4] = t;
 }
 
-template <int NT, int PF>
-__global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyParams P) {
+// ACT: the activations are computed from the gate/up output while staging
+// (token-major, NT <= 8); the kernels below instantiate the body both ways.
+template <int NT, int PF, bool ACT>
+__device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParams& P) {
     constexpr int F = skinny_staging_loads(NT, PF); // activation loads per lane
     constexpr int TB = (NT + 15) / 16;              // 16-column MFMA blocks
     constexpr int NB8 = XStage<NT>::NB8;
@@ -285,7 +308,7 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
         const int o = b / NB8, nb8 = b % NB8;     // NB8 is a power of two
         int64_t k0 = (int64_t)gw0 * kGroup + (int64_t)o * 8;
         k0 = k0 < a.K - 8 ? k0 : a.K - 8;
-        xst[j].load(a.x, k0, nb8, a.tm != 0, a.K);
+        xst[j].template load<ACT>(a.x, k0, nb8, a.tm != 0, a.K);
     }
     // ---- 2. scales: lane (row li, group 4 j + kb); zero words: lane (row
     // li, word kb)
@@ -527,19 +550,43 @@ __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyP
 }
 
 template <int NT, int PF>
-hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
+__global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyParams P) {
+    skinny_body<NT, PF, false>(a, P);
+}
+
+template <int NT, int PF>
+__global__ void __launch_bounds__(kMaxThreads) skinny_silu_kernel(GemmArgs a, SkinnyParams P) {
+    skinny_body<NT, PF, true>(a, P);
+}
+
+template <int NT, int PF, bool ACT>
+hipError_t launch_kernel(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
+    const void* fn;
+    if constexpr (ACT)
+        fn = reinterpret_cast<const void*>(&skinny_silu_kernel<NT, PF>);
+    else
+        fn = reinterpret_cast<const void*>(&skinny_kernel<NT, PF>);
     dim3 grid((unsigned)((a.M + P.rows - 1) / P.rows), (unsigned)s.splitk);
     dim3 block((unsigned)(64 * s.wm * s.wk));
     // dynamic LDS above 64 KB must be allowed per kernel, once
-    static const hipError_t lds_ok = [] {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<NT, PF>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    static const hipError_t lds_ok = [fn] {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         if (e != hipSuccess) (void)hipGetLastError();   // keep a refusal out of later launches' status
         return e;
     }();
     if (lds_ok != hipSuccess && P.total > 65536) return lds_ok;
-    hipLaunchKernelGGL((skinny_kernel<NT, PF>), grid, block, P.total, stream, a, P);
+    if constexpr (ACT)
+        hipLaunchKernelGGL((skinny_silu_kernel<NT, PF>), grid, block, P.total, stream, a, P);
+    else
+        hipLaunchKernelGGL((skinny_kernel<NT, PF>), grid, block, P.total, stream, a, P);
     return hipGetLastError();
+}
+
+template <int NT, int PF>
+hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
+    if constexpr (NT <= 8)
+        if (a.act) return launch_kernel<NT, PF, true>(a, s, P, stream);
+    return launch_kernel<NT, PF, false>(a, s, P, stream);
 }
 
 template <int NT>
@@ -573,6 +620,7 @@ const char* skinny_check(const GemmArgs& a, const SkinnyShape& s) {
         return "ncol must be 1..8, 16, 32 or 64, rb 1, wm * wk <= 16";
     if (s.splitk > a.G) return "splitk exceeds the number of groups";
     if (a.tm && a.N > 8) return "token-major activations only for N <= 8";
+    if (a.act && !a.tm) return "the gated activation prologue needs token-major activations";
     SkinnyParams P;
     if (!skinny_params(s.ncol, a.G, s.splitk, s.rb, s.wm, s.wk, P))
         return "a wave's groups exceed its load registers, or the staged data the workgroup's LDS; "

@@ -108,6 +108,34 @@ __global__ void __launch_bounds__(256) xpack_tm_kernel(const uint16_t* __restric
     if (n0 + lo < N) xp[(ko0 + hi) * N + n0 + lo] = tile[hi * 17 + lo];
 }
 
+// The same transpose from a gate/up output gu [N, 2K] (token-major): the
+// chunks hold silu(gate) * up, formed in float32 and rounded once to fp16.
+__device__ __forceinline__ uint32_t silu_mul_h2(uint32_t g, uint32_t u) {
+    const half2v gh = as_h2(g), uh = as_h2(u);
+    const float g0 = (float)gh[0], g1 = (float)gh[1];
+    const _Float16 lo = (_Float16)(g0 / (1.0f + expf(-g0)) * (float)uh[0]);
+    const _Float16 hi = (_Float16)(g1 / (1.0f + expf(-g1)) * (float)uh[1]);
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+__global__ void __launch_bounds__(256) xpack_silu_kernel(const uint16_t* __restrict__ gu, u32x4* __restrict__ xp,
+                                                         int64_t K, int64_t N) {
+    __shared__ u32x4 tile[16 * 17];
+    const int64_t KO = K / 8;
+    const int64_t kob = KO / 16;
+    const int64_t ko0 = ((int64_t)blockIdx.x % kob) * 16, n0 = ((int64_t)blockIdx.x / kob) * 16;
+    const int t = threadIdx.x, lo = t & 15, hi = t >> 4;
+    if (n0 + hi < N) {
+        const uint16_t* row = gu + (n0 + hi) * 2 * K + (ko0 + lo) * 8;
+        const u32x4 g = *reinterpret_cast<const u32x4*>(row);
+        const u32x4 u = *reinterpret_cast<const u32x4*>(row + K);
+        tile[lo * 17 + hi] = permute_k8(u32x4{silu_mul_h2(g.x, u.x), silu_mul_h2(g.y, u.y), silu_mul_h2(g.z, u.z),
+                                              silu_mul_h2(g.w, u.w)});
+    }
+    __syncthreads();
+    if (n0 + lo < N) xp[(ko0 + hi) * N + n0 + lo] = tile[hi * 17 + lo];
+}
+
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM>
 __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
@@ -393,8 +421,12 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
     if (a.xp_ready) return hipSuccess;
     if (a.tm) {
         const int64_t blocks = (a.K / 128) * ((a.N + 15) / 16);
-        hipLaunchKernelGGL(xpack_tm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.x,
-                           reinterpret_cast<u32x4*>(a.xp), a.K, a.N);
+        if (a.act)
+            hipLaunchKernelGGL(xpack_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.x,
+                               reinterpret_cast<u32x4*>(a.xp), a.K, a.N);
+        else
+            hipLaunchKernelGGL(xpack_tm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.x,
+                               reinterpret_cast<u32x4*>(a.xp), a.K, a.N);
         return hipGetLastError();
     }
     u32x4* xp = reinterpret_cast<u32x4*>(a.xp);

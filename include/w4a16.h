@@ -390,6 +390,25 @@ size_t w4a16_decode_attention_workspace_size_plan(int64_t B, int64_t H,
 int w4a16_silu_mul(const void *gu, void *act, int64_t N, int64_t I,
                    void *stream);
 
+/*
+ * The down projection of the decoder layer's MLP with its gated activation
+ * as a prologue (token-major):
+ *   c[n, m] = sum_k Wdeq[m, k] * act[n, k],
+ *   act[n, k] = fp16(silu(gu[n, k]) * gu[n, K + k])  (as w4a16_silu_mul)
+ *   gu : fp16 [N, 2 K], the fused gate/up projection's output;  c : fp16 [N, M]
+ * act never reaches memory: the skinny kernel forms it while staging the
+ * activations, the tiled and narrow kernels while rewriting them into their
+ * chunk layout.  Bit-identical to w4a16_silu_mul followed by w4a16_gemm_ex
+ * (token layout) under the same plan.  plan NULL: the token-major default.
+ * Workspace as w4a16_workspace_size_ex(M, N, K, 128, W4A16_LAYOUT_TOKEN,
+ * plan); other requirements and errors as w4a16_gemm_ex.
+ */
+int w4a16_gemm_silu(const uint32_t *q_packed, const void *scales,
+                    const uint32_t *z_packed, const void *gu, void *c,
+                    int64_t M, int64_t N, int64_t K, int32_t group_size,
+                    const w4a16_plan *plan, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* One W4A16 linear layer's weights, as w4a16_gemm takes them. */
 typedef struct {
     const uint32_t *q_packed;
@@ -419,8 +438,7 @@ typedef struct {
  *   a   = decode attention(qkv, caches, pos)                  (w4a16_decode_attention)
  *   x   = a . Wo^T                                             (w4a16_gemm_ex)
  *   r   = fp16(x + r);  y = rmsnorm(r) * mlp_norm;  gu = y . Wgu^T
- *   act = silu(gate) * up                                       (w4a16_silu_mul)
- *   x   = act . Wdown^T                                         (w4a16_gemm_ex)
+ *   x   = (silu(gate) * up) . Wdown^T                          (w4a16_gemm_silu)
  * residual (r) and x are fp16 [B, H D], both read and overwritten: on entry
  * x is the previous layer's output still to be added to the stream, on exit
  * this layer's.  Default plans, scale 1 / sqrt(D).  Every step is checked

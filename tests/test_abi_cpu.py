@@ -372,3 +372,14 @@ def test_decode_layer_and_silu_checks(lib):
             == INVALID)
     assert (lib.w4a16_decode_layer(ctypes.byref(layer), 1, 4, 128, 1024, 64, 64, X, 1e-6, 1e4, Q, S, WS, need - 1,
                                    NULL) == WORKSPACE)
+
+
+def test_gemm_silu_checks(lib):
+    # output over the gate/up input's second half (gu is N x 2K)
+    M, N, K = 64, 2, 256
+    assert lib.w4a16_gemm_silu(Q, S, Z, X, ctypes.c_void_p(0x400000 + N * K * 2), M, N, K, 128, None, WS, 1 << 20,
+                               NULL) == INVALID
+    assert lib.w4a16_gemm_silu(Q, S, Z, X, C, M, N, K, 64, None, WS, 1 << 20, NULL) == UNSUPPORTED
+    assert lib.w4a16_gemm_silu(NULL, S, Z, X, C, M, N, K, 128, None, WS, 1 << 20, NULL) == INVALID
+    sk = B.Plan.make(kernel=B.KERNEL_SKINNY, ncol=16, rb=1, wm=1, wk=4, splitk=1)
+    assert lib.w4a16_gemm_silu(Q, S, Z, X, C, M, 16, 1152, 128, ctypes.byref(sk), WS, 1 << 20, NULL) == UNSUPPORTED

@@ -160,3 +160,44 @@ def test_decode_graph_replays_match_eager():
         for lg, le in zip(g.layers, e.layers):
             assert torch.equal(lg["k_cache"].view(torch.int16), le["k_cache"].view(torch.int16)), step
     assert g.graph is not None
+
+
+FUSED_SILU = [
+    # (M, K, N, plan fields or None): the skinny kernel (N <= 8, with and
+    # without splits), narrow and tiled kernels, ragged tails
+    (300, 1152, 1, None),
+    (77, 1152, 5, None),
+    (96, 1152, 8, dict(kernel=1, ncol=8, rb=1, wm=2, wk=2, splitk=3)),
+    (130, 4096, 1, dict(kernel=1, ncol=1, rb=1, wm=1, wk=8, splitk=2)),
+    (300, 1152, 16, None),
+    (257, 4096, 11, dict(kernel=3, ncol=16, pf=16, splitk=3, rb=1, wk=1)),
+    (333, 1152, 100, None),
+    (129, 384, 130, dict(kernel=2, bm=256, bn=128, splitk=2, wm=4)),
+    (4096, 11008, 1, None),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_SILU, ids=lambda c: "M%d_K%d_N%d" % c[:3])
+def test_gemm_silu(case):
+    """The fused activation prologue equals silu_mul + the token-major GEMM
+    bit for bit, and meets the GEMM rule against the oracle."""
+    M, K, N, fields = case
+    log("gemm_silu %s" % (case[:3],))
+    p = Problem(M, K, seed=300 + N)
+    rng = np.random.default_rng(M + K + N)
+    gu = (rng.standard_normal((N, 2 * K), dtype=np.float32) * 2).astype(np.float16)
+    plan = None if fields is None else B.Plan.make(**fields)
+    gud = dev(gu)
+    fused = B.gemm_silu(p.qpk, p.s_d, p.zpk, gud, plan=plan)
+    act = B.silu_mul(gud)
+    ref_gpu = B.gemm(p.qpk, p.s_d, p.zpk, act, plan=plan, layout=B.LAYOUT_TOKEN)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), ref_gpu.view(torch.int16))
+    a_ref = ora.silu_mul(gu)
+    C_ref, A_ref = (p.reference(a_ref.T) if M <= 512 else
+                    p.reference_rows(a_ref.T, np.random.default_rng(1).choice(M, 64, replace=False)))
+    C = fused.cpu().numpy().T
+    if M > 512:
+        C = C[np.random.default_rng(1).choice(M, 64, replace=False)]
+    from gpu_util import assert_parity
+    assert_parity(C, C_ref, A_ref, "gemm_silu %s" % (case[:3],))
