@@ -440,6 +440,26 @@ int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, 
     a.scales = static_cast<const uint16_t*>(scales);
     a.zpk = zpk;
     a.c = static_cast<uint16_t*>(c);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // one launch: the skinny kernel normalizes while it stages (every
+    // workgroup reads all of x and the residual, so h must not be the
+    // residual itself, and one workgroup must cover all of K)
+    if (p.kernel == W4A16_KERNEL_SKINNY && p.splitk == 1 && h != residual) {
+        GemmArgs an = a;
+        an.norm = 1;
+        an.eps = eps;
+        an.x = static_cast<const uint16_t*>(x);
+        an.res = static_cast<const uint16_t*>(residual);
+        an.gamma = static_cast<const uint16_t*>(gamma);
+        an.hout = static_cast<uint16_t*>(h);
+        const char* why = skinny_check(an, skinny_of(p));
+        if (!why) {
+            if (dry) return ok();
+            hipError_t e = launch_skinny(an, skinny_of(p), s);
+            if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+            return ok();
+        }
+    }
     const bool chunks = p.kernel != W4A16_KERNEL_SKINNY;
     if (chunks) {
         a.xp = y;
@@ -450,7 +470,6 @@ int run_gemm_norm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, 
     }
     if (dry) return ok();
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_add_rmsnorm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(residual),
                                       static_cast<const uint16_t*>(gamma), eps, static_cast<uint16_t*>(h), y, N, K,
                                       chunks, s);
@@ -576,10 +595,11 @@ int run_silu_mul(const void* gu, void* act, int64_t N, int64_t I, void* stream, 
 }
 
 // Decoder layer workspace: [shared region: the largest workspace any step
-// needs, steps run one after another][qkv][attention output][gate/up], each
-// at a 256-byte boundary.  The down projection forms silu(gate) * up itself.
+// needs, steps run one after another][qkv][attention output][gate/up][the
+// stream after the attention's residual add], each at a 256-byte boundary.
+// The down projection forms silu(gate) * up itself.
 struct LayerLayout {
-    size_t shared, qkv, attn, gu, total;
+    size_t shared, qkv, attn, gu, h, total;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -620,7 +640,8 @@ int layer_layout(int64_t B, int64_t H, int64_t D, int64_t I, int64_t S, int64_t 
     L.qkv = L.shared;
     L.attn = L.qkv + round256((size_t)B * 3 * HD * 2);
     L.gu = L.attn + round256((size_t)B * HD * 2);
-    L.total = L.gu + round256((size_t)B * 2 * I * 2);
+    L.h = L.gu + round256((size_t)B * 2 * I * 2);
+    L.total = L.h + round256((size_t)B * HD * 2);
     return W4A16_OK;
 }
 
@@ -645,13 +666,17 @@ int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_
     void* qkv = w + L.qkv;
     void* attn = w + L.attn;
     void* gu = w + L.gu;
+    void* hbuf = w + L.h;
     const int64_t HD = H * D;
     const float scale = (float)(1.0 / sqrt((double)D));
     // every step checked first (dry), then enqueued
     for (int pass = 0; pass < 2; ++pass) {
         const bool dry = pass == 0;
+        // the stream goes residual -> hbuf -> residual, so that no
+        // normalizing step writes the buffer it reads (the skinny kernel's
+        // one-launch prologue needs that)
         st = run_gemm_norm(ly->qkv.q_packed, ly->qkv.scales, ly->qkv.z_packed, x, residual, ly->attn_norm, eps,
-                           residual, qkv, 3 * HD, B, HD, kGroupSize, nullptr, shared, L.shared, stream, dry);
+                           hbuf, qkv, 3 * HD, B, HD, kGroupSize, nullptr, shared, L.shared, stream, dry);
         if (!st)
             st = run_attention(qkv, ly->k_cache, ly->v_cache, pos, attn, B, H, D, S, max_len, rope_base, scale,
                                shared, L.shared, stream, dry);
@@ -659,7 +684,7 @@ int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_
             st = run_gemm(ly->o.q_packed, ly->o.scales, ly->o.z_packed, attn, x, HD, B, HD, kGroupSize,
                           W4A16_LAYOUT_TOKEN, nullptr, shared, L.shared, stream, dry);
         if (!st)
-            st = run_gemm_norm(ly->gate_up.q_packed, ly->gate_up.scales, ly->gate_up.z_packed, x, residual,
+            st = run_gemm_norm(ly->gate_up.q_packed, ly->gate_up.scales, ly->gate_up.z_packed, x, hbuf,
                                ly->mlp_norm, eps, residual, gu, 2 * I, B, HD, kGroupSize, nullptr, shared, L.shared,
                                stream, dry);
         if (!st)

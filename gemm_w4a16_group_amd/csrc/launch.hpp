@@ -21,6 +21,13 @@ struct GemmArgs {
     int32_t xp_ready;         // 1: a.xp already holds the activation chunks (no rewrite before the GEMM)
     int32_t act;              // 1: x is a gate/up output [N, 2K] (token-major); the activations are
                               //    silu(gate) * up, formed while staging or rewriting them
+    // residual add + RMSNorm while staging (skinny kernel, token-major, splitk 1): the
+    // activations are rmsnorm(x + res) * gamma and h = fp16(x + res) is written to hout
+    int32_t norm;
+    float eps;
+    const uint16_t* res;      // [N, K]
+    const uint16_t* gamma;    // [K]
+    uint16_t* hout;           // [N, K], must not alias x or res
 };
 
 // One decode step of multi-head attention (head dimension 128).

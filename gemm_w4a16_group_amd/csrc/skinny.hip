@@ -41,6 +41,7 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 // half bank-row later so that both the load-order writes and the MFMA-order
 // reads touch all 64 banks.
 constexpr int kPairBytes = 2304;
+constexpr uint32_t kNormSumBytes = 16 * 8 * 4;   // [waves][8 columns] float sums of squares
 
 // Activation columns the kernel is built for: any N <= 8, or 16 or 32.
 __host__ __device__ constexpr bool ncol_ok(int n) {
@@ -78,6 +79,7 @@ struct SkinnyParams {
     uint32_t t_off;           // group-sum table offset inside it
     uint32_t q_off;           // two weight-transpose buffers inside it
     uint32_t flag_off, total; // arrival flag, total dynamic LDS
+    uint32_t norm_off;        // per-wave column sums of squares (normalizing prologue), after the rest
 };
 
 // Every wave stages, in its own LDS region, what its groups need: the
@@ -166,6 +168,19 @@ struct XStage {
     static constexpr int T8 = NT < 8 ? NT : 8;
     static constexpr int NB8 = NT <= 8 ? 1 : NT / 8;   // column octets
     u32x4 v[T8];
+    u32x4 r[T8];   // normalizing prologue: the residual's octets
+    u32x4 g;       //   and the gains of the octet
+
+    // normalizing prologue (token-major, NT <= 8): x, the residual and the gains
+    __device__ __forceinline__ void load_norm(const uint16_t* x, const uint16_t* res, const uint16_t* gamma,
+                                              int64_t k0, int64_t K) {
+#pragma unroll
+        for (int t = 0; t < T8; ++t) {
+            v[t] = *reinterpret_cast<const u32x4*>(x + (int64_t)t * K + k0);
+            r[t] = *reinterpret_cast<const u32x4*>(res + (int64_t)t * K + k0);
+        }
+        g = *reinterpret_cast<const u32x4*>(gamma + k0);
+    }
 
     template <bool ACT>
     __device__ __forceinline__ void load(const uint16_t* x, int64_t k0, int nb8, bool tm, int64_t K) {
@@ -248,10 +263,13 @@ __device__ __forceinline__ void group_sums_one_column(const u32x4& v, int b, int
     if ((b & 15) == 0 && b < nxb) stab[b >> 4] = t;
 }
 
-// ACT: the activations are computed from the gate/up output while staging
-// (token-major, NT <= 8); the kernels below instantiate the body both ways.
-template <int NT, int PF, bool ACT>
+// MODE 1: the activations are silu(gate) * up of a gate/up output, formed
+// while staging; MODE 2: they are rmsnorm(x + res) * gamma, the sum of
+// squares of each column reduced over the workgroup (which covers all of K)
+// while the weights are in flight.  Both token-major, NT <= 8.
+template <int NT, int PF, int MODE>
 __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParams& P) {
+    constexpr bool ACT = MODE == 1, NORM = MODE == 2;
     constexpr int F = skinny_staging_loads(NT, PF); // activation loads per lane
     constexpr int TB = (NT + 15) / 16;              // 16-column MFMA blocks
     constexpr int NB8 = XStage<NT>::NB8;
@@ -301,6 +319,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     // ---- 1. activations of the wave's groups: block b = lane + 64 j
     const int nxb = ng * 16 * NB8;
     XStage<NT> xst[F];
+    int64_t k0s[F];   // normalizing prologue: where each block sits along K
 #pragma unroll
     for (int j = 0; j < F; ++j) {
         int b = lane + j * 64;
@@ -308,7 +327,11 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
         const int o = b / NB8, nb8 = b % NB8;     // NB8 is a power of two
         int64_t k0 = (int64_t)gw0 * kGroup + (int64_t)o * 8;
         k0 = k0 < a.K - 8 ? k0 : a.K - 8;
-        xst[j].template load<ACT>(a.x, k0, nb8, a.tm != 0, a.K);
+        k0s[j] = k0;
+        if constexpr (NORM)
+            xst[j].load_norm(a.x, a.res, a.gamma, k0, a.K);
+        else
+            xst[j].template load<ACT>(a.x, k0, nb8, a.tm != 0, a.K);
     }
     // ---- 2. scales: lane (row li, group 4 j + kb); zero words: lane (row
     // li, word kb)
@@ -344,6 +367,77 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
             buf[pp][h] = __builtin_nontemporal_load(src);
         }
     __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3b. normalizing prologue, while the weights are in flight: h =
+    // fp16(x + res) per block (written out by the first row tile), the
+    // squares of h summed per column over the wave's blocks, then over the
+    // waves along K in LDS (the workgroup covers all of K), and the staged
+    // activations become fp16(h * rsqrt(mean h^2 + eps) * gamma)
+    if constexpr (NORM) {
+        constexpr int T8 = XStage<NT>::T8;
+        float ssq[T8];
+#pragma unroll
+        for (int t = 0; t < T8; ++t) ssq[t] = 0.f;
+        const bool write_h = blockIdx.x == 0 && wave_m == 0;
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const bool live = lane + j * 64 < nxb;   // clamped duplicates count once
+#pragma unroll
+            for (int t = 0; t < T8; ++t) {
+                const uint32_t xw[4] = {xst[j].v[t].x, xst[j].v[t].y, xst[j].v[t].z, xst[j].v[t].w};
+                const uint32_t rw[4] = {xst[j].r[t].x, xst[j].r[t].y, xst[j].r[t].z, xst[j].r[t].w};
+                uint32_t hw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half2v xh = as_h2(xw[i]), rh = as_h2(rw[i]);
+                    const _Float16 lo = (_Float16)((float)xh[0] + (float)rh[0]);
+                    const _Float16 hi = (_Float16)((float)xh[1] + (float)rh[1]);
+                    if (live) {
+                        ssq[t] = fmaf((float)lo, (float)lo, ssq[t]);
+                        ssq[t] = fmaf((float)hi, (float)hi, ssq[t]);
+                    }
+                    hw[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                xst[j].v[t] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                if (write_h && live)
+                    *reinterpret_cast<u32x4*>(a.hout + (int64_t)t * a.K + k0s[j]) = xst[j].v[t];
+            }
+        }
+        float* nsum = reinterpret_cast<float*>(smem + P.norm_off);
+#pragma unroll
+        for (int t = 0; t < T8; ++t) {
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) ssq[t] += __shfl_xor(ssq[t], m);
+            if (lane == 0) nsum[wave * 8 + t] = ssq[t];
+        }
+        __syncthreads();
+        float rs[T8];
+#pragma unroll
+        for (int t = 0; t < T8; ++t) {
+            float tot = 0.f;
+            for (int k = 0; k < P.wk; ++k) tot += nsum[(k * P.wm + wave_m) * 8 + t];
+            rs[t] = 1.0f / sqrtf(tot / (float)a.K + a.eps);
+        }
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const uint32_t gw[4] = {xst[j].g.x, xst[j].g.y, xst[j].g.z, xst[j].g.w};
+#pragma unroll
+            for (int t = 0; t < T8; ++t) {
+                const uint32_t hw[4] = {xst[j].v[t].x, xst[j].v[t].y, xst[j].v[t].z, xst[j].v[t].w};
+                uint32_t yw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half2v hh = as_h2(hw[i]), gg = as_h2(gw[i]);
+                    const _Float16 lo = (_Float16)((float)hh[0] * rs[t] * (float)gg[0]);
+                    const _Float16 hi = (_Float16)((float)hh[1] * rs[t] * (float)gg[1]);
+                    yw[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                xst[j].v[t] = u32x4{yw[0], yw[1], yw[2], yw[3]};
+            }
+        }
+    }
 
     // ---- 4. stage activations, scales and zeros; group sums
     // S[g][t] = sum of the group's 128 activations of column t
@@ -551,19 +645,26 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
 
 template <int NT, int PF>
 __global__ void __launch_bounds__(kMaxThreads) skinny_kernel(GemmArgs a, SkinnyParams P) {
-    skinny_body<NT, PF, false>(a, P);
+    skinny_body<NT, PF, 0>(a, P);
 }
 
 template <int NT, int PF>
 __global__ void __launch_bounds__(kMaxThreads) skinny_silu_kernel(GemmArgs a, SkinnyParams P) {
-    skinny_body<NT, PF, true>(a, P);
+    skinny_body<NT, PF, 1>(a, P);
 }
 
-template <int NT, int PF, bool ACT>
+template <int NT, int PF>
+__global__ void __launch_bounds__(kMaxThreads) skinny_norm_kernel(GemmArgs a, SkinnyParams P) {
+    skinny_body<NT, PF, 2>(a, P);
+}
+
+template <int NT, int PF, int MODE>
 hipError_t launch_kernel(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
     const void* fn;
-    if constexpr (ACT)
+    if constexpr (MODE == 1)
         fn = reinterpret_cast<const void*>(&skinny_silu_kernel<NT, PF>);
+    else if constexpr (MODE == 2)
+        fn = reinterpret_cast<const void*>(&skinny_norm_kernel<NT, PF>);
     else
         fn = reinterpret_cast<const void*>(&skinny_kernel<NT, PF>);
     dim3 grid((unsigned)((a.M + P.rows - 1) / P.rows), (unsigned)s.splitk);
@@ -575,8 +676,10 @@ hipError_t launch_kernel(const GemmArgs& a, const SkinnyShape& s, const SkinnyPa
         return e;
     }();
     if (lds_ok != hipSuccess && P.total > 65536) return lds_ok;
-    if constexpr (ACT)
+    if constexpr (MODE == 1)
         hipLaunchKernelGGL((skinny_silu_kernel<NT, PF>), grid, block, P.total, stream, a, P);
+    else if constexpr (MODE == 2)
+        hipLaunchKernelGGL((skinny_norm_kernel<NT, PF>), grid, block, P.total, stream, a, P);
     else
         hipLaunchKernelGGL((skinny_kernel<NT, PF>), grid, block, P.total, stream, a, P);
     return hipGetLastError();
@@ -584,9 +687,16 @@ hipError_t launch_kernel(const GemmArgs& a, const SkinnyShape& s, const SkinnyPa
 
 template <int NT, int PF>
 hipError_t launch_one(const GemmArgs& a, const SkinnyShape& s, const SkinnyParams& P, hipStream_t stream) {
-    if constexpr (NT <= 8)
-        if (a.act) return launch_kernel<NT, PF, true>(a, s, P, stream);
-    return launch_kernel<NT, PF, false>(a, s, P, stream);
+    if constexpr (NT <= 8) {
+        if (a.act) return launch_kernel<NT, PF, 1>(a, s, P, stream);
+        if (a.norm) {
+            SkinnyParams Q = P;
+            Q.norm_off = (P.total + 15u) & ~15u;
+            Q.total = Q.norm_off + kNormSumBytes;
+            return launch_kernel<NT, PF, 2>(a, s, Q, stream);
+        }
+    }
+    return launch_kernel<NT, PF, 0>(a, s, P, stream);
 }
 
 template <int NT>
@@ -621,10 +731,16 @@ const char* skinny_check(const GemmArgs& a, const SkinnyShape& s) {
     if (s.splitk > a.G) return "splitk exceeds the number of groups";
     if (a.tm && a.N > 8) return "token-major activations only for N <= 8";
     if (a.act && !a.tm) return "the gated activation prologue needs token-major activations";
+    if (a.norm) {
+        if (!a.tm || a.N > 8) return "the normalizing prologue needs token-major activations and N <= 8";
+        if (s.splitk != 1) return "the normalizing prologue needs splitk 1 (a workgroup covers all of K)";
+    }
     SkinnyParams P;
     if (!skinny_params(s.ncol, a.G, s.splitk, s.rb, s.wm, s.wk, P))
         return "a wave's groups exceed its load registers, or the staged data the workgroup's LDS; "
                "add waves along K or splits";
+    if (a.norm && ((P.total + 15u) & ~15u) + kNormSumBytes > (uint32_t)kMaxLds)
+        return "the normalizing prologue's sums do not fit in LDS";
     return nullptr;
 }
 

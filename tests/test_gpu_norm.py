@@ -102,6 +102,10 @@ FUSED = [
     (257, 1152, 264, dict(kernel=2, bm=128, bn=256, splitk=2, wm=2)),
     (129, 384, 130, dict(kernel=2, bm=256, bn=128, splitk=2, wm=4)),
     (64, 11008, 5, None),
+    # the one-launch prologue inside the skinny kernel: waves along M and K
+    (200, 1152, 4, dict(kernel=1, ncol=4, rb=1, wm=2, wk=4, splitk=1)),
+    (77, 1152, 8, dict(kernel=1, ncol=8, rb=1, wm=2, wk=2, splitk=1)),
+    (33, 4096, 2, dict(kernel=1, ncol=2, rb=1, wm=1, wk=16, splitk=1)),
 ]
 
 
