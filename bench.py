@@ -49,12 +49,19 @@ def alg_flops(M, K, N):
 
 
 def sources_sha(kernel):
-    """sha256 over the source files a kernel is built from."""
+    """sha256 over the code of the source files a kernel is built from
+    (comments and blank lines left out, so that editing a comment does not
+    retire the stored counters)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel.split("<")[0]]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+        h.update(code.encode())
     return h.hexdigest()
 
 

@@ -3,8 +3,11 @@
 // tokens, item 2 for one token).
 //
 // Every packed weight word is read from HBM exactly once, with 16-byte
-// loads: lane (r, kb) of a wave reads words 4kb .. 4kb+3 of one 128-weight
-// group of row r, so one load per lane brings in a whole group of 16 rows.
+// loads: eight lanes read one row's 128 bytes of a group pair, so one load
+// instruction brings in eight rows x 128 bytes (whole lines); a per-wave LDS
+// transpose then gives lane (r, kb) words 4kb .. 4kb+3 of row r's group,
+// the MFMA layout (16-row x 64-byte loads straight into that layout stream
+// about a fifth slower).
 // The B operand of a 16x16x32 fp16 MFMA is made from each word with two
 // masks and a shift and nothing else: a nibble q at bits 0-3 of a half is
 // the fp16 subnormal q * 2^-24, a nibble at bits 4-7 is 16 q * 2^-24 (the
@@ -28,6 +31,12 @@
 // Latency: all small loads (scales, zeros, activations) are issued before
 // the weight loads, so that staging them never waits for the weight stream;
 // up to PF groups of weights per wave are in flight at any time.
+//
+// Prologues (token-major activations, N <= 8), each its own kernel name so
+// that the plain kernel's code is untouched: skinny_silu_kernel stages
+// silu(gate) * up of a gate/up output; skinny_norm_kernel stages
+// rmsnorm(x + res) * gamma, reducing the sums of squares over the workgroup
+// while the weights are in flight.
 #include "device.hpp"
 #include "launch.hpp"
 

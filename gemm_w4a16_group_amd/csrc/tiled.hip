@@ -5,7 +5,9 @@
 // Two launches.  xpack_kernel rewrites the activations X [K, N] (N
 // contiguous) once into 16-byte chunks, chunk (ko, n) holding the eight k of
 // octet ko of column n in the order 0, 4, 1, 5, 2, 6, 3, 7 that the
-// dequantized weight words use.  The chunks are exactly the B operand of
+// dequantized weight words use (xpack_col_kernel for N <= 32,
+// xpack_tm_kernel for token-major X^T [N, K], xpack_silu_kernel for a
+// gate/up output; the normalizing prologue writes the chunks itself).  The chunks are exactly the B operand of
 // v_mfma_f32_32x32x16_f16, so the GEMM stages them into LDS with
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
 // reads them back conflict-free.
