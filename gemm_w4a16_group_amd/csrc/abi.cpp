@@ -149,12 +149,12 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
             if (wk < 1) wk = 1;
             while (wk * p.wm > 16) wk /= 2;
             // small grids: more waves along K (at least two groups each);
-            // up to twice as many while every wave keeps four groups, except
-            // at N = 2 (measured at 12288x4096: N = 1 and N >= 3 gain 3-9 %,
-            // N = 2 loses 12 %)
+            // up to twice as many while every wave keeps four groups
+            // (measured: 12288x4096 N = 1, 2 and 22016x4096 N = 1 gain
+            // 2-6 %)
             while (wk * 2 * p.wm <= 16 && ngs >= 4 * wk &&
                    (tiles * splitk * p.wm * wk < 2048 ||
-                    (N != 2 && tiles * splitk * p.wm * wk < 4096 && ngs >= 8 * wk)))
+                    (tiles * splitk * p.wm * wk < 8192 && ngs >= 8 * wk)))
                 wk *= 2;
             p.wk = (int32_t)wk;
             p.splitk = (int32_t)splitk;

@@ -86,7 +86,7 @@ struct SkinnyParams {
     uint32_t wave_bytes;      // one wave's LDS region
     uint32_t s_off, z_off;    // scale / zero-word offsets inside it
     uint32_t t_off;           // group-sum table offset inside it
-    uint32_t q_off;           // two weight-transpose buffers inside it
+    uint32_t q_off;           // the weight-transpose buffer inside it
     uint32_t flag_off, total; // arrival flag, total dynamic LDS
     uint32_t norm_off;        // per-wave column sums of squares (normalizing prologue), after the rest
 };
@@ -126,7 +126,7 @@ inline bool skinny_params(int NT, int G, int splitk, int rb, int wm, int wk, Ski
     P.z_off = (uint32_t)(P.s_off + ((sb + 15) & ~(size_t)15));
     P.t_off = (uint32_t)(P.z_off + ((zb + 15) & ~(size_t)15));
     P.q_off = (uint32_t)(P.t_off + ((tb + 15) & ~(size_t)15));
-    const size_t wave_bytes = P.q_off + 2 * (size_t)kPairBytes;
+    const size_t wave_bytes = P.q_off + (size_t)kPairBytes;
     size_t main_bytes = wave_bytes * wm * wk;
     // partial sums of waves 1 .. wk-1, written after the staged data is dead
     const size_t red = (size_t)(wk - 1) * wm * rb * TB * 4 * 64 * 4;
@@ -516,7 +516,13 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
         if (2 * pp < ng) {
-            unsigned char* qb = qbuf + (pp & 1) * kPairBytes;
+            // one transpose buffer: a wave's LDS accesses complete in
+            // order, so these writes cannot overtake the previous pair's
+            // reads; the fences keep the compiler from moving them up
+            unsigned char* qb = qbuf;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             *reinterpret_cast<u32x4*>(qb + wslot0) = buf[pp][0];
             *reinterpret_cast<u32x4*>(qb + wslot1) = buf[pp][1];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

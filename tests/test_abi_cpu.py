@@ -172,7 +172,7 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
 def test_kernel_name_follows_the_plan(lib):
     # eight waves along K, four groups each: four weight groups in flight per wave
     assert B.kernel_name(12288, 1, 4096) == "skinny_kernel<1, 4>"
-    assert B.kernel_name(22016, 1, 4096) == "skinny_kernel<1, 8>"
+    assert B.kernel_name(4096, 1, 11008) == "skinny_kernel<1, 8>"
     assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<256, 128, 4>"
     p = B.Plan.make(kernel=2, bm=128, bn=256, splitk=1, wm=2)
     assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2>"
