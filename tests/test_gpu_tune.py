@@ -27,3 +27,21 @@ def test_tuned_plan_is_valid_and_correct(N, layout):
     C = run(p, X, plan=plan, layout=layout)
     C_ref, A_ref = p.reference(X)
     assert_parity(C, C_ref, A_ref, "tuned N=%d %s" % (N, plan.as_dict()))
+
+
+def test_plan_table_tunes_and_serves(tmp_path):
+    """A tuned table entry round-trips through JSON and drives gemm()."""
+    from gemm_w4a16_group_amd.plans import PlanTable
+    M, K, N = 300, 1152, 24
+    p = Problem(M, K, seed=90)
+    X = inputs.activations(K, N, wid=790)
+    t = PlanTable()
+    t.tune(p.qpk, p.s_d, p.zpk, dev(X), iters=2)
+    path = tmp_path / "plans.json"
+    t.save(str(path))
+    u = PlanTable.load(str(path))
+    assert u.plan(M, N, K) is not None
+    C = u.gemm(p.qpk, p.s_d, p.zpk, dev(X))
+    torch.cuda.synchronize()
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C.cpu().numpy(), C_ref, A_ref, "plan table")
