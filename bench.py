@@ -87,13 +87,16 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=400)
+    # about 0.3 s of untimed calls first: from idle the clocks take a few
+    # milliseconds to ramp up, and the first thousands of calls run slower
+    ap.add_argument("--warmup", type=int, default=40000)
     ap.add_argument("--copies", type=int, default=40, help="weight copies cycled through (cold cache)")
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
                              "quantize_12288x4096", "prologue", "attention", "tune_table", "decode_step"])
     ap.add_argument("--gemm-iters", type=int, default=20)
+    ap.add_argument("--gemm-warmup", type=int, default=1000, help="untimed N = 4096 calls first (about 0.4 s)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
@@ -135,6 +138,17 @@ def capture(calls, stream):
     return g
 
 
+def warm_graph(g, stream, seconds):
+    """Replay ``g`` untimed for about ``seconds`` (clock ramp-up)."""
+    import torch
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        while time.time() - t0 < seconds:
+            for _ in range(4):
+                g.replay()
+            torch.cuda.synchronize()
+
+
 def time_graph(g, replays, stream):
     """Milliseconds of ``replays`` graph replays, HIP events on ``stream``."""
     import torch
@@ -171,8 +185,9 @@ def gemv_rotation(M, K, wid, copies, steps, warmup, plan=None):
     return ms / (reps * copies), B.plan_default(M, 1, K).as_dict(), reps * copies, lay, x, outs[0]
 
 
-def gemm_large(M, K, N, wid, iters):
-    """Eager timing of the large-N GEMM (each call is hundreds of us)."""
+def gemm_large(M, K, N, wid, iters, warmup=1000):
+    """Eager timing of the large-N GEMM (each call is hundreds of us), after
+    ``warmup`` untimed calls."""
     import torch
     from gemm_w4a16_group_amd import binding as B
     from gemm_w4a16_group_amd import inputs
@@ -182,7 +197,7 @@ def gemm_large(M, K, N, wid, iters):
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for _ in range(3):
+        for _ in range(warmup):
             B.gemm(qpk, sd, zpk, x, out=out)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
@@ -232,11 +247,11 @@ def cpu_baseline(M, K, seconds, wid):
     }
 
 
-def gemm_secondary(iters):
+def gemm_secondary(iters, warmup):
     """The N = 4096 GEMM figure (one call = activation re-layout + tiled kernel)."""
     from gemm_w4a16_group_amd import binding as B
     M, K, N = 12288, 4096, 4096
-    gms, gplan = gemm_large(M, K, N, 4, iters)
+    gms, gplan = gemm_large(M, K, N, 4, iters, warmup)
     tf = alg_flops(M, K, N) / (gms * 1e-3) / 1e12
     kern = B.kernel_name(M, N, K)
     return {
@@ -281,7 +296,7 @@ def headline(args):
                      "us_per_launch": round(ms * 1e3, 3)},
     }
     if not args.no_gemm:
-        line["secondary"] = gemm_secondary(args.gemm_iters)
+        line["secondary"] = gemm_secondary(args.gemm_iters, args.gemm_warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(M, K, args.cpu_seconds, wid)
     print(json.dumps(line), flush=True)
@@ -313,7 +328,7 @@ def extra(args):
         copy_calib()
         return
     if args.workload == "gemm_12288x4096_n4096":
-        print(json.dumps(gemm_secondary(args.gemm_iters)), flush=True)
+        print(json.dumps(gemm_secondary(args.gemm_iters, args.gemm_warmup)), flush=True)
         return
     if args.workload == "quantize_12288x4096":
         # fp16 weights -> packed codes, scales, packed zeros; 4 copies of the
@@ -413,7 +428,7 @@ def extra(args):
                     stream = torch.cuda.Stream()
                     g = capture(calls, stream)
                     reps = max(2, (args.steps // ncalls) if N <= 256 else 5)
-                    time_graph(g, 2, stream)
+                    warm_graph(g, stream, 0.3)
                     res[name] = time_graph(g, reps, stream) / (reps * ncalls) * 1e3
                     del g
                 print(json.dumps({"workload": "tune_table_12288x4096", "layout": "token" if layout else "kn",
@@ -447,7 +462,7 @@ def extra(args):
                      for k, v, o in zip(kcs, vcs, outs)]
             stream = torch.cuda.Stream()
             g = capture(calls, stream)
-            time_graph(g, 2, stream)
+            warm_graph(g, stream, 0.3)
             reps = max(2, args.steps // cps)
             us = time_graph(g, reps, stream) / (reps * cps) * 1e3
             print(json.dumps({"workload": "decode_attention", "B": Bn, "H": H, "D": D, "S": S,
@@ -484,7 +499,7 @@ def extra(args):
                 for vname, calls in variants.items():
                     stream = torch.cuda.Stream()
                     g = capture(calls, stream)
-                    time_graph(g, 2, stream)
+                    warm_graph(g, stream, 0.3)
                     reps = max(2, args.steps // cps)
                     res[vname] = time_graph(g, reps, stream) / (reps * cps) * 1e3
                     del g
@@ -524,7 +539,7 @@ def extra(args):
             stream = torch.cuda.Stream()
             g = capture(calls, stream)
             reps = max(2, (args.steps // ncalls) if N <= 256 else 5)
-            time_graph(g, 2, stream)
+            warm_graph(g, stream, 0.3)
             ms = time_graph(g, reps, stream) / (reps * ncalls)
             rows.append(("12288x4096" + ("_token" if args.token else ""), M, K, N, ms,
                          B.plan_default(M, N, K, layout).as_dict()))

@@ -29,6 +29,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
 // the first 64 KB of the workspace, so partial sums of one call can never
 // land on the counters of another call with a different shape.
 constexpr int64_t kCounterSlots = 16384;
+// compute units of an MI355X (default plans balance tiles over them)
+constexpr int64_t kCus = 256;
 constexpr size_t kCounterBytes = kCounterSlots * 4;
 
 int fail(int status, const char* fmt, ...) {
@@ -88,7 +90,9 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_LAYOU
 }
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
-TiledShape tiled_of(const w4a16_plan& p) { return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm}; }
+TiledShape tiled_of(const w4a16_plan& p) {
+    return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm, p.pf == 0 ? 1 : p.pf};
+}
 NarrowShape narrow_of(const w4a16_plan& p) {
     return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb, p.wk == 0 ? 1 : p.wk};
 }
@@ -107,7 +111,9 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // across workgroups only when the staged activations would not fit in LDS.
 //
 // Tiled kernel otherwise: 256 x 128 tiles from N = 4096 on (from N = 1024
-// when that still gives 256 tiles), 128 x 128 from N = 512, 128 x 64 below; a split along K only when there are too few
+// when that still gives 256 tiles), 128 x 128 from N = 512, 128 x 64 below,
+// 512 x 128 tiles of eight waves instead of 256 x 128 where they load the
+// CUs as evenly (e.g. N = 1024 and 4096 at M = 12288, not N = 2048); a split along K only when there are too few
 // tiles to fill the chip (N <= 32: two-way, four-way under 64 tiles; larger
 // N: two-way for long rows, K >= 8192).
 //
@@ -171,6 +177,19 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     // 256-row tiles from N = 1024 on when they still give 256 tiles
     p.bm = (N >= 4096 || (N >= 1024 && ((M + 255) / 256) * ((N + 127) / 128) >= 256)) ? 256 : 128;
     p.bn = N >= 512 ? 128 : 64;
+    // 512 x 128 tiles of eight waves (weights two stages ahead) from N = 1024
+    // when they give a CU no more rows than 256 x 128 tiles do: with one of
+    // them per CU against two of the others, the busiest CU then has the
+    // same work and the activation chunks are staged half as often
+    if (N >= 1024 && M >= 512) {
+        const int64_t t256 = ((M + 255) / 256) * ((N + 127) / 128);
+        const int64_t t512 = ((M + 511) / 512) * ((N + 127) / 128);
+        if ((t512 + kCus - 1) / kCus * 512 <= (t256 + kCus - 1) / kCus * 256) {
+            p.bm = 512;
+            p.wm = 8;
+            p.pf = 2;
+        }
+    }
     const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     int64_t splitk = 1;
     if (t < 160 && t <= kCounterSlots) {
@@ -364,18 +383,20 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
                         }
     }
     if (N >= 8) {
-        for (int bm : {128, 256})
+        for (int bm : {128, 256, 512})
             for (int bn : {64, 128, 256})
-                for (int wm : {4, 2})
-                    for (int splitk : {1, 2, 4}) {
-                        memset(&p, 0, sizeof(p));
-                        p.kernel = W4A16_KERNEL_TILED;
-                        p.bm = bm;
-                        p.bn = bn;
-                        p.wm = wm;
-                        p.splitk = splitk;
-                        add(p);
-                    }
+                for (int wm : {4, 2, 8})
+                    for (int pf : {0, 2})
+                        for (int splitk : {1, 2, 4}) {
+                            memset(&p, 0, sizeof(p));
+                            p.kernel = W4A16_KERNEL_TILED;
+                            p.bm = bm;
+                            p.bn = bn;
+                            p.wm = wm;
+                            p.pf = pf;
+                            p.splitk = splitk;
+                            add(p);
+                        }
     }
     return out;
 }
@@ -801,7 +822,10 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     else if (p.kernel == W4A16_KERNEL_NARROW)
         snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d>", p.ncol / 16, p.pf, narrow_of(p).rb, narrow_of(p).wk);
     else
-        snprintf(buf, len, "tiled_kernel<%d, %d, %d>", p.bm, p.bn, p.wm == 0 ? 4 : p.wm);
+    {
+        const TiledShape t = tiled_of(p);
+        snprintf(buf, len, "tiled_kernel<%d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf);
+    }
     return ok();
 }
 

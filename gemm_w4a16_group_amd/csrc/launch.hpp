@@ -51,7 +51,8 @@ struct SkinnyShape {
 
 struct TiledShape {
     int bm, bn, splitk;
-    int wm;   // waves along M: 4 (4 x 1) or 2 (2 x 2)
+    int wm;    // waves along M: 4 (4 x 1), 2 (2 x 2) or 8 (8 x 1, bm = 512)
+    int wpf;   // stages of weights loaded ahead: 1 or 2
 };
 
 struct NarrowShape {

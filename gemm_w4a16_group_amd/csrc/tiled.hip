@@ -139,16 +139,36 @@ __global__ void __launch_bounds__(256) xpack_silu_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM>
-__global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
-    constexpr int WGN = 4 / WGM;            // waves along N
+// NWV waves per workgroup (4 or 8) in a WGM x (NWV / WGM) grid.  WPF is how
+// many stages ahead a wave loads its weight words (1 or 2, in WPF + 1
+// register sets); the activation chunks are always one stage ahead (two LDS
+// buffers).  With WPF = 2 a stage ends by waiting for all but the newest
+// stage's weight loads instead of for every load: each stage issues its
+// activation loads before its weight loads, and loads return in order, so
+// that wait also covers the next stage's chunks.
+// Waves per SIMD the register budget is held to: two when a wave's
+// accumulators take at most 128 registers (so two waves fit in the 512),
+// else one.
+__host__ __device__ constexpr int tiled_waves_per_simd(int BM, int BN, int WGM, int NWV) {
+    return (BM / WGM / 32) * (BN / (NWV / WGM) / 32) * 16 <= 128 ? 2 : 1;
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF>
+__global__ void __launch_bounds__(64 * NWV)
+__attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd(BM, BN, WGM, NWV))))
+tiled_kernel(GemmArgs a, int splitk) {
+    constexpr int WGN = NWV / WGM;          // waves along N
     constexpr int WM = BM / WGM;            // rows per wave
     constexpr int WN = BN / WGN;            // columns per wave
     constexpr int RBW = WM / 32;            // 32-row MFMA blocks per wave
     constexpr int CBW = WN / 32;            // 32-column MFMA blocks per wave
     constexpr int XBYTES = kStageRows * BN * 16;        // one stage of activation chunks
-    constexpr int XLOADS = kStageRows * BN / 64 / 4;    // 1 KB buffer-to-LDS loads per wave and stage
-    static_assert(BN % 64 == 0 && XLOADS % (BN / 64) == 0, "tile");
+    constexpr int XLOADS = kStageRows * BN / 64 / NWV;  // 1 KB buffer-to-LDS loads per wave and stage
+    constexpr int NSET = WPF + 1;                       // weight register sets
+    constexpr int WLOADS = 4 * RBW;                     // weight, zero and scale loads per wave and stage
+    static_assert(BN % 64 == 0 && XLOADS >= 1 && XLOADS % (BN / 64) == 0, "tile");
+    static_assert(WPF == 1 || WPF == 2, "weight prefetch distance");
+    static_assert(WLOADS < 64, "vmcnt");
     __shared__ __attribute__((aligned(16))) unsigned char xs[2][XBYTES];
     __shared__ int flag;
 
@@ -215,18 +235,18 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
     }
     const int xrow = (int)(N * 16);   // bytes per chunk row
 
-    // weight words, zero word and scale of a stage, in two register sets
-    // used alternately (stage pairs are unrolled, so no copies between them)
-    u32x4 wA[RBW][2], wB[RBW][2];
-    uint32_t zA[RBW], sA[RBW], zB[RBW], sB[RBW];
+    // weight words, zero word and scale of a stage, in NSET register sets
+    // used in turn (the stage loop is unrolled NSET times, so no copies)
+    u32x4 wS[NSET][RBW][2];
+    uint32_t zS[NSET][RBW], sS[NSET][RBW];
 
-    auto load_w = [&](int g, u32x4 (*wr)[2], uint32_t* zr, uint32_t* sr) {
+    auto load_w = [&](int g, int set) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
-            wr[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, 0);
-            wr[rb][1] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb] + 16, g * 64, 0);
-            zr[rb] = __builtin_amdgcn_raw_buffer_load_b32(zres, zoff[rb], (g >> 3) * 4, 0);
-            sr[rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
+            wS[set][rb][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, 0);
+            wS[set][rb][1] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb] + 16, g * 64, 0);
+            zS[set][rb] = __builtin_amdgcn_raw_buffer_load_b32(zres, zoff[rb], (g >> 3) * 4, 0);
+            sS[set][rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
         }
     };
     auto load_x = [&](int g, int buf) {
@@ -254,19 +274,26 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
     // B fragment of lane (l32, hh), block cb, MFMA step t: chunk row 8 hh + t,
     // column WN wave_n + 32 cb + l32 -> one base plus an immediate offset
     const int bbase = ((8 * hh) * BN + WN * wave_n + l32) * 16;
+    const int last = st1 - 1;
 
-    // One stage: prefetch stage nx (weights into the other register set,
-    // activation chunks into the other LDS buffer), then 8 MFMA steps on
-    // stage st from buffer cur, then wait for the prefetch and meet.
-    auto stage = [&](int st, int nx, int cur, u32x4 (*wc)[2], const uint32_t* zc, const uint32_t* sc,
-                     u32x4 (*wn)[2], uint32_t* zn, uint32_t* sn) {
-        load_w(nx, wn, zn, sn);
+    // One stage st (the i-th of this split, weights in register set `set`):
+    // prefetch the next stage's activation chunks into the other LDS buffer
+    // and the weights of stage st + WPF into the set last used by stage
+    // st - 1 (both clamped to the last stage, which then loads itself again
+    // into a buffer or set nobody reads any more), then 8 MFMA steps on stage
+    // st, then wait for what the next stage reads and meet.
+    auto stage = [&](int st, int set) {
+        const int cur = (st - st0) & 1;
+        const int nx = st + 1 < st1 ? st + 1 : last;
+        const int nw = st + WPF < st1 ? st + WPF : last;
         load_x(nx, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(nw, (set + WPF) % NSET);
         // keep every load of the next stage at the top of this one
         __builtin_amdgcn_sched_barrier(0);
         // scale and zero of this group
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zc[rb] >> (4 * (st & 7))) & 0xFu, sc[rb]);
+        for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zS[set][rb] >> (4 * (st & 7))) & 0xFu, sS[set][rb]);
 
         const unsigned char* xb = &xs[cur][bbase];
         // A operand of MFMA step t: word t of the lane's eight (k-octet
@@ -279,7 +306,7 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
         };
         auto make_a = [&](int t, half8* af) {
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) af[rb] = dq[rb](wc[rb][t >> 2][t & 3]);
+            for (int rb = 0; rb < RBW; ++rb) af[rb] = dq[rb](wS[set][rb][t >> 2][t & 3]);
         };
         read_b(0, bfrag[0]);
         make_a(0, afrag[0]);
@@ -296,27 +323,44 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
                     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[t & 1][rb], bfrag[t & 1][cb],
                                                                          acc[rb][cb], 0, 0, 0);
         }
-        // the prefetched chunks have landed in LDS and every wave is done
-        // with buffer cur
-        __builtin_amdgcn_s_waitcnt(0);
+        // the next stage's chunks have landed in LDS (and its weights in
+        // registers) and every wave is done with buffer cur
+        if (WPF == 1)
+            __builtin_amdgcn_s_waitcnt(0);
+        else   // vmcnt(WLOADS); expcnt and lgkmcnt left alone
+            __builtin_amdgcn_s_waitcnt((WLOADS & 15) | ((WLOADS >> 4) << 14) | (7 << 4) | (15 << 8));
         __syncthreads();
+        // each stage is its own scheduling region (no stage's registers
+        // live into the next)
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // every split has at least one group (splitk <= G); the last stage
-    // prefetches itself again (no branch around the loads; the buffer it
-    // fills was last read before the previous barrier)
-    load_w(st0, wA, zA, sA);
+    // every split has at least one group (splitk <= G)
+    // (issue order kept: chunks, then stage st0's weights, then the next
+    // stage's, so that the waits below and the compiler's own agree)
     load_x(st0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int st = st0; st < st1; st += 2) {
-        const int n1 = st + 1 < st1 ? st + 1 : st;
-        stage(st, n1, 0, wA, zA, sA, wB, zB, sB);
-        if (st + 1 < st1) {
-            const int n2 = st + 2 < st1 ? st + 2 : st + 1;
-            stage(st + 1, n2, 1, wB, zB, sB, wA, zA, sA);
-        }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(st0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (WPF == 2) {
+        load_w(st0 + 1 < st1 ? st0 + 1 : last, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((WLOADS & 15) | ((WLOADS >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
     }
+    __syncthreads();
+    // whole rounds of NSET stages, then the rest (so that every path back
+    // to the loop head has the same loads in flight)
+    int st = st0;
+    for (; st + NSET <= st1; st += NSET) {
+#pragma unroll
+        for (int j = 0; j < NSET; ++j) stage(st + j, j);
+    }
+    if (st < st1) stage(st, 0);
+    if (NSET > 2 && st + 1 < st1) stage(st + 1, 1);
+    // the last stage's own reload may still be in flight
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
     // (token-major output: the four consecutive rows e = 4 j .. 4 j + 3 of a
@@ -388,17 +432,24 @@ __global__ void __launch_bounds__(256, 1) tiled_kernel(GemmArgs a, int splitk) {
     }
 }
 
-template <int BM, int BN, int WGM = 4>
+template <int BM, int BN, int WGM = 4, int NWV = 4>
 hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles, (unsigned)t.splitk);
-    hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM>), grid, dim3(256), 0, stream, a, t.splitk);
+    if (t.wpf == 2)
+        hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, 2>), grid, dim3(64 * NWV), 0, stream, a, t.splitk);
+    else
+        hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, 1>), grid, dim3(64 * NWV), 0, stream, a, t.splitk);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool tiled_supported(const TiledShape& t) {
+    if (t.wpf != 1 && t.wpf != 2) return false;
+    // a third weight register set spills with the 2 x 2 wave grid
+    if (t.wpf == 2 && t.wm == 2) return false;
+    if (t.wm == 8) return t.bm == 512 && t.bn == 128 && t.splitk >= 1;
     const bool bm_ok = t.bm == 128 || t.bm == 256;
     const bool bn_ok = t.bn == 64 || t.bn == 128 || t.bn == 256;
     const bool wm_ok = t.wm == 4 || (t.wm == 2 && t.bn >= 128);
@@ -406,9 +457,9 @@ bool tiled_supported(const TiledShape& t) {
 }
 
 const char* tiled_check(const GemmArgs& a, const TiledShape& t) {
-    (void)t;
-    // 32-bit buffer offsets: a 256-row weight tile and a 16-row chunk slab
-    if (a.K > ((int64_t)1 << 24)) return "K above 2^24";
+    // 32-bit buffer offsets and record counts: a tile's weight rows and a
+    // 16-row chunk slab
+    if ((int64_t)t.bm * (a.K / 2) > 0x7FFFFFFF) return "bm * K / 2 above 2^31 - 1 bytes";
     if (a.N > ((int64_t)1 << 23)) return "N above 2^23";
     return nullptr;
 }
@@ -450,6 +501,10 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
     hipError_t e = launch_xpack(a, stream);
     if (e != hipSuccess) return e;
+    if (t.wm == 8) {
+        if (t.bm == 512 && t.bn == 128) return launch_bmbn<512, 128, 8, 8>(a, t, stream);
+        return hipErrorInvalidValue;
+    }
     if (t.wm == 2) {
         if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256, 2>(a, t, stream);
         if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128, 2>(a, t, stream);

@@ -123,10 +123,14 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            tile along K (>= 1).  A wave takes at most 16 groups (8 for
  *            N > 4, 4 for N = 16, 2 for N = 32); plans beyond that, or whose
  *            staged activations exceed 160 KB of LDS, are rejected.
- *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256});
+ *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256},
+ *            or bm = 512 with bn = 128 and wm = 8);
  *            wm = waves along rows: 4 (each wave owns bm/4 rows and all
- *            bn columns) or 2 (2 x 2 waves, bn >= 128); 0 means 4;
- *            splitk as above; K <= 2^24 and N <= 2^23.
+ *            bn columns), 2 (2 x 2 waves, bn >= 128) or 8 (eight waves of
+ *            64 rows, bm = 512); 0 means 4;
+ *            pf = stages (groups of 128 k) of weights a wave loads ahead:
+ *            0 or 1 (one) or 2 (two; not with wm = 2);
+ *            splitk as above; bm * K / 2 < 2^31 and N <= 2^23.
  *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
  *            weights in flight per wave (8 or 16); rb = 16-row blocks per
  *            wave (1 or 2: 64 or 128 rows per workgroup, 0 means 2); wk =

@@ -110,6 +110,14 @@ def test_plan_checks(lib):
     assert gp(kernel=2, bm=128, bn=64, splitk=9) == UNSUPPORTED             # > 8 groups
     assert gp(kernel=2, bm=128, bn=64, splitk=1, wm=2) == UNSUPPORTED       # 2 x 2 needs bn >= 128
     assert gp(kernel=2, bm=128, bn=128, splitk=1, wm=3) == UNSUPPORTED
+    assert gp(kernel=2, bm=512, bn=128, splitk=1, wm=8) == WORKSPACE        # valid eight-wave plan
+    assert gp(kernel=2, bm=512, bn=128, splitk=1, wm=8, pf=2) == WORKSPACE
+    assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=2) == WORKSPACE
+    assert gp(kernel=2, bm=512, bn=128, splitk=1, wm=4) == UNSUPPORTED      # 512 rows need eight waves
+    assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=8) == UNSUPPORTED      # eight waves need 512 rows
+    assert gp(kernel=2, bm=512, bn=64, splitk=1, wm=8) == UNSUPPORTED
+    assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=2, pf=2) == UNSUPPORTED  # 2 x 2 with a third set
+    assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=3) == UNSUPPORTED
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2) == WORKSPACE        # valid narrow plan
     assert gp(kernel=3, ncol=8, pf=8, splitk=1, rb=2) == UNSUPPORTED       # 16, 32 or 64 columns
     assert gp(kernel=3, ncol=16, pf=4, splitk=1, rb=2) == UNSUPPORTED      # ring of 8 or 16
@@ -173,9 +181,14 @@ def test_kernel_name_follows_the_plan(lib):
     # eight waves along K, four groups each: four weight groups in flight per wave
     assert B.kernel_name(12288, 1, 4096) == "skinny_kernel<1, 4>"
     assert B.kernel_name(4096, 1, 11008) == "skinny_kernel<1, 8>"
-    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<256, 128, 4>"
+    # 512-row tiles where they load the 256 CUs as evenly as 256-row tiles
+    # (768 = 3 x 256 tiles at N = 4096, 192 at N = 1024), not at N = 2048
+    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<512, 128, 8, 8, 2>"
+    assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2>"
+    assert B.kernel_name(12288, 2048, 4096) == "tiled_kernel<256, 128, 4, 4, 1>"
+    assert B.kernel_name(12288, 512, 4096) == "tiled_kernel<128, 128, 4, 4, 1>"
     p = B.Plan.make(kernel=2, bm=128, bn=256, splitk=1, wm=2)
-    assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2>"
+    assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2, 4, 1>"
     buf = ctypes.create_string_buffer(8)
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128

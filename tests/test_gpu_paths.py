@@ -103,6 +103,41 @@ def test_tiled_plan(case):
     assert_parity(C, C_ref, A_ref, str(case))
 
 
+TILED_DEEP = [
+    # (M, K, N, bm, bn, splitk, wm, pf): eight-wave 512-row tiles and weights
+    # two stages ahead; group counts that leave 0, 1 or 2 stages after the
+    # last whole round of three (1, 2, 3, 4, 5, 9 and 86 groups), splits of
+    # uneven length, ragged M and N
+    (1, 128, 1, 512, 128, 1, 8, 2),
+    (129, 256, 77, 128, 128, 1, 4, 2),
+    (513, 384, 130, 512, 128, 1, 8, 2),
+    (300, 512, 100, 256, 128, 1, 4, 2),
+    (1030, 640, 257, 512, 128, 1, 8, 0),
+    (1030, 640, 257, 512, 128, 1, 8, 2),
+    (700, 1152, 200, 512, 128, 2, 8, 2),
+    (700, 1152, 200, 512, 128, 4, 8, 2),
+    (257, 1152, 264, 128, 64, 3, 4, 2),
+    (520, 896, 520, 256, 256, 1, 4, 2),
+    (64, 11008, 65, 512, 128, 1, 8, 2),
+]
+
+
+@pytest.mark.parametrize("case", TILED_DEEP, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d_wm%d_pf%d" % c)
+def test_tiled_deep_plan(case):
+    M, K, N, bm, bn, splitk, wm, pf = case
+    log("tiled deep %s" % (case,))
+    p = prob(M, K)
+    X = X_for(K, N)
+    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk, wm=wm, pf=pf)
+    C = run(p, X, plan=plan)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, str(case))
+    # how far ahead the weights are loaded and how many rows a tile has
+    # change no arithmetic: the same as 128-row tiles of four waves
+    base = B.Plan.make(kernel=B.KERNEL_TILED, bm=128, bn=bn if bn != 256 else 128, splitk=splitk, wm=4)
+    assert np.array_equal(C, run(p, X, plan=base)), case
+
+
 NARROW = [
     # (M, K, N, ncol, pf, splitk, rb, wk): 64- or 128-row tiles with ragged
     # tails, every column width, columns past N, fewer groups than the ring,

@@ -69,6 +69,9 @@ PLANS = [
     (129, 384, 130, dict(kernel=2, bm=256, bn=128, splitk=2, wm=4)),   # M % 4 != 0
     (130, 384, 40, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4)),     # M % 4 == 2
     (40, 128, 3, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4)),
+    (520, 640, 520, dict(kernel=2, bm=512, bn=128, splitk=1, wm=8, pf=2)),
+    (129, 384, 130, dict(kernel=2, bm=512, bn=128, splitk=2, wm=8, pf=2)),   # M % 4 != 0
+    (300, 512, 100, dict(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=2)),
 ]
 
 
