@@ -118,6 +118,18 @@ def test_plan_checks(lib):
     assert gp(kernel=2, bm=512, bn=64, splitk=1, wm=8) == UNSUPPORTED
     assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=2, pf=2) == UNSUPPORTED  # 2 x 2 with a third set
     assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=3) == UNSUPPORTED
+
+    # a tile's weight rows must fit 32-bit buffer offsets: bm * K / 2 < 2^31
+    def gk(K, **kw):
+        pl = B.Plan.make(kernel=2, bn=128, splitk=1, **kw)
+        far = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]
+        st = lib.w4a16_gemm_plan(*far, 64, 4, K, 128, ctypes.byref(pl), NULL, 0, NULL)
+        return st, lib.w4a16_last_error()
+    st, msg = gk(1 << 23, bm=512, wm=8)
+    assert st == UNSUPPORTED and b"2^31" in msg
+    assert gk((1 << 23) - 128, bm=512, wm=8)[0] == WORKSPACE
+    assert gk(1 << 24, bm=256, wm=4)[0] == UNSUPPORTED
+    assert gk((1 << 24) - 128, bm=256, wm=4)[0] == WORKSPACE
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2) == WORKSPACE        # valid narrow plan
     assert gp(kernel=3, ncol=8, pf=8, splitk=1, rb=2) == UNSUPPORTED       # 16, 32 or 64 columns
     assert gp(kernel=3, ncol=16, pf=4, splitk=1, rb=2) == UNSUPPORTED      # ring of 8 or 16
