@@ -94,34 +94,49 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     }
 
     // ---- scales and zero words of the tile's rows and groups, staged in LDS
-    // once ([group][row] halves and [word][row] words, so that the 16 rows a
-    // lane group reads are consecutive): one instruction per stage would
-    // otherwise touch 16 cache lines for 2 or 4 bytes each.  Thread t takes
-    // row t % BM and every TPR-th group / word from t / BM on; the loads are
-    // unconditional (clamped) and issued before the weight prefetch, the LDS
-    // stores after it.
-    constexpr int TPR = NT / kNarrowBM;      // threads per row
-    constexpr int SMAX = 16, ZMAX = 3;       // loads per thread (ngmax <= 16 TPR)
+    // once ([group][row] halves and [word][row] words, rows padded by two
+    // halves / one word so that the stores below hit distinct banks, and so
+    // that the 16 rows a lane group reads are consecutive).  Consecutive
+    // threads take consecutive groups (words) of one row, GP (ZP2) slots per
+    // row, GP the power of two >= the groups (words) of the range: one load
+    // instruction reads a few rows' contiguous runs instead of one value
+    // from each of 64 rows.  The loads are issued before the weight
+    // prefetch, the LDS stores after it; slots past the range reload the
+    // row's last value.
+    constexpr int SP = kNarrowBM + 2, ZP = kNarrowBM + 1;   // padded row counts
+    // loads per thread at most: plans keep ngmax <= 16 NT / BM (NT / BM a
+    // power of two), so GP <= 16 NT / BM and BM GP / NT <= 16 scale passes;
+    // a range of ngmax groups spans at most 2 NT / BM + 1 zero words, so
+    // ZP2 <= 4 NT / BM and at most 4 zero passes
+    constexpr int SMAX = 16, ZMAX = 4;
     const int ngmax = (G + splitk - 1) / splitk;
     const int zw0 = g0 >> 3, nzw = ((g1 - 1) >> 3) - zw0 + 1;
     uint16_t* sl = reinterpret_cast<uint16_t*>(xs + (size_t)ngmax * 16 * NCOL * 16);
-    uint32_t* zl = reinterpret_cast<uint32_t*>(sl + (size_t)ngmax * kNarrowBM);
-    const int sr_row = tid % kNarrowBM, sr_g = tid / kNarrowBM;
-    const int sr_rc = sr_row < tile_rows ? sr_row : tile_rows - 1;
+    uint32_t* zl = reinterpret_cast<uint32_t*>(sl + (size_t)ngmax * SP);
+    const int lgp = ng > 1 ? 32 - __builtin_clz((unsigned)(ng - 1)) : 0;     // GP = 1 << lgp >= ng
+    const int lzp = nzw > 1 ? 32 - __builtin_clz((unsigned)(nzw - 1)) : 0;   // ZP2 = 1 << lzp >= nzw
+    const int sg = tid & ((1 << lgp) - 1), sr0 = tid >> lgp, srs = NT >> lgp;
+    const int zg = tid & ((1 << lzp) - 1), zr0 = tid >> lzp, zrs = NT >> lzp;
+    const int spass = (tile_rows + srs - 1) / srs, zpass = (tile_rows + zrs - 1) / zrs;   // uniform
     const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(a.scales + row0 * G, (int64_t)tile_rows * G * 2);
     const __amdgpu_buffer_rsrc_t zres = buffer_rsrc(a.zpk + row0 * a.ZW, (int64_t)tile_rows * a.ZW * 4);
     uint32_t sv[SMAX], zv[ZMAX];
+    {
+        const int gc = sg < ng ? sg : ng - 1, wc = zg < nzw ? zg : nzw - 1;
 #pragma unroll
-    for (int j = 0; j < SMAX; ++j) {
-        int g = sr_g + TPR * j;
-        g = g < ng ? g : ng - 1;
-        sv[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, (sr_rc * G + g0 + g) * 2, 0, 0);
-    }
+        for (int j = 0; j < SMAX; ++j)
+            if (j < spass) {
+                int r = sr0 + srs * j;
+                r = r < tile_rows ? r : tile_rows - 1;
+                sv[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, (r * G + g0 + gc) * 2, 0, 0);
+            }
 #pragma unroll
-    for (int j = 0; j < ZMAX; ++j) {
-        int w = sr_g + TPR * j;
-        w = w < nzw ? w : nzw - 1;
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b32(zres, (sr_rc * a.ZW + zw0 + w) * 4, 0, 0);
+        for (int j = 0; j < ZMAX; ++j)
+            if (j < zpass) {
+                int r = zr0 + zrs * j;
+                r = r < tile_rows ? r : tile_rows - 1;
+                zv[j] = __builtin_amdgcn_raw_buffer_load_b32(zres, (r * a.ZW + zw0 + wc) * 4, 0, 0);
+            }
     }
 
     // ring of PF stages of packed words
@@ -139,14 +154,18 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         load(p, g0 + gw0 + (p < ngw ? p : ngw - 1));
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (sr_row < tile_rows) {
 #pragma unroll
-        for (int j = 0; j < SMAX; ++j)
-            if (sr_g + TPR * j < ng) sl[(sr_g + TPR * j) * kNarrowBM + sr_row] = (uint16_t)sv[j];
+    for (int j = 0; j < SMAX; ++j)
+        if (j < spass) {
+            const int r = sr0 + srs * j;
+            if (sg < ng && r < tile_rows) sl[sg * SP + r] = (uint16_t)sv[j];
+        }
 #pragma unroll
-        for (int j = 0; j < ZMAX; ++j)
-            if (sr_g + TPR * j < nzw) zl[(sr_g + TPR * j) * kNarrowBM + sr_row] = zv[j];
-    }
+    for (int j = 0; j < ZMAX; ++j)
+        if (j < zpass) {
+            const int r = zr0 + zrs * j;
+            if (zg < nzw && r < tile_rows) zl[zg * ZP + r] = zv[j];
+        }
     // the activation copies were issued before the scale, zero and these
     // PF * WLOADS weight loads
     wait_vmcnt<PF * WLOADS>();
@@ -171,8 +190,8 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
             const int r = 16 * (kRB * wave_m + rb) + r16;
-            const uint32_t zw = zl[((g >> 3) - zw0) * kNarrowBM + r];
-            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[gl * kNarrowBM + r]);
+            const uint32_t zw = zl[((g >> 3) - zw0) * ZP + r];
+            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[gl * SP + r]);
         }
         const unsigned char* xg = xl + gl * 16 * NCOL * 16;
 #pragma unroll
@@ -273,7 +292,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     // ---- split-K: the last workgroup of a row tile sums the partials in
     // order (agent-coherent accesses; every store done before the counter
     // moves, so no cache flush is needed)
-    int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * kNarrowBM);
+    int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * ZP);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -347,8 +366,8 @@ size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
     const size_t chunks = (size_t)ngmax * 16 * s.ncol * 16;                        // activation chunks
     const size_t red = (size_t)(s.wk - 1) * 4 * s.rb * (s.ncol / 16) * 64 * 16;   // K-wave sums (reuse)
     return (chunks > red ? chunks : red)
-           + (size_t)ngmax * bm * 2                  // scales
-           + (size_t)((ngmax + 15) / 8) * bm * 4     // zero words (a range of ngmax groups spans at most this many)
+           + (size_t)ngmax * (bm + 2) * 2            // scales ([group][row], rows padded by two halves)
+           + (size_t)((ngmax + 15) / 8) * (bm + 1) * 4   // zero words (a range of ngmax groups spans at most this many)
            + 16;                                     // split-K flag
 }
 
