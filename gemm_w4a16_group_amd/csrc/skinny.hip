@@ -48,8 +48,10 @@ constexpr int kMaxThreads = 1024;
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 // One group pair of one wave's 16 rows (16 x 128 B), rows 8..15 placed one
 // half bank-row later so that both the load-order writes and the MFMA-order
-// reads touch all 64 banks.
-constexpr int kPairBytes = 2304;
+// reads touch all 64 banks: 17 slots of 128 B (row r at slot r + r / 8).
+// Exactly that and no more, since LDS per wave decides how many workgroups
+// a CU holds (eight waves at N = 4 fit three to a CU with it).
+constexpr int kPairBytes = 17 * 128;
 constexpr uint32_t kNormSumBytes = 16 * 8 * 4;   // [waves][8 columns] float sums of squares
 
 // Activation columns the kernel is built for: any N <= 8, or 16 or 32.
