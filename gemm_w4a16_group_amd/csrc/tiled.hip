@@ -12,13 +12,13 @@
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
 // reads them back conflict-free.
 //
-// tiled_kernel: a workgroup of four waves owns a BM x BN tile of C and walks
-// K one group (128 k) per stage.  The waves form a WGM x (4 / WGM) grid.
-// Each wave loads the packed weight words of its rows straight into
-// registers (32 bytes per lane per 32-row block and stage, one stage ahead)
-// and dequantizes them there, one MFMA step ahead, to fp16 (q - z) * s: one
-// fp16 rounding per weight, q - z being exact before the scale is applied.
-// fp32 accumulation throughout.
+// tiled_kernel: a workgroup of NWV waves (four, or eight for 512-row tiles)
+// owns a BM x BN tile of C and walks K one group (128 k) per stage.  The
+// waves form a WGM x (NWV / WGM) grid.  Each wave loads the packed weight
+// words of its rows straight into registers (32 bytes per lane per 32-row
+// block and stage, one or two stages ahead) and dequantizes them there, one
+// MFMA step ahead, to fp16 (q - z) * s: one fp16 rounding per weight, q - z
+// being exact before the scale is applied.  fp32 accumulation throughout.
 #include "device.hpp"
 #include "launch.hpp"
 
