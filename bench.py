@@ -261,7 +261,7 @@ def gemm_secondary(iters, warmup):
                      "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4),
                      "traffic": traffic(kern, M, K, N), "kernel": kern,
                      "flops_per_launch": alg_flops(M, K, N),
-                     "timed": "whole call: xpack_kernel (activation re-layout) + %s" % kern}}
+                     "timed": "whole call: xpack_col_kernel (activation re-layout) + %s" % kern}}
 
 
 def headline(args):

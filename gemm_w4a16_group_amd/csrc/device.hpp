@@ -67,14 +67,6 @@ __device__ __forceinline__ u32x4 permute_k8(u32x4 v) {
     return r;
 }
 
-// Low halves of two words -> (lo(a), lo(b)); high halves -> (hi(a), hi(b)).
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ uint32_t f32_to_h16_bits(float v) {
     _Float16 h = (_Float16)v;   // round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
