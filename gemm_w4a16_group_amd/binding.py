@@ -64,7 +64,12 @@ class DecoderLayer(ctypes.Structure):
 
 
 def load_library(path=None):
-    """Load (once) and return the ctypes handle of libw4a16.so."""
+    """Load (once) and return the ctypes handle of libw4a16.so.
+
+    With no path, the in-tree library is loaded on first use and kept as
+    the handle every function of this module calls.  With a path, the
+    library there is loaded and returned, and the module's handle is left
+    as it was (functions here keep calling the in-tree library)."""
     global _lib
     with _lock:
         if _lib is not None and path is None:
