@@ -23,10 +23,12 @@
 // Scores: 16 fp32 FMAs per lane and a 3-step butterfly over the channel
 // blocks.  Softmax with the wave's maximum; values weighted in fp32; partial
 // sums reduced over key slots (butterfly), then over the four waves in LDS.
-// With several splits, each writes (max, sum, o[D]) with agent-coherent
-// stores and the last one of a head to arrive (an arrival counter in the
-// workspace) merges them in split order, with all of the merge's loads in
-// flight at once.
+// With several splits, each one that holds keys up to p writes (max, sum,
+// o[D]) with agent-coherent stores and the last of them to arrive (an
+// arrival counter in the workspace, compared with the number of such
+// splits) merges them in split order, with all of the merge's loads in
+// flight at once; workgroups past p leave without taking part, so a graph
+// captured for a large max_len pays little for the unused part of it.
 //
 // Angles: theta_i = theta_1^i from theta_1 = base^(-2/D) (double, from the
 // host), p * theta_i in double, reduced modulo 2 pi in double (two-part
@@ -232,7 +234,16 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
         return;
     }
 
-    // ---- 7. several splits: partials, then the last arrival merges them
+    // ---- 7. several splits: only the live ones (keys up to p) take part;
+    // each stores its partials, and the last of them to arrive merges them.
+    // A workgroup past p leaves at once; an invalid position has no live
+    // split, and split 0 writes the sequence's NaN outputs.
+    if (!valid) {
+        if (split == 0 && tid < D) outp[tid] = (uint16_t)f32_to_h16_bits(__builtin_nanf(""));
+        return;
+    }
+    if (!live) return;
+    const int nlive = (int)((int64_t)p / ((int64_t)W * KPW)) + 1;   // splits 0 .. nlive - 1 hold keys <= p
     const int64_t head = (int64_t)b * H + h;
     float* part_base = a.part + (head * splits + split) * (D + 2);
     if (tid < D) __hip_atomic_store(part_base + tid, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -242,7 +253,7 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == (unsigned)(splits - 1);
+        const int last = prev == (unsigned)(nlive - 1);
         if (last) __hip_atomic_store(a.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_flag = last;
     }
@@ -252,29 +263,29 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     // The merge issues all of its loads before it uses any: every split's
     // maximum and sum (into LDS), and this thread's first eight value
     // partials (thread = (channel tid % 128, class tid / 128), class c takes
-    // splits c, c + NC, ...).  Every thread then forms the weights and the
-    // total sum over all splits in split order, so the result is the same
-    // whichever workgroup merges.
+    // splits c, c + NC, ... of the live ones).  Every thread then forms the
+    // weights and the total sum over the live splits in split order, so the
+    // result is the same whichever workgroup merges.
     constexpr int NC = NT / D;
     __shared__ float sms[kAttnMaxSplits], sls[kAttnMaxSplits];
     __shared__ float oh[NC][D];
-    const float* pb = a.part + head * splits * (D + 2);
+    const float* pb = a.part + head * splits * (D + 2);   // the head's partials (stride: every split)
     const int ch = tid & (D - 1), cls = tid / D;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int s = cls + NC * i < splits ? cls + NC * i : 0;
+        const int s = cls + NC * i < nlive ? cls + NC * i : 0;
         v[i] = __hip_atomic_load(pb + s * (D + 2) + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    for (int s = tid; s < splits; s += NT) {
+    for (int s = tid; s < nlive; s += NT) {
         sms[s] = __hip_atomic_load(pb + s * (D + 2) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sls[s] = __hip_atomic_load(pb + s * (D + 2) + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, sms[s]);
+    for (int s = 0; s < nlive; ++s) mx = fmaxf(mx, sms[s]);
     float ls = 0.f;
-    for (int s = 0; s < splits; ++s) {
+    for (int s = 0; s < nlive; ++s) {
         const float ms = sms[s];
         ls = fmaf(ms == -INFINITY ? 0.f : __expf(ms - mx), sls[s], ls);
     }
@@ -285,16 +296,16 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        if (cls + NC * i < splits) acc = fmaf(weight(cls + NC * i), v[i], acc);
-    for (int s0 = cls + 8 * NC; s0 < splits; s0 += 8 * NC) {
+        if (cls + NC * i < nlive) acc = fmaf(weight(cls + NC * i), v[i], acc);
+    for (int s0 = cls + 8 * NC; s0 < nlive; s0 += 8 * NC) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int s = s0 + NC * i < splits ? s0 + NC * i : 0;
+            const int s = s0 + NC * i < nlive ? s0 + NC * i : 0;
             v[i] = __hip_atomic_load(pb + s * (D + 2) + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (s0 + NC * i < splits) acc = fmaf(weight(s0 + NC * i), v[i], acc);
+            if (s0 + NC * i < nlive) acc = fmaf(weight(s0 + NC * i), v[i], acc);
     }
     oh[cls][ch] = acc;
     __syncthreads();
