@@ -323,7 +323,11 @@ tiled_kernel(GemmArgs a, int splitk) {
 
     // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
     // (token-major output: the four consecutive rows e = 4 j .. 4 j + 3 of a
-    // column are one 8-byte store)
+    // column are one 8-byte store).  [M, N] output: each store instruction
+    // writes two 64-byte row runs, which non-temporal stores handle well
+    // (1.3 % faster at N = 4096); the token-major stores are 8 bytes each,
+    // M apart between lanes, and need the L2 to merge them (non-temporal
+    // ones made that path 36 % slower), so they stay ordinary.
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -351,7 +355,7 @@ tiled_kernel(GemmArgs a, int splitk) {
                         const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
                         if (row < M) {
                             if (splitk == 1)
-                                a.c[row * N + col] = (uint16_t)f32_to_h16_bits(acc[rb][cb][e]);
+                                __builtin_nontemporal_store((uint16_t)f32_to_h16_bits(acc[rb][cb][e]), &a.c[row * N + col]);
                             else
                                 __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col, acc[rb][cb][e],
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
