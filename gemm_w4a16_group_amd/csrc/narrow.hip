@@ -25,6 +25,9 @@ namespace w4a16 {
 namespace {
 
 constexpr int kNarrowMaxLds = 160 * 1024;
+// cache-policy operand of the weight loads: non-temporal (each weight byte
+// is read once; 4-5 % faster at N = 8 and 16 than the default policy)
+constexpr int kNonTemporal = 2;
 
 // Wait until at most n vector-memory operations are outstanding.  Inline
 // assembly with a memory clobber, so that the compiler keeps every load
@@ -144,7 +147,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     auto load = [&](int slot, int g) {
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
-            wr[slot][rb] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, 0);
+            wr[slot][rb] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rb], g * 64, kNonTemporal);
     };
     // groups past the range reload the last one (no branch around loads),
     // slot by slot in the order the loop refills them, so that the wait
