@@ -820,7 +820,8 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     if (p.kernel == W4A16_KERNEL_SKINNY)
         snprintf(buf, len, "skinny_kernel<%d, %d>", p.ncol, skinny_pf(a, skinny_of(p)));
     else if (p.kernel == W4A16_KERNEL_NARROW)
-        snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d>", p.ncol / 16, p.pf, narrow_of(p).rb, narrow_of(p).wk);
+        snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d, %s>", p.ncol / 16, p.pf, narrow_of(p).rb, narrow_of(p).wk,
+                 narrow_direct_x(a) ? "true" : "false");
     else
     {
         const TiledShape t = tiled_of(p);

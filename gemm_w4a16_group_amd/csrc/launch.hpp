@@ -82,6 +82,9 @@ bool narrow_supported(const NarrowShape& s);
 const char* narrow_check(const GemmArgs& a, const NarrowShape& s);
 int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s);
 size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s);
+// true when the narrow kernel stages the activations straight from x ([K, N],
+// N a multiple of 8), with no re-layout launch before it
+bool narrow_direct_x(const GemmArgs& a);
 hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream);
 
 // X [K, N] -> 16-byte chunks [K/8][N] in a.xp (the tiled and narrow kernels' B/A operand layout)

@@ -5,9 +5,13 @@
 //
 // A workgroup of four waves owns BM = 4 x 16 RB rows and a contiguous range
 // of groups along K (splitk workgroups share a row tile).  At the start it
-// copies the activation chunks of its groups (the 16-byte chunks of the
-// tiled path: eight k of one column in dequant order) from L2 straight into
-// LDS, where all four waves read them; it never touches them in HBM again.
+// copies the activations of its groups from L2 straight into LDS, where all
+// four waves read them; it never touches them in HBM again.  [K, N]
+// activations with N a multiple of 8 are copied from X itself, eight k rows
+// per octet stored in dequant order and read back with the transposing LDS
+// read (ds_read_b64_tr_b16), which hands each lane one column's k; any
+// other layout or N goes through the re-layout launch first (16-byte chunks:
+// eight k of one column in dequant order).
 // Each wave streams the packed weights of its 16 RB rows through a ring of
 // PF register stages (one 128-k group per stage, 16 bytes per lane and
 // 16-row block), so PF groups of every wave are in flight while it works;
@@ -25,6 +29,7 @@ namespace w4a16 {
 namespace {
 
 constexpr int kNarrowMaxLds = 160 * 1024;
+typedef short short4v __attribute__((ext_vector_type(4)));
 // cache-policy operand of the weight loads: non-temporal (each weight byte
 // is read once; 4-5 % faster at N = 8 and 16 than the default policy)
 constexpr int kNonTemporal = 2;
@@ -39,7 +44,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
 }
 
-template <int NC, int PF, int kRB, int WK>
+template <int NC, int PF, int kRB, int WK, bool DX>
 __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk) {
     constexpr int NCOL = 16 * NC;       // staged columns (N padded to 16 NC)
     constexpr int kNarrowBM = 64 * kRB; // rows per workgroup (16 kRB per wave)
@@ -72,7 +77,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     // (o, n) = X chunk (16 g0 + o, n) at (o NCOL + n) * 16.  Wave w issues
     // instructions j = w, w + 4 WK, ...; instruction j fills chunks
     // [64 j, 64 j + 64).  Columns past N re-read column N - 1.
-    {
+    if constexpr (!DX) {
         const i32x4 xres = raw_rsrc(a.xp + (int64_t)g0 * 16 * N * 8, (int64_t)ng * 16 * N * 16);
         const int nins = ng * 16 * NCOL / 64;
         for (int j = wave; j < nins; j += 4 * WK) {
@@ -80,6 +85,23 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
             const int o = c / NCOL, n = c % NCOL;
             const int64_t nn = n < N ? n : N - 1;
             buffer_load_lds16(xres, xs + 64 * j * 16, (int)((o * N + nn) * 16), 0);
+        }
+    } else {
+        // X read in place ([K, N] rows, N a multiple of 8): octet o of the
+        // range holds its eight k rows of NCOL halves in dequant order
+        // (k offsets 0, 4, 1, 5, 2, 6, 3, 7), so that two transposing reads
+        // of four rows each give a lane one column's eight k in the order
+        // the weight words unpack to.  Chunks past N re-read the row's last.
+        const i32x4 xres = raw_rsrc(a.x + (int64_t)g0 * 128 * N, (int64_t)ng * 128 * N * 2);
+        const int nins = ng * 16 * NCOL / 64;
+        const int n8 = (int)(N >> 3);
+        for (int j = wave; j < nins; j += 4 * WK) {
+            const int c = 64 * j + lane;
+            const int o = c / NCOL, w = c % NCOL;
+            const int p = w / (NCOL / 8), cc = w % (NCOL / 8);
+            const int r = (p >> 1) + 4 * (p & 1);
+            const int ccl = cc < n8 ? cc : n8 - 1;
+            buffer_load_lds16(xres, xs + 64 * j * 16, (int)(((8 * o + r) * N + 8 * ccl) * 2), 0);
         }
     }
 
@@ -185,7 +207,8 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
 
     // activation fragment of MFMA step t, block cb, local group s: chunk
     // (16 s + 4 kq + t, 16 cb + r16)
-    const unsigned char* xl = xs + ((4 * kq) * NCOL + r16) * 16;
+    const unsigned char* xl = DX ? xs + (4 * kq) * NCOL * 16 + (r16 >> 2) * NCOL * 2 + (r16 & 3) * 8
+                                 : xs + ((4 * kq) * NCOL + r16) * 16;
 
     // stage s of this wave: group g0 + gw0 + s, local index gw0 + s
     auto stage = [&](int p, int s) {
@@ -201,7 +224,21 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         for (int t = 0; t < 4; ++t) {
             half8 xf[NC];
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) xf[cb] = *reinterpret_cast<const half8*>(xg + (t * NCOL + 16 * cb) * 16);
+            for (int cb = 0; cb < NC; ++cb) {
+                if constexpr (DX) {
+                    // lanes 4 j .. 4 j + 3 of a 16-lane group read row 4 h + j of
+                    // the octet (columns 16 cb + 4 (lane % 4) ..); the transpose
+                    // hands lane i column 16 cb + i of the four rows
+                    const unsigned char* b = xg + t * NCOL * 16 + cb * 32;
+                    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) short4v*)(b));
+                    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) short4v*)(b + 4 * NCOL * 2));
+                    xf[cb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                } else {
+                    xf[cb] = *reinterpret_cast<const half8*>(xg + (t * NCOL + 16 * cb) * 16);
+                }
+            }
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb) {
                 const half8 wf = dq[rb](wr[p][rb][t]);
@@ -319,7 +356,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     }
 }
 
-template <int NC, int PF, int RB, int WK>
+template <int NC, int PF, int RB, int WK, bool DX>
 hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     dim3 grid((unsigned)((a.M + 64 * RB - 1) / (64 * RB)), (unsigned)s.splitk);
     const size_t lds = narrow_lds_bytes(a, s);
@@ -327,21 +364,22 @@ hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream
     // here (and cleared from the runtime's last error) and reported only to
     // a launch that needs more than the default 64 KB
     static const hipError_t lds_ok = [] {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB, WK>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB, WK, DX>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kNarrowMaxLds);
         if (e != hipSuccess) (void)hipGetLastError();
         return e;
     }();
     if (lds_ok != hipSuccess && lds > 65536) return lds_ok;
-    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB, WK>), grid, dim3(256 * WK), lds, stream, a, s.splitk);
+    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB, WK, DX>), grid, dim3(256 * WK), lds, stream, a, s.splitk);
     return hipGetLastError();
 }
 
 template <int NC, int RB, int WK>
 hipError_t launch_pf(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    const bool dx = narrow_direct_x(a);
     switch (s.pf) {
-        case 8: return launch_nc<NC, 8, RB, WK>(a, s, stream);
-        case 16: return launch_nc<NC, 16, RB, WK>(a, s, stream);
+        case 8: return dx ? launch_nc<NC, 8, RB, WK, true>(a, s, stream) : launch_nc<NC, 8, RB, WK, false>(a, s, stream);
+        case 16: return dx ? launch_nc<NC, 16, RB, WK, true>(a, s, stream) : launch_nc<NC, 16, RB, WK, false>(a, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -374,6 +412,8 @@ size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
            + 16;                                     // split-K flag
 }
 
+bool narrow_direct_x(const GemmArgs& a) { return !a.tm && !a.xp_ready && !a.act && a.N % 8 == 0; }
+
 bool narrow_supported(const NarrowShape& s) {
     return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 8 || s.pf == 16) &&
            (s.rb == 1 || s.rb == 2) && (s.wk == 1 || s.wk == 2 || s.wk == 4) && s.splitk >= 1;
@@ -396,8 +436,10 @@ const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
 int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s) { return (a.M + 64 * s.rb - 1) / (64 * s.rb); }
 
 hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
-    hipError_t e = launch_xpack(a, stream);
-    if (e != hipSuccess) return e;
+    if (!narrow_direct_x(a)) {
+        const hipError_t e = launch_xpack(a, stream);
+        if (e != hipSuccess) return e;
+    }
     switch (s.ncol) {
         case 16: return launch_rb<1>(a, s, stream);
         case 32: return launch_rb<2>(a, s, stream);

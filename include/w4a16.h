@@ -162,9 +162,12 @@ int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
                        w4a16_plan *plan);
 
 /* Name of the main kernel a plan (NULL: the default plan) launches for this
- * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 8>",
- * "narrow_kernel<1, 8>" or "tiled_kernel<256, 128, 4>" (tiled and narrow
- * plans also launch xpack_kernel first).  Writes at most len bytes including the terminating 0 into buf.
+ * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 4>",
+ * "narrow_kernel<1, 8, 1, 1, true>" or "tiled_kernel<512, 128, 8, 8, 2>"
+ * (tiled plans also launch xpack_col_kernel first, and so do narrow plans
+ * whose name ends in "false": N not a multiple of 8; narrow plans ending in
+ * "true" read x in place).  Writes at most len bytes including the
+ * terminating 0 into buf.
  * Returns a status; launches nothing. */
 int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size,
                       const w4a16_plan *plan, char *buf, size_t len);

@@ -201,6 +201,12 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 512, 4096) == "tiled_kernel<128, 128, 4, 4, 1>"
     p = B.Plan.make(kernel=2, bm=128, bn=256, splitk=1, wm=2)
     assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2, 4, 1>"
+    # narrow plans read [K, N] activations in place when N is a multiple of 8
+    # (last template argument true) and re-laid by xpack_col_kernel otherwise
+    assert B.kernel_name(12288, 16, 4096) == "narrow_kernel<1, 8, 1, 1, true>"
+    assert B.kernel_name(12288, 8, 4096) == "narrow_kernel<1, 8, 1, 1, true>"
+    assert B.kernel_name(12288, 12, 4096) == "narrow_kernel<1, 8, 1, 1, false>"
+    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 8, 1, 1, true>"
     buf = ctypes.create_string_buffer(8)
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
