@@ -206,7 +206,9 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 16, 4096) == "narrow_kernel<1, 8, 1, 1, true>"
     assert B.kernel_name(12288, 8, 4096) == "narrow_kernel<1, 8, 1, 1, true>"
     assert B.kernel_name(12288, 12, 4096) == "narrow_kernel<1, 8, 1, 1, false>"
-    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 8, 1, 1, true>"
+    # 32 staged columns: two waves along K per row block
+    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 8, 1, 2, true>"
+    assert B.kernel_name(4096, 24, 11008) == "narrow_kernel<2, 8, 1, 2, true>"
     buf = ctypes.create_string_buffer(8)
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
