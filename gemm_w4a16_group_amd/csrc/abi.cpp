@@ -125,17 +125,22 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
     const GemmArgs a = make_args(M, N, K, layout);
-    // narrow kernel for 8 <= N <= 32: 64 rows per workgroup, a ring of 8
-    // groups per wave, the smallest split whose activations fit in LDS; with
-    // 32 staged columns two waves along K per row block (measured at N = 32:
-    // 12288x4096 25.5 -> 23.7 us, 4096x4096 16.8 -> 13.9 us, 11008x4096
-    // 29.1 -> 26.2 us, 4096x11008 33.7 -> 28.3 us), else one
-    if (N >= 8 && N <= 32) {
+    // narrow kernel for 8 <= N <= 32 (N = 8 on a small [K, N] matrix goes to
+    // the skinny kernel: 4096x4096 7.9 against 10.8 us): 64 rows per
+    // workgroup (128 with 16 columns when 64-row tiles outnumber the CUs:
+    // 22016x4096 N = 8 / 16 21.2 / 21.4 -> 18.5 / 19.1 us), a ring of 8
+    // groups per wave, the smallest split whose activations fit in LDS; two
+    // waves along K per row block with 32 staged columns or more than 32
+    // groups (N = 32: 12288x4096 25.5 -> 23.7 us, 4096x4096 16.8 -> 13.9 us,
+    // 11008x4096 29.1 -> 26.2 us, 4096x11008 33.7 -> 28.3 us; 4096x11008
+    // N = 8 / 16 14.9 / 17.4 -> 13.0 / 15.4 us), else one
+    const bool small = M * K < ((int64_t)1 << 25);
+    if (N >= 8 && N <= 32 && !(N == 8 && !a.tm && small)) {
         p.kernel = W4A16_KERNEL_NARROW;
         p.ncol = N <= 16 ? 16 : 32;
         p.pf = 8;
-        p.rb = 1;
-        for (int wk = p.ncol == 32 ? 2 : 1; wk >= 1; --wk) {
+        p.rb = p.ncol == 16 && (M + 63) / 64 > kCus ? 2 : 1;
+        for (int wk = p.ncol == 32 || G > 32 ? 2 : 1; wk >= 1; --wk) {
             p.wk = wk;
             for (int64_t splitk = 1; splitk <= G; ++splitk) {
                 p.splitk = (int32_t)splitk;
@@ -147,7 +152,6 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         }
         memset(&p, 0, sizeof(p));
     }
-    const bool small = M * K < ((int64_t)1 << 25);
     if (N < 8 || (!a.tm && skinny_columns(N) && small)) {
         p.kernel = W4A16_KERNEL_SKINNY;
         p.ncol = (int32_t)N;

@@ -209,6 +209,11 @@ def test_kernel_name_follows_the_plan(lib):
     # 32 staged columns: two waves along K per row block
     assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 8, 1, 2, true>"
     assert B.kernel_name(4096, 24, 11008) == "narrow_kernel<2, 8, 1, 2, true>"
+    # 128-row workgroups when 64-row tiles outnumber the CUs; two waves along
+    # K beyond 32 groups; the skinny kernel for N = 8 on a small matrix
+    assert B.kernel_name(22016, 16, 4096) == "narrow_kernel<1, 8, 2, 1, true>"
+    assert B.kernel_name(4096, 8, 11008) == "narrow_kernel<1, 8, 1, 2, true>"
+    assert B.kernel_name(4096, 8, 4096) == "skinny_kernel<8, 4>"
     buf = ctypes.create_string_buffer(8)
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
