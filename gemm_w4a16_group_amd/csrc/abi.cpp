@@ -103,7 +103,8 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // is correct, this one only decides speed).
 //
 // Narrow kernel for 8 <= N <= 32 (see below).  Skinny kernel for N < 8,
-// and for N in {16, 32} when the matrix is small and no narrow plan fits
+// for N = 8 on a small [K, N] matrix, and for N in {16, 32} when the
+// matrix is small and no narrow plan fits
 // (below 2^25 weights the tiled kernel has too few tiles to stream the
 // weights fast).  One 16-row block per wave (several waves along M share
 // the staged activations when N grows), about eight groups per wave along K
