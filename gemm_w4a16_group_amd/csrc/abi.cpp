@@ -103,7 +103,7 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // is correct, this one only decides speed).
 //
 // Narrow kernel for 8 <= N <= 32 (see below).  Skinny kernel for N < 8,
-// for N = 8 on a small [K, N] matrix, and for N in {16, 32} when the
+// for N = 8 and 16 on a small [K, N] matrix, and for N = 32 when the
 // matrix is small and no narrow plan fits
 // (below 2^25 weights the tiled kernel has too few tiles to stream the
 // weights fast).  One 16-row block per wave (several waves along M share
@@ -126,8 +126,8 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     memset(&p, 0, sizeof(p));
     const int64_t G = groups_of(K);
     const GemmArgs a = make_args(M, N, K, layout);
-    // narrow kernel for 8 <= N <= 32 (N = 8 on a small [K, N] matrix goes to
-    // the skinny kernel: 4096x4096 7.9 against 10.8 us): 64 rows per
+    // narrow kernel for 8 <= N <= 32 (N = 8 and 16 on a small [K, N] matrix
+    // go to the skinny kernel: 4096x4096 8.1 / 8.7 against 10.8 / 11.0 us): 64 rows per
     // workgroup (128 with 16 columns when 64-row tiles outnumber the CUs:
     // 22016x4096 N = 8 / 16 21.2 / 21.4 -> 18.5 / 19.1 us), a ring of 8
     // groups per wave, the smallest split whose activations fit in LDS; two
@@ -136,7 +136,8 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     // 11008x4096 29.1 -> 26.2 us, 4096x11008 33.7 -> 28.3 us; 4096x11008
     // N = 8 / 16 14.9 / 17.4 -> 13.0 / 15.4 us), else one
     const bool small = M * K < ((int64_t)1 << 25);
-    if (N >= 8 && N <= 32 && !(N == 8 && !a.tm && small)) {
+    const bool small_kn = small && !a.tm && (N == 8 || N == 16);
+    if (N >= 8 && N <= 32 && !small_kn) {
         p.kernel = W4A16_KERNEL_NARROW;
         p.ncol = N <= 16 ? 16 : 32;
         p.pf = 8;
@@ -157,7 +158,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         p.kernel = W4A16_KERNEL_SKINNY;
         p.ncol = (int32_t)N;
         p.rb = 1;
-        p.wm = N <= 8 ? 1 : 4;
+        p.wm = N <= 8 || small_kn ? 1 : 4;
         const int64_t rows = 16LL * p.rb * p.wm;
         const int64_t tiles = (M + rows - 1) / rows;
         for (int64_t splitk = 1; splitk <= G; ++splitk) {

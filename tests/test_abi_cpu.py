@@ -72,7 +72,8 @@ def test_gemm_pointer_checks(lib):
 
 
 def test_workspace_checks(lib):
-    M, N, K = 4096, 16, 4096
+    # a narrow plan: it needs a workspace
+    M, N, K = 12288, 16, 4096
     need = lib.w4a16_gemm_workspace_size(M, N, K, 128)
     assert need > 0
     big = 0x10000000
@@ -214,6 +215,7 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(22016, 16, 4096) == "narrow_kernel<1, 8, 2, 1, true>"
     assert B.kernel_name(4096, 8, 11008) == "narrow_kernel<1, 8, 1, 2, true>"
     assert B.kernel_name(4096, 8, 4096) == "skinny_kernel<8, 4>"
+    assert B.kernel_name(4096, 16, 4096) == "skinny_kernel<16, 4>"
     buf = ctypes.create_string_buffer(8)
     assert lib.w4a16_kernel_name(64, 1, 1024, 128, None, None, 8) == INVALID
     assert lib.w4a16_kernel_name(64, 1, 1000, 128, None, buf, 8) == INVALID      # K % 128
