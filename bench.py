@@ -6,9 +6,11 @@ Default workload (the headline): the decode GEMV C[12288] = Wdeq[12288, 4096]
 one call of the layer on one batch (here one activation column), reading
 the whole packed matrix once.  The weights are replicated into R device
 copies (R * 26 MB > 1 GB, four times the 256 MB last-level cache) and the
-steps cycle through them, so every call streams its weights from HBM.  The
-R calls are captured once in a HIP graph and replayed; HIP events on the
-launch stream bracket the timed steps.
+steps cycle through them, so every call streams its weights from HBM.
+Exactly --steps calls are timed: they are captured in one HIP graph, HIP
+events on the launch stream bracket its replay, and a graph of --warmup
+untimed calls runs right before it, after --clock-warmup seconds of
+untimed calls that bring the clocks up.
 
 Printed (one JSON line): GB/s of algorithmic bytes (packed weights, scales,
 zeros, x and C, each counted once) per call, the roofline fraction against
@@ -17,6 +19,8 @@ fp16 dense peak) as a second measurement, and the CPU oracle timed on a
 bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --trace-summary DIR --kernel NAME --last K   (no GPU: the
+      last K dispatches of a kernel in a rocprofv3 kernel trace)
 """
 
 import argparse
@@ -34,8 +38,8 @@ FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 GROUP = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC = os.path.join(ROOT, "gemm_w4a16_group_amd", "csrc")
-KERNEL_SOURCES = {"skinny_kernel": ("device.hpp", "launch.hpp", "skinny.hip"),
-                  "tiled_kernel": ("device.hpp", "launch.hpp", "tiled.hip")}
+KERNEL_SOURCES = {"skinny_kernel": ("device.hpp", "skinny.hip"),
+                  "tiled_kernel": ("device.hpp", "tiled.hip")}
 
 
 def alg_bytes(M, K, N):
@@ -49,12 +53,17 @@ def alg_flops(M, K, N):
 
 
 def sources_sha(kernel):
-    """sha256 over the code of the source files a kernel is built from
-    (comments and blank lines left out, so that editing a comment does not
-    retire the stored counters)."""
+    """sha256 over the code a kernel is built from: its source file, the
+    device helpers and the kernels' argument struct (comments and blank lines
+    left out, so that editing a comment does not retire the stored
+    counters)."""
     import hashlib
     import re
     h = hashlib.sha256()
+    # the kernels' argument struct, from the launcher declarations
+    with open(os.path.join(CSRC, "launch.hpp")) as fh:
+        m = re.search(r"struct GemmArgs \{.*?\n\};", fh.read(), flags=re.S)
+    h.update(re.sub(r"//[^\n]*", "", m.group(0)).encode())
     for f in KERNEL_SOURCES[kernel.split("<")[0]]:
         with open(os.path.join(CSRC, f)) as fh:
             text = fh.read()
@@ -86,15 +95,17 @@ def traffic(kernel, M, K, N):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    # about 0.3 s of untimed calls first: from idle the clocks take a few
-    # milliseconds to ramp up, and the first thousands of calls run slower
-    ap.add_argument("--warmup", type=int, default=40000)
+    ap.add_argument("--steps", type=int, default=2000, help="timed calls (exactly this many)")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed calls right before the timed ones")
+    # from idle the clocks take a few milliseconds to ramp up and the first
+    # thousands of calls run slower: a time-based warm-up always runs first
+    ap.add_argument("--clock-warmup", type=float, default=0.5, help="seconds of untimed calls first (>= 0.3)")
     ap.add_argument("--copies", type=int, default=40, help="weight copies cycled through (cold cache)")
     ap.add_argument("--workload", default="gemv_12288x4096",
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
-                             "quantize_12288x4096", "prologue", "attention", "tune_table", "decode_step"])
+                             "quantize_12288x4096", "prologue", "attention", "tune_table", "decode_step",
+                             "read_floor"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--gemm-warmup", type=int, default=1000, help="untimed N = 4096 calls first (about 0.4 s)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -102,7 +113,13 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--token", action="store_true",
                     help="small_n / large_n: token-major x [N, K] and c [N, M]")
-    return ap.parse_args()
+    ap.add_argument("--trace-summary", metavar="DIR_OR_CSV",
+                    help="summarize a rocprofv3 kernel trace (no GPU): the last --last dispatches of --kernel")
+    ap.add_argument("--kernel", help="with --trace-summary: the kernel's full name as the trace prints it")
+    ap.add_argument("--last", type=int, default=0, help="with --trace-summary: dispatches counted from the end")
+    args = ap.parse_args()
+    args.clock_warmup = max(args.clock_warmup, 0.3)
+    return args
 
 
 class Layer:
@@ -165,9 +182,39 @@ def time_graph(g, replays, stream):
     return start.elapsed_time(end)
 
 
-def gemv_rotation(M, K, wid, copies, steps, warmup, plan=None):
-    """Time `steps` calls cycling over `copies` weight copies.  Returns
-    (ms per call, plan dict, graph calls per replay)."""
+def timed_calls(calls, steps, warmup, clock_s):
+    """Time exactly ``steps`` calls, call i being calls[i % len(calls)] (one
+    per weight copy, so that every call streams its weights from HBM).
+    Three HIP graphs: one rotation over the copies (replayed for ``clock_s``
+    seconds of clock warm-up), ``warmup`` calls and ``steps`` calls.  The
+    warm-up graph is enqueued right before the timed one, so that the timed
+    calls start without a launch gap; HIP events on the launch stream
+    bracket the timed graph.  Returns (ms per call, seconds of clock warm-up)."""
+    import torch
+    stream = torch.cuda.Stream()
+    rot = capture(calls, stream)
+    timed = capture([calls[i % len(calls)] for i in range(steps)], stream)
+    warm = capture([calls[(steps + i) % len(calls)] for i in range(warmup)], stream) if warmup > 0 else rot
+    t0 = time.time()
+    warm_graph(rot, stream, clock_s)
+    clock = time.time() - t0
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        warm.replay()
+        start.record(stream)
+        timed.replay()
+        end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, clock
+
+
+def gemv_rotation(M, K, wid, copies, steps, warmup, plan=None, clock_s=0.5):
+    """Time exactly `steps` calls cycling over `copies` weight copies, after
+    `warmup` untimed calls and a clock warm-up.  Returns (ms per call, plan
+    dict, seconds of clock warm-up, the weights, x, the first output)."""
     import torch
     from gemm_w4a16_group_amd import binding as B
     from gemm_w4a16_group_amd import inputs
@@ -176,13 +223,8 @@ def gemv_rotation(M, K, wid, copies, steps, warmup, plan=None):
     outs = [torch.empty((M, 1), dtype=torch.float16, device="cuda") for _ in range(copies)]
     calls = [(lambda c=c, o=o: B.gemm(c[0], c[1], c[2], x, out=o, plan=plan))
              for c, o in zip(lay.copies, outs)]
-    stream = torch.cuda.Stream()
-    g = capture(calls, stream)
-    reps_w = max(1, warmup // copies)
-    reps = max(1, steps // copies)
-    time_graph(g, reps_w, stream)
-    ms = time_graph(g, reps, stream)
-    return ms / (reps * copies), B.plan_default(M, 1, K).as_dict(), reps * copies, lay, x, outs[0]
+    ms, clock = timed_calls(calls, steps, warmup, clock_s)
+    return ms, B.plan_default(M, 1, K).as_dict(), clock, lay, x, outs[0]
 
 
 def gemm_large(M, K, N, wid, iters, warmup=1000):
@@ -269,7 +311,8 @@ def headline(args):
     from gemm_w4a16_group_amd import binding as B
     M, K, N = 12288, 4096, 1
     wid = 3
-    ms, plan, steps, *_ = gemv_rotation(M, K, wid, args.copies, args.steps, args.warmup)
+    ms, plan, clock, *_ = gemv_rotation(M, K, wid, args.copies, args.steps, args.warmup, clock_s=args.clock_warmup)
+    steps = args.steps
     b = alg_bytes(M, K, N)
     gbs = b / (ms * 1e-3) / 1e9
     kern = B.kernel_name(M, N, K)
@@ -288,8 +331,11 @@ def headline(args):
         "data": "synthetic",
         "config": {"workload": "gemv_12288x4096_n1", "M": M, "K": K, "N": N, "group_size": GROUP,
                    "weights": "int4 packed, fp16 scale + 4-bit zero per 128",
-                   "cold_cache_copies": args.copies, "timing": "HIP graph of %d calls, HIP events"
-                   % args.copies, "plan": plan},
+                   "cold_cache_copies": args.copies,
+                   "timing": "HIP graph of exactly %d calls cycling over %d weight copies, HIP events on the "
+                             "launch stream; %d untimed calls right before, after %.2f s of clock warm-up"
+                             % (steps, args.copies, args.warmup, clock),
+                   "clock_warmup_s": round(clock, 3), "plan": plan},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic(kern, M, K, N),
                      "kernel": kern, "bytes_per_launch": b,
@@ -326,6 +372,30 @@ def extra(args):
     rows = []
     if args.workload == "copy_calib":
         copy_calib()
+        return
+    if args.workload == "read_floor":
+        # the streaming-read probe (one launch reads a buffer once, in the
+        # GEMV's launch shape: eight waves per workgroup, 4 KB per wave) over
+        # buffers of each decode linear's algorithmic bytes at N = 1 and two
+        # larger sizes, copies cycled through as in the GEMV (cold cache)
+        sizes = [("12288x4096", alg_bytes(12288, 4096, 1))]
+        sizes += [(name + "_%dx%d" % (M, K), alg_bytes(M, K, 1)) for (name, M, K) in inputs.LLAMA7B_PROJ]
+        sizes += [("100MiB", 100 << 20), ("200MiB", 200 << 20)]
+        for name, nb in sizes:
+            nb = nb // 16 * 16
+            cps = max(4, -(-int(1.1e9) // nb))
+            bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(cps)]
+            sinks = [torch.empty(int(B.lib().w4a16_stream_read_sink_words(nb, 8)), dtype=torch.int32, device="cuda")
+                     for _ in range(cps)]
+            calls = [(lambda b=b, k=k: B.stream_read(b, sink=k, waves=8)) for b, k in zip(bufs, sinks)]
+            ms, clock = timed_calls(calls, args.steps, args.warmup, args.clock_warmup)
+            print(json.dumps({"workload": "read_floor", "size": name, "bytes": nb, "copies": cps,
+                              "steps": args.steps, "us": round(ms * 1e3, 3),
+                              "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "kernel": "stream_read_kernel"}), flush=True)
+            del bufs, sinks, calls
+            torch.cuda.empty_cache()
         return
     if args.workload == "gemm_12288x4096_n4096":
         print(json.dumps(gemm_secondary(args.gemm_iters, args.gemm_warmup)), flush=True)
@@ -514,12 +584,13 @@ def extra(args):
             torch.cuda.empty_cache()
         return
     if args.workload == "gemv_4096x4096":
-        ms, plan, steps, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup)
+        ms, plan, *_ = gemv_rotation(4096, 4096, 1, max(args.copies, 120), args.steps, args.warmup,
+                                     clock_s=args.clock_warmup)
         rows.append(("gemv_4096x4096", 4096, 4096, 1, ms, plan))
     elif args.workload == "decode_linears":
         for proj, (name, M, K) in enumerate(inputs.LLAMA7B_PROJ):
             cps = max(8, int(1.1e9 // alg_bytes(M, K, 1)))
-            ms, plan, *_ = gemv_rotation(M, K, 2, cps, args.steps, args.warmup)
+            ms, plan, *_ = gemv_rotation(M, K, 2, cps, args.steps, args.warmup, clock_s=args.clock_warmup)
             rows.append((name, M, K, 1, ms, plan))
     elif args.workload in ("small_n", "large_n"):
         Ns = [1, 2, 4, 8, 16, 32] if args.workload == "small_n" else [64, 128, 256, 512, 1024, 2048, 4096]
@@ -579,8 +650,39 @@ def extra(args):
                           "plan": plan}), flush=True)
 
 
+def trace_summary(path, kernel, last):
+    """Durations of the last ``last`` dispatches of ``kernel`` in a rocprofv3
+    kernel trace (csv), i.e. the timed calls of a bench run; no GPU."""
+    import csv
+    import glob
+    import statistics
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"),
+                                                                 recursive=True))
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Kernel_Name", "").strip() == kernel:
+                    rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    if last > 0:
+        rows = rows[-last:]
+    if not rows:
+        print(json.dumps({"kernel": kernel, "dispatches": 0}))
+        return
+    d = [(e - b) / 1e3 for b, e in rows]
+    span = (rows[-1][1] - rows[0][0]) / 1e3
+    print(json.dumps({"kernel": kernel, "dispatches": len(d), "median_us": round(statistics.median(d), 3),
+                      "mean_us": round(statistics.fmean(d), 3), "min_us": round(min(d), 3),
+                      "max_us": round(max(d), 3), "span_us_per_dispatch": round(span / len(d), 3),
+                      "files": files}))
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.kernel, args.last)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

@@ -142,6 +142,10 @@ def load_library(path=None):
         lib.w4a16_decode_layer_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
         lib.w4a16_gemm_silu.restype = ctypes.c_int
         lib.w4a16_gemm_silu.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.POINTER(Plan), vp, sz, vp]
+        lib.w4a16_stream_read_sink_words.restype = i64
+        lib.w4a16_stream_read_sink_words.argtypes = [i64, i32]
+        lib.w4a16_stream_read.restype = ctypes.c_int
+        lib.w4a16_stream_read.argtypes = [vp, i64, vp, i32, vp]
         if path is None:
             _lib = lib
         return lib
@@ -538,3 +542,16 @@ def gemm_silu(qpk, s, zpk, gu, out=None, plan=None, workspace=None):
     _check(lib().w4a16_gemm_silu(_p(qpk), _p(s), _p(zpk), _p(gu), _p(out), M, N, K, GROUP,
                                  None if plan is None else ctypes.byref(plan), _p(ws), ws_bytes, _stream()))
     return out
+
+
+def stream_read(buf, sink=None, waves=8):
+    """One launch of the streaming-read probe over the bytes of ``buf`` (a
+    contiguous device tensor); returns the sink (one word per wave)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    words = int(lib().w4a16_stream_read_sink_words(nbytes, waves))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
+    _check(lib().w4a16_stream_read(_p(buf), nbytes, _p(sink), int(waves), _stream()))
+    return sink

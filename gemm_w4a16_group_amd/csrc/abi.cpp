@@ -778,6 +778,27 @@ int w4a16_pack(const uint8_t* q, const uint8_t* z, int64_t M, int64_t K, int32_t
     return ok();
 }
 
+int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves) {
+    if (bytes < 16 || bytes % 16 || waves < 1 || waves > 16 || (waves & (waves - 1))) return 0;
+    const int64_t nw = stream_read_waves(bytes);
+    return (nw + waves - 1) / waves * waves;
+}
+
+int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t waves, void* stream) {
+    if (!buf || !sink) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (bytes < 16 || bytes % 16 || bytes > ((int64_t)1 << 40))
+        return fail(W4A16_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %lld)", (long long)bytes);
+    if (waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
+        return fail(W4A16_ERR_INVALID_ARG, "waves must be 1, 2, 4, 8 or 16 (got %d)", (int)waves);
+    if (!aligned16(buf) || !aligned16(sink)) return fail(W4A16_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+    const int64_t words = w4a16_stream_read_sink_words(bytes, waves);
+    if (overlaps(sink, (size_t)words * 4, buf, (size_t)bytes))
+        return fail(W4A16_ERR_INVALID_ARG, "sink overlaps the buffer");
+    const hipError_t e = launch_stream_read(buf, bytes, sink, waves, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int w4a16_quantize(const void* w, int64_t M, int64_t K, int32_t group_size, uint32_t* q_packed, void* scales,
                    uint32_t* z_packed, void* stream) {
     int st = check_dims(M, 1, K, group_size);

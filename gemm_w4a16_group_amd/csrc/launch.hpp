@@ -113,6 +113,11 @@ hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* act, int64_t N, int64_t
 hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,
                            hipStream_t stream);
 
+// streaming-read probe: waves per workgroup `waves`, 4 KB read per wave, one
+// word stored per wave into sink[stream_read_waves(bytes) rounded up to whole workgroups]
+int64_t stream_read_waves(int64_t bytes);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int waves, hipStream_t stream);
+
 hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,
                             hipStream_t stream);
 

@@ -330,13 +330,13 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     if (splitk == 1) return;
 
     // ---- split-K: the last workgroup of a row tile sums the partials in
-    // order (agent-coherent accesses; every store done before the counter
-    // moves, so no cache flush is needed)
+    // order (agent-scope accesses, ordered by a release before the arrival
+    // and an acquire in the last arriver)
     int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * ZP);
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
         if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -344,6 +344,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     }
     __syncthreads();
     if (!*flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int64_t total = (int64_t)tile_rows * N;
     for (int64_t e = tid; e < total; e += NT) {
         const int64_t row = row0 + e / N;

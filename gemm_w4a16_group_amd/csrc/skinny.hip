@@ -631,14 +631,14 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     if (splitk == 1) return;
 
     // ---- 8. split-K: the last workgroup of a row tile sums the partials in
-    // order.  Partials are written and read with agent-coherent accesses
-    // (they bypass the per-XCD L2), and every store has completed before the
-    // arrival counter moves, so no cache flush is needed.
+    // order.  Partials are written and read with agent-scope accesses; the
+    // arrival counter is the synchronizing atomic (release by every writer,
+    // acquire by the last arriver), so the merge sees every partial.
     int* flag = reinterpret_cast<int*>(smem + P.flag_off);
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
         if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -646,6 +646,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     }
     __syncthreads();
     if (!*flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int64_t tile0 = (int64_t)blockIdx.x * P.rows;
     const int64_t rows_here = (M - tile0) < P.rows ? (M - tile0) : P.rows;
     const int64_t total = rows_here * N;

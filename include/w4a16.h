@@ -421,6 +421,20 @@ int w4a16_gemm_silu(const uint32_t *q_packed, const void *scales,
                     const w4a16_plan *plan, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement aid, not part of the layer: one launch that reads `bytes` of
+ * `buf` once (16-byte non-temporal loads, 4 KB per wave, `waves` waves per
+ * workgroup: 1, 2, 4, 8 or 16) and stores one 32-bit word per wave into
+ * `sink` (w4a16_stream_read_sink_words(bytes, waves) words, caller-owned,
+ * overlapping nothing).  Its time per launch is the attainable rate of a
+ * single read of that size, the floor the memory-bound GEMV is held to
+ * (PerfXLLM §3.3 item 2: the GEMV is memory-bound).  Requires bytes a
+ * positive multiple of 16 and 16-byte aligned pointers.
+ */
+int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves);
+int w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
+                      int32_t waves, void *stream);
+
 /* One W4A16 linear layer's weights, as w4a16_gemm takes them. */
 typedef struct {
     const uint32_t *q_packed;

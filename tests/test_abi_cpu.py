@@ -423,3 +423,18 @@ def test_gemm_silu_checks(lib):
     assert lib.w4a16_gemm_silu(NULL, S, Z, X, C, M, N, K, 128, None, WS, 1 << 20, NULL) == INVALID
     sk = B.Plan.make(kernel=B.KERNEL_SKINNY, ncol=16, rb=1, wm=1, wk=4, splitk=1)
     assert lib.w4a16_gemm_silu(Q, S, Z, X, C, M, 16, 1152, 128, ctypes.byref(sk), WS, 1 << 20, NULL) == UNSUPPORTED
+
+
+def test_stream_read_probe_checks(lib):
+    assert lib.w4a16_stream_read_sink_words(4096, 8) == 8
+    assert lib.w4a16_stream_read_sink_words(26181632, 8) == 6392
+    assert lib.w4a16_stream_read_sink_words(4100, 8) == 0
+    assert lib.w4a16_stream_read_sink_words(4096, 3) == 0
+    assert lib.w4a16_stream_read(NULL, 4096, C, 8, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4096, NULL, 8, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4100, C, 8, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 0, C, 8, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4096, C, 3, NULL) == INVALID
+    assert lib.w4a16_stream_read(ctypes.c_void_p(0x100008), 4096, C, 8, NULL) == MISALIGNED
+    assert lib.w4a16_stream_read(Q, 4096, ctypes.c_void_p(0x100000 + 64), 8, NULL) == INVALID
+    assert b"overlap" in lib.w4a16_last_error()

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 
 
 def sample_rows(M, seed, n_random=96):
-    rows = set([0, 1, 15, 16, 17, 31, 32, 63, 64, 127, 128, 255, 256, M - 1, M - 2, M - 17])
+    # first and last rows of 16-, 32-, 64-, 128-, 256- and 512-row tiles
+    rows = set([0, 1, 15, 16, 17, 31, 32, 63, 64, 127, 128, 255, 256, 383, 384, 511, 512, 513,
+                767, 768, 1023, 1024, 1025, 1535, 1536, M - 1, M - 2, M - 17, M - 256, M - 512, M - 513])
     rng = np.random.default_rng(seed)
     rows.update(int(r) for r in rng.integers(0, M, n_random))
     return np.array(sorted(r for r in rows if 0 <= r < M))
