@@ -249,19 +249,21 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     if (tid < D) __hip_atomic_store(part_base + tid, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == D) __hip_atomic_store(part_base + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == D + 1) __hip_atomic_store(part_base + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // every thread's partial stores are released (agent scope) before the
-    // arrival below; the last arriver acquires them before it reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // stores complete, then one release arrival per workgroup; the last
+    // arriver acquires before the barrier that precedes the merge's loads
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(nlive - 1);
-        if (last) __hip_atomic_store(a.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(a.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         last_flag = last;
     }
     __syncthreads();
     if (!last_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // The merge issues all of its loads before it uses any: every split's
     // maximum and sum (into LDS), and this thread's first eight value

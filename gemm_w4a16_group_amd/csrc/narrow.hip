@@ -330,21 +330,24 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     if (splitk == 1) return;
 
     // ---- split-K: the last workgroup of a row tile sums the partials in
-    // order (agent-scope accesses, ordered by a release before the arrival
-    // and an acquire in the last arriver)
+    // order (agent-scope accesses; stores complete, then one release
+    // arrival per workgroup; the last arriver acquires before the barrier
+    // that precedes the merge's loads)
     int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * ZP);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
-        if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         *flag = last;
     }
     __syncthreads();
     if (!*flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int64_t total = (int64_t)tile_rows * N;
     for (int64_t e = tid; e < total; e += NT) {
         const int64_t row = row0 + e / N;

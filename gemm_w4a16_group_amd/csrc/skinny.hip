@@ -631,22 +631,26 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     if (splitk == 1) return;
 
     // ---- 8. split-K: the last workgroup of a row tile sums the partials in
-    // order.  Partials are written and read with agent-scope accesses; the
-    // arrival counter is the synchronizing atomic (release by every writer,
-    // acquire by the last arriver), so the merge sees every partial.
+    // order.  Partials are written and read with agent-scope accesses.  Every
+    // thread waits for its stores to complete, the workgroup meets, and one
+    // thread arrives on the tile's counter with release semantics; the last
+    // arriver's thread acquires, and the barrier after it orders the merge's
+    // loads after that acquire.
     int* flag = reinterpret_cast<int*>(smem + P.flag_off);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
-        if (last) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         *flag = last;
     }
     __syncthreads();
     if (!*flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int64_t tile0 = (int64_t)blockIdx.x * P.rows;
     const int64_t rows_here = (M - tile0) < P.rows ? (M - tile0) : P.rows;
     const int64_t total = rows_here * N;

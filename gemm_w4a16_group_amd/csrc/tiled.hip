@@ -367,21 +367,25 @@ tiled_kernel(GemmArgs a, int splitk) {
     if (splitk == 1) return;
 
     // ---- split-K: the last workgroup of a tile sums the partials in order.
-    // Partials are written and read with agent-scope accesses; the arrival
-    // counter is the synchronizing atomic (release by every writer, acquire
-    // by the last arriver), so the merge sees every partial.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Partials are written and read with agent-scope accesses.  Every thread
+    // waits for its stores to complete, the workgroup meets, and one thread
+    // arrives on the tile's counter with release semantics; the last
+    // arriver's thread acquires, and the barrier after it orders the merge's
+    // loads after that acquire.
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_ACQ_REL,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
-        if (last) __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         flag = last;
     }
     __syncthreads();
     if (!flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int64_t rows_here = (M - row0) < BM ? (M - row0) : BM;
     const int64_t cols_here = (N - col0) < BN ? (N - col0) : BN;
     const int64_t total = rows_here * cols_here;
