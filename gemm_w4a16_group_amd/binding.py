@@ -146,6 +146,10 @@ def load_library(path=None):
         lib.w4a16_stream_read_sink_words.argtypes = [i64, i32]
         lib.w4a16_stream_read.restype = ctypes.c_int
         lib.w4a16_stream_read.argtypes = [vp, i64, vp, i32, vp]
+        lib.w4a16_gemm_noalloc_max_bytes.restype = sz
+        lib.w4a16_gemm_noalloc_max_bytes.argtypes = []
+        lib.w4a16_gemm_noalloc.restype = ctypes.c_int
+        lib.w4a16_gemm_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
         if path is None:
             _lib = lib
         return lib
@@ -555,3 +559,15 @@ def stream_read(buf, sink=None, waves=8):
         sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
     _check(lib().w4a16_stream_read(_p(buf), nbytes, _p(sink), int(waves), _stream()))
     return sink
+
+
+def gemm_noalloc(qpk, s, zpk, x, out):
+    """w4a16_gemm_noalloc: the default-plan product with the library's own
+    device scratch instead of a workspace.  ``out`` [M, N] is required (the
+    call allocates nothing)."""
+    M, N, K = _dims(qpk, s, zpk, x)
+    _need(out, "out", torch.float16)
+    if out.numel() != M * N:
+        raise ValueError("out must hold M*N=%d values" % (M * N))
+    _check(lib().w4a16_gemm_noalloc(_p(qpk), _p(s), _p(zpk), _p(x), _p(out), M, N, K, GROUP, _stream()))
+    return out

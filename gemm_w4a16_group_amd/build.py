@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libw4a16.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["abi.cpp", "pack.hip", "quant.hip", "norm.hip", "attn.hip", "act.hip", "skinny.hip", "narrow.hip", "tiled.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "quant.hip", "norm.hip", "attn.hip", "act.hip", "skinny.hip", "narrow.hip", "tiled.hip", "probe.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -730,6 +730,18 @@ int run_decode_layer(const w4a16_decoder_layer* ly, int64_t B, int64_t H, int64_
 
 }  // namespace
 
+namespace w4a16 {
+int set_last_error(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+}  // namespace w4a16
+
 extern "C" {
 
 const char* w4a16_status_string(int status) {

@@ -113,6 +113,9 @@ hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* act, int64_t N, int64_t
 hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, uint32_t* zpk, int64_t M, int64_t K,
                            hipStream_t stream);
 
+// records `fmt` as the calling thread's w4a16_last_error() and returns status
+int set_last_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 // streaming-read probe: waves per workgroup `waves`, 4 KB read per wave, one
 // word stored per wave into sink[stream_read_waves(bytes) rounded up to whole workgroups]
 int64_t stream_read_waves(int64_t bytes);

@@ -435,6 +435,28 @@ int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves);
 int w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
                       int32_t waves, void *stream);
 
+/*
+ * w4a16_gemm for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * default plan, kernels and results, bit for bit, with no workspace
+ * argument.  The split-K partial sums, arrival counters and activation
+ * chunks live in a fixed device array inside the library,
+ * w4a16_gemm_noalloc_max_bytes() bytes (16 MiB) on each GPU it runs on,
+ * held until the process ends; the first call on a device looks its address
+ * up and clears its counters with a kernel on `stream`.  No call allocates
+ * or frees memory.  A shape whose default plan needs more scratch than that
+ * (w4a16_gemm_workspace_size above the maximum, e.g. the tiled kernel's
+ * K x N activation chunks beyond 16 MiB) fails with W4A16_ERR_WORKSPACE
+ * and writes nothing.  All calls on one GPU share the array: calls that may
+ * run at the same time on that GPU (unordered streams) race and must not be
+ * issued.  Other arguments, requirements and errors as w4a16_gemm.
+ */
+size_t w4a16_gemm_noalloc_max_bytes(void);
+int w4a16_gemm_noalloc(const uint32_t *q_packed, const void *scales,
+                       const uint32_t *z_packed, const void *x, void *c,
+                       int64_t M, int64_t N, int64_t K, int32_t group_size,
+                       void *stream);
+
 /* One W4A16 linear layer's weights, as w4a16_gemm takes them. */
 typedef struct {
     const uint32_t *q_packed;
