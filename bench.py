@@ -383,27 +383,32 @@ def extra(args):
         copy_calib()
         return
     if args.workload == "read_floor":
-        # the streaming-read probe (one launch reads a buffer once, in the
-        # GEMV's launch shape: eight waves per workgroup, 4 KB per wave) over
+        # the streaming-read probe (one launch reads a buffer once) over
         # buffers of each decode linear's algorithmic bytes at N = 1 and two
-        # larger sizes, copies cycled through as in the GEMV (cold cache)
-        sizes = [("12288x4096", alg_bytes(12288, 4096, 1))]
-        sizes += [(name + "_%dx%d" % (M, K), alg_bytes(M, K, 1)) for (name, M, K) in inputs.LLAMA7B_PROJ]
-        sizes += [("100MiB", 100 << 20), ("200MiB", 200 << 20)]
-        for name, nb in sizes:
+        # larger sizes, copies cycled through as in the GEMV (cold cache): in
+        # the GEMV's launch shape (eight waves per workgroup, 4 KB per wave)
+        # and, at the 12288x4096 size, across launch shapes
+        sizes = [("12288x4096", alg_bytes(12288, 4096, 1), [(w, l) for w in (4, 8, 16) for l in (1, 2, 4, 8, 16)])]
+        sizes += [(name + "_%dx%d" % (M, K), alg_bytes(M, K, 1), [(8, 4)]) for (name, M, K) in inputs.LLAMA7B_PROJ]
+        sizes += [("100MiB", 100 << 20, [(8, 4)]), ("200MiB", 200 << 20, [(8, 4)])]
+        for name, nb, shapes in sizes:
             nb = nb // 16 * 16
             cps = max(4, -(-int(1.1e9) // nb))
             bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(cps)]
-            sinks = [torch.empty(int(B.lib().w4a16_stream_read_sink_words(nb, 8)), dtype=torch.int32, device="cuda")
-                     for _ in range(cps)]
-            calls = [(lambda b=b, k=k: B.stream_read(b, sink=k, waves=8)) for b, k in zip(bufs, sinks)]
-            ms, clock = timed_calls(calls, args.steps, args.warmup, args.clock_warmup)
-            print(json.dumps({"workload": "read_floor", "size": name, "bytes": nb, "copies": cps,
-                              "steps": args.steps, "us": round(ms * 1e3, 3),
-                              "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                              "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                              "kernel": "stream_read_kernel"}), flush=True)
-            del bufs, sinks, calls
+            for waves, loads in shapes:
+                words = int(B.lib().w4a16_stream_read_sink_words(nb, waves, loads))
+                sinks = [torch.empty(words, dtype=torch.int32, device="cuda") for _ in range(cps)]
+                calls = [(lambda b=b, k=k, w=waves, l=loads: B.stream_read(b, sink=k, waves=w, loads=l))
+                         for b, k in zip(bufs, sinks)]
+                ms, clock = timed_calls(calls, args.steps, args.warmup, args.clock_warmup)
+                print(json.dumps({"workload": "read_floor", "size": name, "bytes": nb, "copies": cps,
+                                  "waves_per_workgroup": waves, "kb_per_wave": loads,
+                                  "steps": args.steps, "us": round(ms * 1e3, 3),
+                                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "kernel": "stream_read_kernel<%d>" % loads}), flush=True)
+                del sinks, calls
+            del bufs
             torch.cuda.empty_cache()
         return
     if args.workload == "gemm_12288x4096_n4096":

@@ -40,7 +40,8 @@ class W4A16Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("ncol", ctypes.c_int32), ("rb", ctypes.c_int32),
                 ("wm", ctypes.c_int32), ("wk", ctypes.c_int32), ("bm", ctypes.c_int32),
-                ("bn", ctypes.c_int32), ("splitk", ctypes.c_int32), ("pf", ctypes.c_int32)]
+                ("bn", ctypes.c_int32), ("splitk", ctypes.c_int32), ("pf", ctypes.c_int32),
+                ("xpf", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
@@ -143,9 +144,9 @@ def load_library(path=None):
         lib.w4a16_gemm_silu.restype = ctypes.c_int
         lib.w4a16_gemm_silu.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, ctypes.POINTER(Plan), vp, sz, vp]
         lib.w4a16_stream_read_sink_words.restype = i64
-        lib.w4a16_stream_read_sink_words.argtypes = [i64, i32]
+        lib.w4a16_stream_read_sink_words.argtypes = [i64, i32, i32]
         lib.w4a16_stream_read.restype = ctypes.c_int
-        lib.w4a16_stream_read.argtypes = [vp, i64, vp, i32, vp]
+        lib.w4a16_stream_read.argtypes = [vp, i64, vp, i32, i32, vp]
         lib.w4a16_gemm_noalloc_max_bytes.restype = sz
         lib.w4a16_gemm_noalloc_max_bytes.argtypes = []
         lib.w4a16_gemm_noalloc.restype = ctypes.c_int
@@ -548,16 +549,17 @@ def gemm_silu(qpk, s, zpk, gu, out=None, plan=None, workspace=None):
     return out
 
 
-def stream_read(buf, sink=None, waves=8):
+def stream_read(buf, sink=None, waves=8, loads=4):
     """One launch of the streaming-read probe over the bytes of ``buf`` (a
-    contiguous device tensor); returns the sink (one word per wave)."""
+    contiguous device tensor), ``loads`` KB per wave; returns the sink (one
+    word per wave)."""
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous device tensor")
     nbytes = buf.numel() * buf.element_size()
-    words = int(lib().w4a16_stream_read_sink_words(nbytes, waves))
+    words = int(lib().w4a16_stream_read_sink_words(nbytes, waves, loads))
     if sink is None:
         sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
-    _check(lib().w4a16_stream_read(_p(buf), nbytes, _p(sink), int(waves), _stream()))
+    _check(lib().w4a16_stream_read(_p(buf), nbytes, _p(sink), int(waves), int(loads), _stream()))
     return sink
 
 

@@ -91,7 +91,7 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_LAYOU
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
 TiledShape tiled_of(const w4a16_plan& p) {
-    return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm, p.pf == 0 ? 1 : p.pf};
+    return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm, p.pf == 0 ? 1 : p.pf, p.xpf == 0 ? 1 : p.xpf};
 }
 NarrowShape narrow_of(const w4a16_plan& p) {
     return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb, p.wk == 0 ? 1 : p.wk};
@@ -112,11 +112,12 @@ int check_plan(const GemmArgs& a, const w4a16_plan& p);
 // across workgroups only when the staged activations would not fit in LDS.
 //
 // Tiled kernel otherwise: 256 x 128 tiles from N = 4096 on (from N = 1024
-// when that still gives 256 tiles), 128 x 128 from N = 512, 128 x 64 below,
-// 512 x 128 tiles of eight waves instead of 256 x 128 where they load the
-// CUs as evenly (e.g. N = 1024 and 4096 at M = 12288, not N = 2048); a split along K only when there are too few
+// when that still gives 256 tiles), 128 x 128 from N = 256, 128 x 64 below
+// (weights two stages ahead), 512 x 128 tiles of eight waves instead of
+// 256 x 128 where they load the CUs as evenly (e.g. N = 1024 and 4096 at
+// M = 12288, not N = 2048); a split along K only when there are too few
 // tiles to fill the chip (N <= 32: two-way, four-way under 64 tiles; larger
-// N: two-way for long rows, K >= 8192).
+// N: two-way up to N = 128 and for long rows, K >= 8192).
 //
 // Token-major layout: the same choice, except that the skinny kernel takes
 // token-major activations only up to N = 8 (N = 16 and 32 go to the narrow
@@ -188,7 +189,11 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     p.wm = 4;
     // 256-row tiles from N = 1024 on when they still give 256 tiles
     p.bm = (N >= 4096 || (N >= 1024 && ((M + 255) / 256) * ((N + 127) / 128) >= 256)) ? 256 : 128;
-    p.bn = N >= 512 ? 128 : 64;
+    // 128-column tiles from N = 256 (12288x4096 N = 256: 47.3 -> 43.4 us)
+    p.bn = N >= 256 ? 128 : 64;
+    // 128 x 64 tiles load their weights two stages ahead (12288x4096 N = 64
+    // / 128: 37.2 / 37.1 -> 28.3 / 29.0 us)
+    if (p.bm == 128 && p.bn == 64) p.pf = 2;
     // 512 x 128 tiles of eight waves (weights two stages ahead) from N = 1024
     // when they give a CU no more rows than 256 x 128 tiles do: with one of
     // them per CU against two of the others, the busiest CU then has the
@@ -207,7 +212,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     if (t < 160 && t <= kCounterSlots) {
         if (N <= 32)
             splitk = t < 64 ? 4 : 2;
-        else if (K >= 8192)
+        else if (N <= 128 || K >= 8192)   // 12288x4096 N = 64 (96 tiles): 28.3 -> 22.7 us
             splitk = 2;
     }
     while (splitk > G) splitk /= 2;
@@ -221,9 +226,13 @@ int64_t tiles_of(const GemmArgs& a, const w4a16_plan& p) {
                                            : tiled_tiles(a, tiled_of(p));
 }
 
-// Workspace layout: [counters: 64 KB][fp32 partials: splitk * M * N]
-// [tiled kernel only: activation chunks, K * N fp16, at a 256-byte boundary].
+// Workspace layout: [counters: 64 KB][fp32 partials: splitk * M * N for the
+// skinny kernel, splitk whole tiles per tile (in the register layout of the
+// waves that hold the sums) for the tiled and narrow kernels]
+// [tiled and narrow kernels: activation chunks, K * N fp16, at a 256-byte boundary].
 size_t partial_bytes(const GemmArgs& a, const w4a16_plan& p) {
+    if (p.kernel == W4A16_KERNEL_TILED) return tiled_partial_bytes(a, tiled_of(p));
+    if (p.kernel == W4A16_KERNEL_NARROW) return narrow_partial_bytes(a, narrow_of(p));
     return p.splitk <= 1 ? 0 : (size_t)p.splitk * (size_t)a.M * (size_t)a.N * 4;
 }
 size_t chunks_offset(const GemmArgs& a, const w4a16_plan& p) {
@@ -395,17 +404,19 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
                         }
     }
     if (N >= 8) {
+        const int pipes[][2] = {{0, 0}, {2, 0}, {2, 2}, {4, 2}, {4, 3}};   // (pf, xpf)
         for (int bm : {128, 256, 512})
             for (int bn : {64, 128, 256})
                 for (int wm : {4, 2, 8})
-                    for (int pf : {0, 2})
-                        for (int splitk : {1, 2, 4}) {
+                    for (const auto& pp : pipes)
+                        for (int splitk : {1, 2, 3, 4}) {
                             memset(&p, 0, sizeof(p));
                             p.kernel = W4A16_KERNEL_TILED;
                             p.bm = bm;
                             p.bn = bn;
                             p.wm = wm;
-                            p.pf = pf;
+                            p.pf = pp[0];
+                            p.xpf = pp[1];
                             p.splitk = splitk;
                             add(p);
                         }
@@ -758,7 +769,7 @@ const char* w4a16_status_string(int status) {
 
 const char* w4a16_last_error(void) { return g_err.c_str(); }
 
-int w4a16_version(void) { return 100; }
+int w4a16_version(void) { return 101; }
 
 int w4a16_pack(const uint8_t* q, const uint8_t* z, int64_t M, int64_t K, int32_t group_size,
                uint32_t* q_packed, uint32_t* z_packed, void* stream) {
@@ -790,23 +801,27 @@ int w4a16_pack(const uint8_t* q, const uint8_t* z, int64_t M, int64_t K, int32_t
     return ok();
 }
 
-int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves) {
-    if (bytes < 16 || bytes % 16 || waves < 1 || waves > 16 || (waves & (waves - 1))) return 0;
-    const int64_t nw = stream_read_waves(bytes);
+int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves, int32_t loads) {
+    const bool pow2 = waves >= 1 && waves <= 16 && !(waves & (waves - 1)) && loads >= 1 && loads <= 16 &&
+                      !(loads & (loads - 1));
+    if (bytes < 16 || bytes % 16 || !pow2) return 0;
+    const int64_t nw = stream_read_waves(bytes, loads);
     return (nw + waves - 1) / waves * waves;
 }
 
-int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t waves, void* stream) {
+int w4a16_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t waves, int32_t loads, void* stream) {
     if (!buf || !sink) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
     if (bytes < 16 || bytes % 16 || bytes > ((int64_t)1 << 40))
         return fail(W4A16_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %lld)", (long long)bytes);
     if (waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
         return fail(W4A16_ERR_INVALID_ARG, "waves must be 1, 2, 4, 8 or 16 (got %d)", (int)waves);
+    if (loads != 1 && loads != 2 && loads != 4 && loads != 8 && loads != 16)
+        return fail(W4A16_ERR_INVALID_ARG, "loads must be 1, 2, 4, 8 or 16 (got %d)", (int)loads);
     if (!aligned16(buf) || !aligned16(sink)) return fail(W4A16_ERR_MISALIGNED, "pointers must be 16-byte aligned");
-    const int64_t words = w4a16_stream_read_sink_words(bytes, waves);
+    const int64_t words = w4a16_stream_read_sink_words(bytes, waves, loads);
     if (overlaps(sink, (size_t)words * 4, buf, (size_t)bytes))
         return fail(W4A16_ERR_INVALID_ARG, "sink overlaps the buffer");
-    const hipError_t e = launch_stream_read(buf, bytes, sink, waves, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_stream_read(buf, bytes, sink, waves, loads, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, "stream read launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -870,7 +885,7 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     else
     {
         const TiledShape t = tiled_of(p);
-        snprintf(buf, len, "tiled_kernel<%d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf);
+        snprintf(buf, len, "tiled_kernel<%d, %d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf);
     }
     return ok();
 }

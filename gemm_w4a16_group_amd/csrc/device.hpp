@@ -67,6 +67,15 @@ __device__ __forceinline__ u32x4 permute_k8(u32x4 v) {
     return r;
 }
 
+// Bits of a float, taken from a value (a __builtin_bit_cast applied directly
+// to an element of an ext_vector_type yields element 0 whatever the index
+// with this compiler, so vector elements pass through here by value).
+__device__ __forceinline__ uint32_t f32_bits(float v) {
+    uint32_t u;
+    __builtin_memcpy(&u, &v, 4);
+    return u;
+}
+
 __device__ __forceinline__ uint32_t f32_to_h16_bits(float v) {
     _Float16 h = (_Float16)v;   // round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);

@@ -13,7 +13,8 @@ struct GemmArgs {
     const uint16_t* x;        // fp16 bits [K, N]
     uint16_t* xp;             // tiled kernel: X as 16-byte chunks [K/8][N] (workspace)
     uint16_t* c;              // fp16 bits [M, N]
-    float* part;              // fp32 [splitk, M, N] partial sums (splitk > 1)
+    float* part;              // fp32 partial sums (splitk > 1): [splitk, M, N]; the tiled kernel keeps
+                              //    [splitk, tiles, waves, its register layout]
     uint32_t* counters;       // one arrival counter per output tile (splitk > 1)
     int64_t M, N, K;
     int32_t G, ZW;
@@ -52,7 +53,8 @@ struct SkinnyShape {
 struct TiledShape {
     int bm, bn, splitk;
     int wm;    // waves along M: 4 (4 x 1), 2 (2 x 2) or 8 (8 x 1, bm = 512)
-    int wpf;   // stages of weights loaded ahead: 1 or 2
+    int wpf;   // stages of weights loaded ahead: 1 or 2 (up to 4 with xpf > 1)
+    int xpf;   // stages of activation chunks staged ahead: 1, or 2 or 3 (four-wave tiles up to 256 x 64)
 };
 
 struct NarrowShape {
@@ -74,6 +76,8 @@ bool tiled_supported(const TiledShape& t);
 // nullptr if the tiled kernel can run this shape, else the reason.
 const char* tiled_check(const GemmArgs& a, const TiledShape& t);
 int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t);
+// fp32 partial tiles of a split plan (whole tiles, in the waves' register layout)
+size_t tiled_partial_bytes(const GemmArgs& a, const TiledShape& t);
 size_t xpack_bytes(const GemmArgs& a);   // workspace the tiled kernel's activation chunks take
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream);
 
@@ -81,6 +85,8 @@ bool narrow_supported(const NarrowShape& s);
 // nullptr if the narrow kernel can run this shape and plan, else the reason.
 const char* narrow_check(const GemmArgs& a, const NarrowShape& s);
 int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s);
+// fp32 partial tiles of a split plan (whole row tiles, ncol columns, register layout)
+size_t narrow_partial_bytes(const GemmArgs& a, const NarrowShape& s);
 size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s);
 // true when the narrow kernel stages the activations straight from x ([K, N],
 // N a multiple of 8), with no re-layout launch before it
@@ -116,10 +122,11 @@ hipError_t launch_quantize(const uint16_t* w, uint32_t* qpk, uint16_t* scales, u
 // records `fmt` as the calling thread's w4a16_last_error() and returns status
 int set_last_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// streaming-read probe: waves per workgroup `waves`, 4 KB read per wave, one
-// word stored per wave into sink[stream_read_waves(bytes) rounded up to whole workgroups]
-int64_t stream_read_waves(int64_t bytes);
-hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int waves, hipStream_t stream);
+// streaming-read probe: waves per workgroup `waves`, `loads` KB read per wave, one
+// word stored per wave into sink[stream_read_waves(bytes, loads) rounded up to whole workgroups]
+int64_t stream_read_waves(int64_t bytes, int loads);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int waves, int loads,
+                              hipStream_t stream);
 
 hipError_t launch_pack_rows(const uint8_t* codes, uint32_t* words, int64_t rows, int64_t len,
                             hipStream_t stream);

@@ -293,46 +293,69 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
 
     // ---- epilogue: lane holds row 16 (kRB wave + rb) + r16 and columns
     // 16 cb + 4 kq .. + 3
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
+    auto store_c = [&](int rb, int cb, const floatx4& v) {
         const int64_t row = row0 + 16 * (kRB * wave_m + rb) + r16;
-        if (wave_k != 0 || row >= M) continue;
+        const int64_t col = 16 * cb + 4 * kq;
+        if (row >= M || col >= N) return;
+        if (a.tm) {
+            // token-major output: the 16 lanes of a k-quarter write 16
+            // consecutive rows of one column
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-            const int64_t col = 16 * cb + 4 * kq;
-            if (col >= N) continue;
-            if (splitk == 1 && a.tm) {
-                // token-major output: the 16 lanes of a k-quarter write 16
-                // consecutive rows of one column
+            for (int j = 0; j < 4; ++j)
+                if (col + j < N) a.c[(col + j) * M + row] = (uint16_t)f32_to_h16_bits(v[j]);
+        } else if (col + 4 <= N && (N & 3) == 0) {
+            uint2 u;
+            u.x = f32_to_h16_bits(v[0]) | (f32_to_h16_bits(v[1]) << 16);
+            u.y = f32_to_h16_bits(v[2]) | (f32_to_h16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(a.c + row * N + col) = u;
+        } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (col + j < N) a.c[(col + j) * M + row] = (uint16_t)f32_to_h16_bits(acc[rb][cb][j]);
-            } else if (splitk == 1) {
-                if (col + 4 <= N && (N & 3) == 0) {
-                    uint2 v;
-                    v.x = f32_to_h16_bits(acc[rb][cb][0]) | (f32_to_h16_bits(acc[rb][cb][1]) << 16);
-                    v.y = f32_to_h16_bits(acc[rb][cb][2]) | (f32_to_h16_bits(acc[rb][cb][3]) << 16);
-                    *reinterpret_cast<uint2*>(a.c + row * N + col) = v;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (col + j < N) a.c[row * N + col + j] = (uint16_t)f32_to_h16_bits(acc[rb][cb][j]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (col + j < N)
-                        __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col + j, acc[rb][cb][j],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int j = 0; j < 4; ++j)
+                if (col + j < N) a.c[row * N + col + j] = (uint16_t)f32_to_h16_bits(v[j]);
         }
+    };
+    if (splitk == 1) {
+        if (wave_k == 0) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) store_c(rb, cb, acc[rb][cb]);
+        }
+        return;
     }
-    if (splitk == 1) return;
 
-    // ---- split-K: the last workgroup of a row tile sums the partials in
-    // order (agent-scope accesses; stores complete, then one release
-    // arrival per workgroup; the last arriver acquires before the barrier
-    // that precedes the merge's loads)
+    // ---- split-K: every split stores its fp32 partial tile; the last
+    // workgroup of a row tile to arrive adds them in split order, its own
+    // from its registers, and stores C.  A partial tile is kept in the
+    // register layout of the four waves that hold the sums
+    // ([wave][block][element][lane], 256 contiguous bytes per element, a
+    // private slot per split and tile): every access is one coalesced store
+    // or load with no mask, and a split's loads are all in flight at once.
+    // Partials are stored and loaded agent-coherently (cache policy sc1, as
+    // agent-scope atomics are).  Every thread waits for its stores to
+    // complete, the workgroup meets, and one thread arrives on the tile's
+    // counter with release semantics; the last arriver's thread acquires,
+    // and the barrier after it orders the merge's loads after that.
+    constexpr int kAgent = 16;                  // cache policy sc1
+    constexpr int SLOT = kRB * NC * 4 * 64;     // floats per wave and split
+    const __amdgpu_buffer_rsrc_t pres =
+        buffer_rsrc(a.part, (int64_t)splitk * gridDim.x * 4 * SLOT * 4);
+    auto slot_off = [&](int s, int rb, int cb) {   // uniform byte offset of a block
+        return (int)(((((int64_t)s * gridDim.x + blockIdx.x) * 4 + wave_m) * SLOT + (rb * NC + cb) * 4 * 64) * 4);
+    };
+    const int lo = lane * 4;
+    if (wave_k == 0) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) {
+                const int so = slot_off(sidx, rb, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[rb][cb][j]), pres,
+                                                          lo + j * 256, so, kAgent);
+            }
+    }
     int* flag = reinterpret_cast<int*>(zl + (size_t)((ngmax + 15) / 8) * ZP);
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
@@ -347,17 +370,49 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         *flag = last;
     }
     __syncthreads();
-    if (!*flag) return;
-    const int64_t total = (int64_t)tile_rows * N;
-    for (int64_t e = tid; e < total; e += NT) {
-        const int64_t row = row0 + e / N;
-        const int64_t col = e % N;
-        float v = 0.f;
-        for (int s = 0; s < splitk; ++s)
-            v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        a.c[a.tm ? col * M + row : row * N + col] = (uint16_t)f32_to_h16_bits(v);
+    if (!*flag || wave_k != 0) return;
+    // the sum runs in split order, (p_0 + ... + p_(sidx-1)) + own +
+    // p_(sidx+1) + ..., the order of a plain left-to-right sum whichever
+    // split arrives last
+    auto load_part = [&](int s, floatx4 (&p)[kRB][NC]) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) {
+                const int so = slot_off(s, rb, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    p[rb][cb][j] = __builtin_bit_cast(float,
+                                                      __builtin_amdgcn_raw_buffer_load_b32(pres, lo + j * 256, so, kAgent));
+            }
+    };
+    floatx4 p[kRB][NC];
+    if (sidx > 0) {
+        floatx4 pre[kRB][NC];
+        load_part(0, pre);
+        for (int s = 1; s < sidx; ++s) {
+            load_part(s, p);
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) pre[rb][cb] += p[rb][cb];
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) acc[rb][cb] = pre[rb][cb] + acc[rb][cb];
     }
+    for (int s = sidx + 1; s < splitk; ++s) {
+        load_part(s, p);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) acc[rb][cb] += p[rb][cb];
+    }
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) store_c(rb, cb, acc[rb][cb]);
 }
 
 template <int NC, int PF, int RB, int WK, bool DX>
@@ -434,10 +489,16 @@ const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
     // 32-bit buffer offsets over the activation chunks and a 128-row weight tile
     if (a.K * a.N * 2 >= ((int64_t)1 << 31)) return "K * N too large";
     if (a.K > ((int64_t)1 << 24)) return "K above 2^24";
+    // 32-bit buffer offsets over the split partials
+    if ((int64_t)narrow_partial_bytes(a, s) > 0x7FFFFFFF) return "the split partial tiles exceed 2^31 - 1 bytes";
     return nullptr;
 }
 
 int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s) { return (a.M + 64 * s.rb - 1) / (64 * s.rb); }
+
+size_t narrow_partial_bytes(const GemmArgs& a, const NarrowShape& s) {
+    return s.splitk <= 1 ? 0 : (size_t)s.splitk * (size_t)narrow_row_tiles(a, s) * (64 * s.rb) * s.ncol * 4;
+}
 
 hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     if (!narrow_direct_x(a)) {

@@ -4,11 +4,11 @@
 // item 2: the GEMV is memory-bound, its efficiency is that of its memory
 // accesses) are measured against, not part of the layer.
 //
-// A workgroup of `waves` waves reads a contiguous 4 KB per wave (four
-// non-temporal 16-byte loads per lane, each instruction one 1 KB run), all
-// loads issued before any is used, XORs what it read and stores one word
-// per wave, so that no load can be dropped and the kernel ends with a
-// store, as the GEMV does.
+// A workgroup of `waves` waves reads a contiguous L KB per wave (L
+// non-temporal 16-byte loads per lane, each instruction one 1 KB run; the
+// GEMV's shape is L = 4), all loads issued before any is used, XORs what it
+// read and stores one word per wave, so that no load can be dropped and the
+// kernel ends with a store, as the GEMV does.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -16,8 +16,7 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kProbeLoads = 4;   // 16-byte loads per lane
-
+template <int kProbeLoads>
 __global__ void __launch_bounds__(1024) stream_read_kernel(const u32x4* __restrict__ src, uint32_t* __restrict__ sink,
                                                            int64_t n16) {
     const int lane = threadIdx.x & 63;
@@ -39,18 +38,32 @@ __global__ void __launch_bounds__(1024) stream_read_kernel(const u32x4* __restri
     if (lane == 0) sink[wave_id] = x;
 }
 
-}  // namespace
-
-int64_t stream_read_waves(int64_t bytes) { return (bytes / 16 + 64 * kProbeLoads - 1) / (64 * kProbeLoads); }
-
-hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int waves, hipStream_t stream) {
-    const int64_t n16 = bytes / 16;
-    const int64_t nw = stream_read_waves(bytes);
+template <int L>
+hipError_t launch_l(const void* buf, int64_t n16, uint32_t* sink, int waves, hipStream_t stream) {
+    const int64_t nw = (n16 + 64 * L - 1) / (64 * L);
     const int64_t blocks = (nw + waves - 1) / waves;
-    if (n16 < 1 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(64 * waves), 0, stream,
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read_kernel<L>, dim3((unsigned)blocks), dim3(64 * waves), 0, stream,
                        static_cast<const u32x4*>(buf), sink, n16);
     return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t stream_read_waves(int64_t bytes, int loads) { return (bytes / 16 + 64 * loads - 1) / (64 * loads); }
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int waves, int loads,
+                              hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    if (n16 < 1) return hipErrorInvalidValue;
+    switch (loads) {
+        case 1: return launch_l<1>(buf, n16, sink, waves, stream);
+        case 2: return launch_l<2>(buf, n16, sink, waves, stream);
+        case 4: return launch_l<4>(buf, n16, sink, waves, stream);
+        case 8: return launch_l<8>(buf, n16, sink, waves, stream);
+        case 16: return launch_l<16>(buf, n16, sink, waves, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4a16

@@ -98,13 +98,14 @@ __global__ void __launch_bounds__(256) xpack_silu_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// NWV waves per workgroup (4 or 8) in a WGM x (NWV / WGM) grid.  WPF is how
-// many stages ahead a wave loads its weight words (1 or 2, in WPF + 1
-// register sets); the activation chunks are always one stage ahead (two LDS
-// buffers).  With WPF = 2 a stage ends by waiting for all but the newest
-// stage's weight loads instead of for every load: each stage issues its
-// activation loads before its weight loads, and loads return in order, so
-// that wait also covers the next stage's chunks.
+// NWV waves per workgroup (4 or 8) in a WGM x (NWV / WGM) grid.  Weights are
+// loaded WPF stages ahead into WPF + 1 register sets; activation chunks XPF
+// stages ahead into a ring of XPF + 1 LDS buffers.  Every stage issues its
+// activation loads, then its weight loads, and ends by waiting for exactly
+// what the next stage reads (loads return in issue order, so the wait
+// leaves the later stages' loads in flight), then one barrier.  Deep
+// pipelines matter where a workgroup's stage is short (few columns): its
+// MFMA work then covers only a fraction of the memory latency.
 // Waves per SIMD the register budget is held to: two when a wave's
 // accumulators take at most 128 registers (so two waves fit in the 512),
 // else one.
@@ -112,7 +113,26 @@ __host__ __device__ constexpr int tiled_waves_per_simd(int BM, int BN, int WGM, 
     return (BM / WGM / 32) * (BN / (NWV / WGM) / 32) * 16 <= 128 ? 2 : 1;
 }
 
-template <int BM, int BN, int WGM, int NWV, int WPF>
+// Loads that may stay outstanding at the end of a stage: those issued after
+// the later of the next stage's activation chunks and weights.
+__host__ __device__ constexpr int tiled_vmcnt(int WPF, int XPF, int XL, int WL) {
+    return XPF >= WPF ? (WPF - 1) * (XL + WL) : WL + (XPF - 1) * (XL + WL);
+}
+
+__host__ __device__ constexpr int tiled_lds_bytes(int BN, int XPF) { return (XPF + 1) * kStageRows * BN * 16; }
+
+// Prefetch distances built for a tile: (1, 1) and (2, 1) everywhere; deeper
+// pipelines for four waves along M and tiles of at most 256 x 64 outputs,
+// as long as a wave never has more than 63 loads outstanding (the load
+// counter's range).
+__host__ __device__ constexpr bool tiled_pipe_ok(int BM, int BN, int WGM, int NWV, int WPF, int XPF) {
+    const int xl = kStageRows * BN / 64 / NWV, wl = 4 * (BM / WGM / 32);
+    if (XPF == 1) return WPF == 1 || WPF == 2;
+    const bool pair = (XPF == 2 && WPF >= 2 && WPF <= 4) || (XPF == 3 && (WPF == 3 || WPF == 4));
+    return pair && NWV == 4 && WGM == 4 && BN <= 128 && BM * BN <= 256 * 64 && (XPF + WPF) * (xl + wl) < 64;
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
 __global__ void __launch_bounds__(64 * NWV)
 __attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd(BM, BN, WGM, NWV))))
 tiled_kernel(GemmArgs a, int splitk) {
@@ -124,11 +144,14 @@ tiled_kernel(GemmArgs a, int splitk) {
     constexpr int XBYTES = kStageRows * BN * 16;        // one stage of activation chunks
     constexpr int XLOADS = kStageRows * BN / 64 / NWV;  // 1 KB buffer-to-LDS loads per wave and stage
     constexpr int NSET = WPF + 1;                       // weight register sets
+    constexpr int NXB = XPF + 1;                        // activation buffers
     constexpr int WLOADS = 4 * RBW;                     // weight, zero and scale loads per wave and stage
+    constexpr int VMW = tiled_vmcnt(WPF, XPF, XLOADS, WLOADS);
     static_assert(BN % 64 == 0 && XLOADS >= 1 && XLOADS % (BN / 64) == 0, "tile");
-    static_assert(WPF == 1 || WPF == 2, "weight prefetch distance");
-    static_assert(WLOADS < 64, "vmcnt");
-    __shared__ __attribute__((aligned(16))) unsigned char xs[2][XBYTES];
+    static_assert(WPF >= 1 && WPF <= 4 && XPF >= 1 && XPF <= 3, "prefetch distances");
+    static_assert(VMW < 64, "vmcnt");
+    // dynamic LDS: NXB activation buffers
+    extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
     __shared__ int flag;
 
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -208,14 +231,16 @@ tiled_kernel(GemmArgs a, int splitk) {
             sS[set][rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
         }
     };
-    auto load_x = [&](int g, int buf) {
+    // stage st's chunks go to buffer (st - st0) % NXB
+    auto load_x = [&](int g, int slot) {
         const i32x4 xres = raw_rsrc(a.xp + (int64_t)g * kStageRows * N * 8, (int64_t)kStageRows * N * 16);
+        unsigned char* buf = xs + slot * XBYTES;
 #pragma unroll
         for (int i = 0; i < XLOADS; ++i) {
             // XLOADS is a multiple of NCB, so the column base depends on i only
             const int chunk = 64 * (wave * XLOADS + i);
             const int row = chunk / BN, cb = i % NCB;
-            buffer_load_lds16(xres, &xs[buf][chunk * 16], xcoff[cb], row * xrow);
+            buffer_load_lds16(xres, buf + chunk * 16, xcoff[cb], row * xrow);
         }
     };
 
@@ -236,16 +261,16 @@ tiled_kernel(GemmArgs a, int splitk) {
     const int last = st1 - 1;
 
     // One stage st (the i-th of this split, weights in register set `set`):
-    // prefetch the next stage's activation chunks into the other LDS buffer
-    // and the weights of stage st + WPF into the set last used by stage
-    // st - 1 (both clamped to the last stage, which then loads itself again
-    // into a buffer or set nobody reads any more), then 8 MFMA steps on stage
-    // st, then wait for what the next stage reads and meet.
+    // prefetch the chunks of stage st + XPF into the buffer stage st - 1 used
+    // and the weights of stage st + WPF into the set stage st - 1 used (both
+    // clamped to the last stage, which then loads itself again into a buffer
+    // or set nobody reads any more), then 8 MFMA steps on stage st, then wait
+    // for what the next stage reads and meet.
     auto stage = [&](int st, int set) {
-        const int cur = (st - st0) & 1;
-        const int nx = st + 1 < st1 ? st + 1 : last;
+        const int rel = st - st0;
+        const int nx = st + XPF < st1 ? st + XPF : last;
         const int nw = st + WPF < st1 ? st + WPF : last;
-        load_x(nx, cur ^ 1);
+        load_x(nx, (rel + XPF) % NXB);
         __builtin_amdgcn_sched_barrier(0);
         load_w(nw, (set + WPF) % NSET);
         // keep every load of the next stage at the top of this one
@@ -254,7 +279,7 @@ tiled_kernel(GemmArgs a, int splitk) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zS[set][rb] >> (4 * (st & 7))) & 0xFu, sS[set][rb]);
 
-        const unsigned char* xb = &xs[cur][bbase];
+        const unsigned char* xb = xs + (rel % NXB) * XBYTES + bbase;
         // A operand of MFMA step t: word t of the lane's eight (k-octet
         // 8 hh + t), dequantized one step ahead; B fragments likewise
         half8 afrag[2][RBW], bfrag[2][CBW];
@@ -283,31 +308,34 @@ tiled_kernel(GemmArgs a, int splitk) {
                                                                          acc[rb][cb], 0, 0, 0);
         }
         // the next stage's chunks have landed in LDS (and its weights in
-        // registers) and every wave is done with buffer cur
-        if (WPF == 1)
-            __builtin_amdgcn_s_waitcnt(0);
-        else   // vmcnt(WLOADS); expcnt and lgkmcnt left alone
-            __builtin_amdgcn_s_waitcnt((WLOADS & 15) | ((WLOADS >> 4) << 14) | (7 << 4) | (15 << 8));
+        // registers) and every wave is done with this stage's buffer;
+        // vmcnt(VMW), expcnt and lgkmcnt left alone
+        __builtin_amdgcn_s_waitcnt((VMW & 15) | ((VMW >> 4) << 14) | (7 << 4) | (15 << 8));
         __syncthreads();
         // each stage is its own scheduling region (no stage's registers
         // live into the next)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // every split has at least one group (splitk <= G)
-    // (issue order kept: chunks, then stage st0's weights, then the next
-    // stage's, so that the waits below and the compiler's own agree)
-    load_x(st0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(st0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (WPF == 2) {
-        load_w(st0 + 1 < st1 ? st0 + 1 : last, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((WLOADS & 15) | ((WLOADS >> 4) << 14) | (7 << 4) | (15 << 8));
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);
+    // every split has at least one group (splitk <= G).  The prologue issues
+    // what the stages before st0 would have: for j = -D .. -1, the chunks of
+    // stage st0 + j + XPF and the weights of stage st0 + j + WPF (those at or
+    // after st0), so that the waits below count the same loads as in the loop
+    constexpr int D = XPF > WPF ? XPF : WPF;
+#pragma unroll
+    for (int j = -D; j < 0; ++j) {
+        if (j + XPF >= 0) {
+            const int g = st0 + j + XPF;
+            load_x(g < st1 ? g : last, (j + XPF) % NXB);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j + WPF >= 0) {
+            const int g = st0 + j + WPF;
+            load_w(g < st1 ? g : last, (j + WPF) % NSET);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    __builtin_amdgcn_s_waitcnt((VMW & 15) | ((VMW >> 4) << 14) | (7 << 4) | (15 << 8));
     __syncthreads();
     // whole rounds of NSET stages, then the rest (so that every path back
     // to the loop head has the same loads in flight)
@@ -316,9 +344,10 @@ tiled_kernel(GemmArgs a, int splitk) {
 #pragma unroll
         for (int j = 0; j < NSET; ++j) stage(st + j, j);
     }
-    if (st < st1) stage(st, 0);
-    if (NSET > 2 && st + 1 < st1) stage(st + 1, 1);
-    // the last stage's own reload may still be in flight
+#pragma unroll
+    for (int j = 0; j < NSET - 1; ++j)
+        if (st + j < st1) stage(st + j, j);
+    // the last stages' own reloads may still be in flight
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
@@ -328,93 +357,157 @@ tiled_kernel(GemmArgs a, int splitk) {
     // (1.3 % faster at N = 4096); the token-major stores are 8 bytes each,
     // M apart between lanes, and need the L2 to merge them (non-temporal
     // ones made that path 36 % slower), so they stay ordinary.
+    auto store_c = [&](int rb, int cb, const floatx16& v) {
+        const int64_t col = col0 + WN * wave_n + cb * 32 + l32;
+        if (col >= N) return;
+        if (a.tm) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t row = row0 + WM * wave_m + 32 * rb + j * 8 + 4 * hh;
+                if ((M & 3) == 0 && row + 3 < M) {
+                    uint2 u;
+                    u.x = f32_to_h16_bits(v[4 * j]) | (f32_to_h16_bits(v[4 * j + 1]) << 16);
+                    u.y = f32_to_h16_bits(v[4 * j + 2]) | (f32_to_h16_bits(v[4 * j + 3]) << 16);
+                    *reinterpret_cast<uint2*>(a.c + col * M + row) = u;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (row + i < M) a.c[col * M + row + i] = (uint16_t)f32_to_h16_bits(v[4 * j + i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
+                if (row < M) __builtin_nontemporal_store((uint16_t)f32_to_h16_bits(v[e]), &a.c[row * N + col]);
+            }
+        }
+    };
+    if (splitk == 1) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) store_c(rb, cb, acc[rb][cb]);
+        return;
+    }
+
+    // ---- split-K: every split stores its fp32 partial tile; the last
+    // workgroup of a tile to arrive adds them in split order, its own from
+    // its registers, and stores C.  A partial tile is kept in the waves'
+    // register layout ([wave][block][element][lane], 256 contiguous bytes
+    // per element and wave, a private slot per split and tile), so that
+    // every access is one coalesced store or load, no lane needs a mask, and
+    // a split's loads are all in flight at once.  Partials are stored and
+    // loaded agent-coherently (cache policy sc1, as agent-scope atomics
+    // are).  Every thread waits for its stores to complete, the workgroup
+    // meets, and one thread arrives on the tile's counter with release
+    // semantics; the last arriver's thread acquires, and the barrier after
+    // it orders the merge's loads after that.
+    constexpr int kAgent = 16;                      // cache policy sc1
+    constexpr int SLOT = RBW * CBW * 16 * 64;       // floats per wave and split
+    const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(a.part, (int64_t)splitk * T * NWV * SLOT * 4);
+    auto slot_off = [&](int s, int rb, int cb) {     // uniform byte offset of a block
+        return (int)(((((int64_t)s * T + tile_id) * NWV + wave) * SLOT + (rb * CBW + cb) * 16 * 64) * 4);
+    };
+    const int lo = lane * 4;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CBW; ++cb) {
-            const int64_t col = col0 + WN * wave_n + cb * 32 + l32;
-            if (col < N) {
-                if (splitk == 1 && a.tm) {
+            const int so = slot_off(sidx, rb, cb);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int64_t row = row0 + WM * wave_m + 32 * rb + j * 8 + 4 * hh;
-                        if ((M & 3) == 0 && row + 3 < M) {
-                            uint2 v;
-                            v.x = f32_to_h16_bits(acc[rb][cb][4 * j]) | (f32_to_h16_bits(acc[rb][cb][4 * j + 1]) << 16);
-                            v.y = f32_to_h16_bits(acc[rb][cb][4 * j + 2]) | (f32_to_h16_bits(acc[rb][cb][4 * j + 3]) << 16);
-                            *reinterpret_cast<uint2*>(a.c + col * M + row) = v;
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (row + i < M) a.c[col * M + row + i] = (uint16_t)f32_to_h16_bits(acc[rb][cb][4 * j + i]);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int64_t row = row0 + WM * wave_m + 32 * rb + (e >> 2) * 8 + 4 * hh + (e & 3);
-                        if (row < M) {
-                            if (splitk == 1)
-                                __builtin_nontemporal_store((uint16_t)f32_to_h16_bits(acc[rb][cb][e]), &a.c[row * N + col]);
-                            else
-                                __hip_atomic_store(a.part + ((int64_t)sidx * M + row) * N + col, acc[rb][cb][e],
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                    }
-                }
-            }
+            for (int e = 0; e < 16; ++e)
+                __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[rb][cb][e]), pres, lo + e * 256,
+                                                      so, kAgent);
         }
-    if (splitk == 1) return;
-
-    // ---- split-K: the last workgroup of a tile sums the partials in order.
-    // Partials are written and read with agent-scope accesses.  Every thread
-    // waits for its stores to complete, the workgroup meets, and one thread
-    // arrives on the tile's counter with release semantics; the last
-    // arriver's thread acquires, and the barrier after it orders the merge's
-    // loads after that acquire.
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELEASE,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == (unsigned)(splitk - 1);
-        if (last) {
+        const int is_last = prev == (unsigned)(splitk - 1);
+        if (is_last) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        flag = last;
+        flag = is_last;
     }
     __syncthreads();
     if (!flag) return;
-    const int64_t rows_here = (M - row0) < BM ? (M - row0) : BM;
-    const int64_t cols_here = (N - col0) < BN ? (N - col0) : BN;
-    const int64_t total = rows_here * cols_here;
-    for (int64_t e = tid; e < total; e += 256) {
-        const int64_t row = row0 + e / cols_here;
-        const int64_t col = col0 + e % cols_here;
-        float v = 0.f;
-        for (int s = 0; s < splitk; ++s)
-            v += __hip_atomic_load(a.part + ((int64_t)s * M + row) * N + col, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        a.c[a.tm ? col * M + row : row * N + col] = (uint16_t)f32_to_h16_bits(v);
+    // the sum runs in split order, (p_0 + ... + p_(sidx-1)) + own +
+    // p_(sidx+1) + ..., the order of a plain left-to-right sum whichever
+    // split arrives last
+    auto load_part = [&](int s, int rb, int cb) {
+        const int so = slot_off(s, rb, cb);
+        floatx16 p;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            p[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pres, lo + e * 256, so, kAgent));
+        return p;
+    };
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CBW; ++cb) {
+            if (sidx > 0) {
+                floatx16 pre = load_part(0, rb, cb);
+                for (int s = 1; s < sidx; ++s) pre += load_part(s, rb, cb);
+                acc[rb][cb] = pre + acc[rb][cb];
+            }
+            for (int s = sidx + 1; s < splitk; ++s) acc[rb][cb] += load_part(s, rb, cb);
+            store_c(rb, cb, acc[rb][cb]);
+        }
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const dim3 grid((unsigned)tiles, (unsigned)t.splitk);
+    constexpr int lds = tiled_lds_bytes(BN, XPF);
+    if constexpr (lds > 65536) {
+        // dynamic LDS above 64 KB must be allowed per kernel, once
+        static const hipError_t ok = [] {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) (void)hipGetLastError();
+            return e;
+        }();
+        if (ok != hipSuccess) return ok;
     }
+    hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(64 * NWV), lds, stream, a, t.splitk);
+    return hipGetLastError();
+}
+
+// The weight / activation prefetch distances built for a tile shape: one or
+// two stages of weights and one of activations for every tile, deeper
+// pipelines for the tiles of four waves that the few-column calls use.
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+hipError_t launch_if(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
+    if constexpr (tiled_pipe_ok(BM, BN, WGM, NWV, WPF, XPF))
+        return launch_one<BM, BN, WGM, NWV, WPF, XPF>(a, t, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WGM = 4, int NWV = 4>
 hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
-    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    dim3 grid((unsigned)tiles, (unsigned)t.splitk);
-    if (t.wpf == 2)
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, 2>), grid, dim3(64 * NWV), 0, stream, a, t.splitk);
-    else
-        hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, 1>), grid, dim3(64 * NWV), 0, stream, a, t.splitk);
-    return hipGetLastError();
+    switch (t.wpf * 10 + t.xpf) {
+        case 11: return launch_if<BM, BN, WGM, NWV, 1, 1>(a, t, stream);
+        case 21: return launch_if<BM, BN, WGM, NWV, 2, 1>(a, t, stream);
+        case 22: return launch_if<BM, BN, WGM, NWV, 2, 2>(a, t, stream);
+        case 32: return launch_if<BM, BN, WGM, NWV, 3, 2>(a, t, stream);
+        case 42: return launch_if<BM, BN, WGM, NWV, 4, 2>(a, t, stream);
+        case 33: return launch_if<BM, BN, WGM, NWV, 3, 3>(a, t, stream);
+        case 43: return launch_if<BM, BN, WGM, NWV, 4, 3>(a, t, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 bool tiled_supported(const TiledShape& t) {
-    if (t.wpf != 1 && t.wpf != 2) return false;
+    if (t.wm != 2 && t.wm != 4 && t.wm != 8) return false;
+    if (!tiled_pipe_ok(t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf)) return false;
     // a third weight register set spills with the 2 x 2 wave grid
     if (t.wpf == 2 && t.wm == 2) return false;
     if (t.wm == 8) return t.bm == 512 && t.bn == 128 && t.splitk >= 1;
@@ -429,11 +522,18 @@ const char* tiled_check(const GemmArgs& a, const TiledShape& t) {
     // 16-row chunk slab
     if ((int64_t)t.bm * (a.K / 2) > 0x7FFFFFFF) return "bm * K / 2 above 2^31 - 1 bytes";
     if (a.N > ((int64_t)1 << 23)) return "N above 2^23";
+    // 32-bit buffer offsets over the split partials
+    if (t.splitk > 1 && (int64_t)tiled_partial_bytes(a, t) > 0x7FFFFFFF)
+        return "the split partial tiles exceed 2^31 - 1 bytes";
     return nullptr;
 }
 
 int64_t tiled_tiles(const GemmArgs& a, const TiledShape& t) {
     return ((a.M + t.bm - 1) / t.bm) * ((a.N + t.bn - 1) / t.bn);
+}
+
+size_t tiled_partial_bytes(const GemmArgs& a, const TiledShape& t) {
+    return t.splitk <= 1 ? 0 : (size_t)t.splitk * (size_t)tiled_tiles(a, t) * t.bm * t.bn * 4;
 }
 
 size_t xpack_bytes(const GemmArgs& a) { return (size_t)a.K * (size_t)a.N * 2; }

@@ -129,7 +129,10 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            bn columns), 2 (2 x 2 waves, bn >= 128) or 8 (eight waves of
  *            64 rows, bm = 512); 0 means 4;
  *            pf = stages (groups of 128 k) of weights a wave loads ahead:
- *            0 or 1 (one) or 2 (two; not with wm = 2);
+ *            0 or 1 (one) or 2 (two; not with wm = 2); xpf = stages of
+ *            activations staged ahead: 0 or 1 (one); deeper pipelines,
+ *            (pf, xpf) in {(2, 2), (3, 2), (4, 2), (3, 3), (4, 3)}, for
+ *            wm = 4 and tiles of at most 256 x 64 outputs with bn <= 128;
  *            splitk as above; bm * K / 2 < 2^31 and N <= 2^23.
  *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
  *            weights in flight per wave (8 or 16); rb = 16-row blocks per
@@ -155,6 +158,7 @@ typedef struct {
     int32_t bn;
     int32_t splitk;
     int32_t pf;
+    int32_t xpf;
 } w4a16_plan;
 
 /* The plan w4a16_gemm uses for this shape.  Returns a status. */
@@ -423,17 +427,18 @@ int w4a16_gemm_silu(const uint32_t *q_packed, const void *scales,
 
 /*
  * Measurement aid, not part of the layer: one launch that reads `bytes` of
- * `buf` once (16-byte non-temporal loads, 4 KB per wave, `waves` waves per
- * workgroup: 1, 2, 4, 8 or 16) and stores one 32-bit word per wave into
- * `sink` (w4a16_stream_read_sink_words(bytes, waves) words, caller-owned,
- * overlapping nothing).  Its time per launch is the attainable rate of a
- * single read of that size, the floor the memory-bound GEMV is held to
- * (PerfXLLM §3.3 item 2: the GEMV is memory-bound).  Requires bytes a
- * positive multiple of 16 and 16-byte aligned pointers.
+ * `buf` once (16-byte non-temporal loads, `loads` KB per wave: 1, 2, 4, 8
+ * or 16; `waves` waves per workgroup: 1, 2, 4, 8 or 16) and stores one
+ * 32-bit word per wave into `sink` (w4a16_stream_read_sink_words(bytes,
+ * waves, loads) words, caller-owned, overlapping nothing).  Its time per
+ * launch is the attainable rate of a single read of that size, the floor
+ * the memory-bound GEMV is held to (PerfXLLM §3.3 item 2: the GEMV is
+ * memory-bound).  Requires bytes a positive multiple of 16 and 16-byte
+ * aligned pointers.
  */
-int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves);
+int64_t w4a16_stream_read_sink_words(int64_t bytes, int32_t waves, int32_t loads);
 int w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
-                      int32_t waves, void *stream);
+                      int32_t waves, int32_t loads, void *stream);
 
 /*
  * w4a16_gemm for callers that cannot allocate (code under HIP graph

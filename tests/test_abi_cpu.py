@@ -196,12 +196,12 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(4096, 1, 11008) == "skinny_kernel<1, 8>"
     # 512-row tiles where they load the 256 CUs as evenly as 256-row tiles
     # (768 = 3 x 256 tiles at N = 4096, 192 at N = 1024), not at N = 2048
-    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<512, 128, 8, 8, 2>"
-    assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2>"
-    assert B.kernel_name(12288, 2048, 4096) == "tiled_kernel<256, 128, 4, 4, 1>"
-    assert B.kernel_name(12288, 512, 4096) == "tiled_kernel<128, 128, 4, 4, 1>"
+    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"
+    assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"
+    assert B.kernel_name(12288, 2048, 4096) == "tiled_kernel<256, 128, 4, 4, 1, 1>"
+    assert B.kernel_name(12288, 512, 4096) == "tiled_kernel<128, 128, 4, 4, 1, 1>"
     p = B.Plan.make(kernel=2, bm=128, bn=256, splitk=1, wm=2)
-    assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2, 4, 1>"
+    assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2, 4, 1, 1>"
     # narrow plans read [K, N] activations in place when N is a multiple of 8
     # (last template argument true) and re-laid by xpack_col_kernel otherwise
     assert B.kernel_name(12288, 16, 4096) == "narrow_kernel<1, 8, 1, 1, true>"
@@ -426,15 +426,18 @@ def test_gemm_silu_checks(lib):
 
 
 def test_stream_read_probe_checks(lib):
-    assert lib.w4a16_stream_read_sink_words(4096, 8) == 8
-    assert lib.w4a16_stream_read_sink_words(26181632, 8) == 6392
-    assert lib.w4a16_stream_read_sink_words(4100, 8) == 0
-    assert lib.w4a16_stream_read_sink_words(4096, 3) == 0
-    assert lib.w4a16_stream_read(NULL, 4096, C, 8, NULL) == INVALID
-    assert lib.w4a16_stream_read(Q, 4096, NULL, 8, NULL) == INVALID
-    assert lib.w4a16_stream_read(Q, 4100, C, 8, NULL) == INVALID
-    assert lib.w4a16_stream_read(Q, 0, C, 8, NULL) == INVALID
-    assert lib.w4a16_stream_read(Q, 4096, C, 3, NULL) == INVALID
-    assert lib.w4a16_stream_read(ctypes.c_void_p(0x100008), 4096, C, 8, NULL) == MISALIGNED
-    assert lib.w4a16_stream_read(Q, 4096, ctypes.c_void_p(0x100000 + 64), 8, NULL) == INVALID
+    assert lib.w4a16_stream_read_sink_words(4096, 8, 4) == 8
+    assert lib.w4a16_stream_read_sink_words(26181632, 8, 4) == 6392
+    assert lib.w4a16_stream_read_sink_words(26181632, 4, 16) == 1600
+    assert lib.w4a16_stream_read_sink_words(4100, 8, 4) == 0
+    assert lib.w4a16_stream_read_sink_words(4096, 3, 4) == 0
+    assert lib.w4a16_stream_read_sink_words(4096, 8, 3) == 0
+    assert lib.w4a16_stream_read(NULL, 4096, C, 8, 4, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4096, NULL, 8, 4, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4100, C, 8, 4, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 0, C, 8, 4, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4096, C, 3, 4, NULL) == INVALID
+    assert lib.w4a16_stream_read(Q, 4096, C, 8, 32, NULL) == INVALID
+    assert lib.w4a16_stream_read(ctypes.c_void_p(0x100008), 4096, C, 8, 4, NULL) == MISALIGNED
+    assert lib.w4a16_stream_read(Q, 4096, ctypes.c_void_p(0x100000 + 64), 8, 4, NULL) == INVALID
     assert b"overlap" in lib.w4a16_last_error()

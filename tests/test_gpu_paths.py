@@ -138,6 +138,40 @@ def test_tiled_deep_plan(case):
     assert np.array_equal(C, run(p, X, plan=base)), case
 
 
+TILED_PIPE = [
+    # (M, K, N, bm, bn, splitk, pf, xpf): weights pf and activations xpf
+    # stages ahead; fewer stages than the pipeline is deep (1, 2, 3 groups),
+    # uneven splits, one stage per split (splitk = G), the 86-group tail,
+    # ragged M and N
+    (1, 128, 1, 128, 64, 1, 4, 3),
+    (129, 256, 77, 128, 64, 1, 2, 2),
+    (300, 384, 64, 128, 64, 1, 4, 2),
+    (300, 640, 100, 128, 64, 2, 4, 3),
+    (257, 1152, 128, 128, 128, 3, 3, 2),
+    (257, 1152, 130, 128, 128, 2, 2, 2),
+    (520, 4096, 64, 256, 64, 4, 3, 2),
+    (200, 11008, 70, 128, 64, 3, 4, 3),
+    (1000, 4096, 130, 128, 64, 3, 4, 2),
+    (64, 1152, 40, 128, 64, 9, 4, 3),
+    (333, 2048, 96, 256, 64, 2, 2, 2),
+]
+
+
+@pytest.mark.parametrize("case", TILED_PIPE, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d_pf%d_xpf%d" % c)
+def test_tiled_pipeline_plan(case):
+    M, K, N, bm, bn, splitk, pf, xpf = case
+    log("tiled pipeline %s" % (case,))
+    p = prob(M, K)
+    X = X_for(K, N)
+    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk, wm=4, pf=pf, xpf=xpf)
+    C = run(p, X, plan=plan)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, str(case))
+    # prefetch distances change no arithmetic: the same bits as one stage ahead
+    base = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk, wm=4, pf=1, xpf=1)
+    assert np.array_equal(C.view(np.uint16), run(p, X, plan=base).view(np.uint16)), case
+
+
 NARROW = [
     # (M, K, N, ncol, pf, splitk, rb, wk): 64- or 128-row tiles with ragged
     # tails, every column width, columns past N, fewer groups than the ring,
@@ -209,6 +243,7 @@ def test_repeatable_bitwise():
     for N, plan in [(1, None), (16, None), (200, None),
                     (8, B.Plan.make(kernel=1, ncol=8, rb=1, wm=2, wk=2, splitk=3)),
                     (264, B.Plan.make(kernel=2, bm=128, bn=256, splitk=2)),
+                    (100, B.Plan.make(kernel=2, bm=128, bn=64, splitk=3, pf=4, xpf=3)),
                     (30, B.Plan.make(kernel=3, ncol=32, pf=8, splitk=3, rb=2, wk=1)),
                     (12, B.Plan.make(kernel=3, ncol=16, pf=8, splitk=1, rb=1, wk=4))]:
         X = X_for(K, N, seed=3)

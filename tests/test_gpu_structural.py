@@ -81,6 +81,12 @@ EXPLICIT = [
     ("tiled_256x64_pf2_split4", _mk(kernel=TI, bm=256, bn=64, wm=4, pf=2, splitk=4), 4096, 64, KN),
     ("tiled_512x128_k11008", _mk(kernel=TI, bm=512, bn=128, wm=8, pf=2, splitk=1), 11008, 24, KN),
     ("tiled_128x64_token", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=1, splitk=1), 4096, 40, TOK),
+    ("tiled_128x64_p42_split3", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=2, splitk=3), 4096, 64, KN),
+    ("tiled_128x64_p43_split4", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=3, splitk=4), 4096, 100, KN),
+    ("tiled_128x128_p32_split2", _mk(kernel=TI, bm=128, bn=128, wm=4, pf=3, xpf=2, splitk=2), 4096, 136, KN),
+    ("tiled_256x64_p22_split3", _mk(kernel=TI, bm=256, bn=64, wm=4, pf=2, xpf=2, splitk=3), 4096, 72, KN),
+    ("tiled_128x64_p43_k11008", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=3, splitk=3), 11008, 64, KN),
+    ("tiled_128x64_p42_token", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=2, splitk=2), 4096, 64, TOK),
     ("skinny_c1_wk4", _mk(kernel=SK, ncol=1, rb=1, wm=1, wk=4, splitk=1), 4096, 1, KN),
     ("skinny_c16_split", _mk(kernel=SK, ncol=16, rb=1, wm=2, wk=4, splitk=4), 4096, 16, KN),
     ("skinny_c32_split8", _mk(kernel=SK, ncol=32, rb=1, wm=1, wk=2, splitk=8), 4096, 32, KN),
