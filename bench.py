@@ -115,7 +115,12 @@ def parse():
                     help="small_n / large_n: token-major x [N, K] and c [N, M]")
     ap.add_argument("--trace-summary", metavar="DIR_OR_CSV",
                     help="summarize a rocprofv3 kernel trace (no GPU): the last --last dispatches of --kernel")
-    ap.add_argument("--kernel", help="with --trace-summary: the kernel's full name as the trace prints it")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="write profiles/traffic_counters.{json,md} from counter summaries (no GPU)")
+    ap.add_argument("--counter-summary", metavar="DIR_OR_CSV",
+                    help="summarize rocprofv3 --pmc counters of --kernel (no GPU)")
+    ap.add_argument("--kernel", help="with --trace-summary / --counter-summary: the kernel's full name as "
+                                     "rocprofv3 prints it")
     ap.add_argument("--last", type=int, default=0, help="with --trace-summary: dispatches counted from the end")
     args = ap.parse_args()
     args.clock_warmup = max(args.clock_warmup, 0.3)
@@ -664,6 +669,43 @@ def extra(args):
                           "plan": plan}), flush=True)
 
 
+def short_kernel_name(name):
+    """A profiler's kernel name reduced to the form w4a16_kernel_name prints:
+    no return type, namespaces or parameter list ("void ns::(anonymous
+    namespace)::tiled_kernel<512, 128, 8, 8, 2, 1>(ns::GemmArgs, int)" ->
+    "tiled_kernel<512, 128, 8, 8, 2, 1>")."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not name.startswith("(anonymous", i):
+            cut = i
+            break
+    name = name[:cut]
+    depth, start = 0, 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == ":" and depth == 0 and name[i:i + 2] == "::":
+            start = i + 2
+    return name[start:].strip()
+
+
+def kernel_matches(name, query):
+    """Profiler kernel name against a query: the short name exactly, or a
+    substring of the full name when the query starts with "~"."""
+    if query.startswith("~"):
+        return query[1:] in name
+    return short_kernel_name(name) == query
+
+
 def trace_summary(path, kernel, last):
     """Durations of the last ``last`` dispatches of ``kernel`` in a rocprofv3
     kernel trace (csv), i.e. the timed calls of a bench run; no GPU."""
@@ -676,7 +718,7 @@ def trace_summary(path, kernel, last):
     for f in files:
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                if r.get("Kernel_Name", "").strip() == kernel:
+                if kernel_matches(r.get("Kernel_Name", ""), kernel):
                     rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     rows.sort()
     if last > 0:
@@ -692,10 +734,117 @@ def trace_summary(path, kernel, last):
                       "files": files}))
 
 
+def counter_summary(path, kernel):
+    """Means per dispatch of the rocprofv3 --pmc counters recorded for
+    ``kernel`` (csv files under ``path``), with the derived ratios they
+    allow: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x
+    GRBM_GUI_ACTIVE), VALU busy (SQ_ACTIVE_INST_VALU over 256 CUs x
+    GRBM_GUI_ACTIVE), mean waves resident per CU (SQ_WAVE_CYCLES /
+    SQ_BUSY_CYCLES), instruction mix per wave; no GPU."""
+    import collections
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                                 recursive=True))
+    acc = collections.defaultdict(list)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_matches(r.get("Kernel_Name", ""), kernel):
+                    acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    c = {k: sum(v) / len(v) for k, v in acc.items()}
+    out = {"kernel": kernel, "dispatches": max((len(v) for v in acc.values()), default=0),
+           "counters": {k: round(v, 1) for k, v in sorted(c.items())}}
+    g = c.get("GRBM_GUI_ACTIVE")
+    if g:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            out["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * g), 4)
+        if "SQ_ACTIVE_INST_VALU" in c:
+            out["valu_busy"] = round(c["SQ_ACTIVE_INST_VALU"] / (256 * g), 4)
+        if "SQ_ACTIVE_INST_LDS" in c:
+            out["lds_busy"] = round(c["SQ_ACTIVE_INST_LDS"] / (256 * g), 4)
+    if c.get("SQ_BUSY_CYCLES") and "SQ_WAVE_CYCLES" in c:
+        out["waves_per_busy_cycle"] = round(c["SQ_WAVE_CYCLES"] / c["SQ_BUSY_CYCLES"], 3)
+    if c.get("SQ_WAVES"):
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+            if k in c:
+                out["per_wave_" + k[9:].lower()] = round(c[k] / c["SQ_WAVES"], 1)
+    print(json.dumps(out))
+
+
+# (tag, kernel as w4a16_kernel_name prints it, M, K, N, bench.py arguments) of
+# the HBM-traffic records; "copy" is the calibration
+TRAFFIC_RUNS = [
+    ("copy", "~elementwise_kernel", 0, 0, 0, "--workload copy_calib"),
+    ("gemv", "skinny_kernel<1, 4>", 12288, 4096, 1, "--steps 400 --warmup 40 --no-gemm --no-cpu-baseline"),
+    ("gemm", "tiled_kernel<512, 128, 8, 8, 2, 1>", 12288, 4096, 4096,
+     "--workload gemm_12288x4096_n4096 --gemm-iters 5 --gemm-warmup 3"),
+]
+
+
+def traffic_commands(tag, args_):
+    return ["rocprofv3 --pmc %s -d /tmp/prof_%s_%s -o pmc --output-format csv -- python3 bench.py %s" % (c, tag, c, args_)
+            for c in ("FETCH_SIZE", "WRITE_SIZE")]
+
+
+def write_traffic(path):
+    """profiles/traffic_counters.{json,md} from the per-run counter summaries
+    <tag>_<FETCH_SIZE|WRITE_SIZE>.json under ``path`` (each the output of
+    --counter-summary for TRAFFIC_RUNS' kernel); no GPU."""
+    def mean(tag, ctr):
+        with open(os.path.join(path, "%s_%s.json" % (tag, ctr))) as fh:
+            d = json.loads(fh.read().strip().splitlines()[-1])
+        return d["counters"][ctr], d["dispatches"]
+    n_copy = 256 << 20
+    cf, _ = mean("copy", "FETCH_SIZE")
+    cw, _ = mean("copy", "WRITE_SIZE")
+    cal = {"kernel": "torch fp16 elementwise copy (torch.mul(src, 1, out=dst)), 256 Mi elements",
+           "bytes_read": 2 * n_copy, "bytes_written": 2 * n_copy, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+           "fetch_factor": 2 * n_copy / (cf * 1024), "write_factor": 2 * n_copy / (cw * 1024),
+           "commands": traffic_commands("copy", TRAFFIC_RUNS[0][5])}
+    recs = {}
+    lines = ["HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), one MI355X", "",
+             "Calibration: %s reads and writes %d B per launch; the counters read %.1f KiB fetched and %.1f KiB "
+             "written," % (cal["kernel"], cal["bytes_read"], cal["fetch_kib"], cal["write_kib"]),
+             "so fetch_factor = %.5f and write_factor = %.5f (applied to every figure below)."
+             % (cal["fetch_factor"], cal["write_factor"])]
+    lines += ["  " + c for c in cal["commands"]] + [""]
+    for tag, kern, M, K, N, a in TRAFFIC_RUNS[1:]:
+        f, nf = mean(tag, "FETCH_SIZE")
+        w, _ = mean(tag, "WRITE_SIZE")
+        b = f * 1024 * cal["fetch_factor"] + w * 1024 * cal["write_factor"]
+        r = {"fetch_kib": round(f, 1), "write_kib": round(w, 1), "dispatches": nf,
+             "sources_sha256": sources_sha(kern), "bytes_per_launch": int(round(b)),
+             "algorithmic_bytes": alg_bytes(M, K, N), "commands": traffic_commands(tag, a)}
+        recs["%s@%dx%dx%d" % (kern, M, K, N)] = r
+        lines.append("%s@%dx%dx%d: FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB per dispatch (mean of %d dispatches)"
+                     % (kern, M, K, N, f, w, nf))
+        lines.append("  HBM bytes per launch %d = %.3f x the algorithmic %d"
+                     % (r["bytes_per_launch"], b / r["algorithmic_bytes"], r["algorithmic_bytes"]))
+        lines += ["  " + c for c in r["commands"]] + [""]
+    lines.append("Summaries: python3 bench.py --counter-summary /tmp/prof_<tag>_<counter> --kernel <kernel>;")
+    lines.append("this file: python3 bench.py --write-traffic <directory of those summaries>.")
+    out = {"note": "HBM bytes per launch = FETCH_SIZE KiB * 1024 * fetch_factor + WRITE_SIZE KiB * 1024 * "
+                   "write_factor; the factors make the counters read the copy kernel's known bytes. Counters were "
+                   "taken on the sources whose sha256 is stored; bench.py reports null traffic once they change.",
+           "calibration": cal, "kernels": recs}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "traffic_counters.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.kernel, args.last)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.kernel)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

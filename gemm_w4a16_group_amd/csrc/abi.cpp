@@ -128,31 +128,62 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     const int64_t G = groups_of(K);
     const GemmArgs a = make_args(M, N, K, layout);
     // narrow kernel for 8 <= N <= 32 (N = 8 and 16 on a small [K, N] matrix
-    // go to the skinny kernel: 4096x4096 8.1 / 8.7 against 10.8 / 11.0 us): 64 rows per
-    // workgroup (128 with 16 columns when 64-row tiles outnumber the CUs:
-    // 22016x4096 N = 8 / 16 21.2 / 21.4 -> 18.5 / 19.1 us), a ring of 8
-    // groups per wave, the smallest split whose activations fit in LDS; two
-    // waves along K per row block with 32 staged columns or more than 32
-    // groups (N = 32: 12288x4096 25.5 -> 23.7 us, 4096x4096 16.8 -> 13.9 us,
-    // 11008x4096 29.1 -> 26.2 us, 4096x11008 33.7 -> 28.3 us; 4096x11008
-    // N = 8 / 16 14.9 / 17.4 -> 13.0 / 15.4 us), else one
+    // go to the skinny kernel: 4096x4096 8.1 / 8.7 against 9.2 / 9.2 us), a
+    // ring of 8 groups per wave, one wave along K per row block, the
+    // smallest split whose activations fit in LDS (each workgroup then holds
+    // a CU's LDS, so about 192 workgroups stream best):
+    // - 16 staged columns: 64 rows per workgroup, 128 when 64-row tiles
+    //   outnumber the CUs (22016x4096 N = 8 / 16: 18.6 / 18.9 us);
+    // - 32 staged columns: 128 rows when that still leaves at least 256
+    //   workgroups' worth of 64-row tiles (12288x4096: 23.4 -> 17.4 us;
+    //   4096x11008: 23.0 -> 17.8 us), else 64 rows and more splits up to
+    //   192 workgroups (4096x4096: 11.3 -> 10.0 us); where even 128-row tiles
+    //   give more than 256 workgroups the tiled kernel is faster
+    //   (22016x4096: 39.4 -> 27.5 us).
     const bool small = M * K < ((int64_t)1 << 25);
     const bool small_kn = small && !a.tm && (N == 8 || N == 16);
     if (N >= 8 && N <= 32 && !small_kn) {
         p.kernel = W4A16_KERNEL_NARROW;
         p.ncol = N <= 16 ? 16 : 32;
         p.pf = 8;
-        p.rb = p.ncol == 16 && (M + 63) / 64 > kCus ? 2 : 1;
-        for (int wk = p.ncol == 32 || G > 32 ? 2 : 1; wk >= 1; --wk) {
-            p.wk = wk;
-            for (int64_t splitk = 1; splitk <= G; ++splitk) {
-                p.splitk = (int32_t)splitk;
-                const std::string saved = g_err;
-                const int st = check_plan(a, p);
-                g_err = saved;
-                if (st == W4A16_OK) return p;
+        p.wk = 1;
+        auto fits = [&](const w4a16_plan& q) {
+            const std::string saved = g_err;
+            const int st = check_plan(a, q);
+            g_err = saved;
+            return st == W4A16_OK;
+        };
+        // smallest feasible split with 64-row tiles
+        p.rb = 1;
+        int64_t smin = 0;
+        for (int64_t splitk = 1; splitk <= G && !smin; ++splitk) {
+            p.splitk = (int32_t)splitk;
+            if (fits(p)) smin = splitk;
+        }
+        const int64_t t64 = (M + 63) / 64, t128 = (M + 127) / 128;
+        bool use = smin > 0;
+        if (use && p.ncol == 16) {
+            p.rb = t64 > kCus ? 2 : 1;
+            p.splitk = (int32_t)smin;
+            use = fits(p);
+        } else if (use) {
+            if (t128 * smin > kCus) {
+                use = false;   // the tiled kernel
+            } else if (t64 * smin >= kCus) {
+                p.rb = 2;
+                p.splitk = (int32_t)smin;
+                use = fits(p);
+            } else {
+                p.splitk = (int32_t)smin;
+                while (t64 * p.splitk < 192) {
+                    w4a16_plan q = p;
+                    q.splitk = p.splitk + 1;
+                    if (!fits(q)) break;
+                    p = q;
+                }
             }
         }
+        if (use) return p;
         memset(&p, 0, sizeof(p));
     }
     if (N < 8 || (!a.tm && skinny_columns(N) && small)) {

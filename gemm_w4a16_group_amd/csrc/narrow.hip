@@ -44,6 +44,32 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
 }
 
+// The eight codes of a packed word as exact fp16 (q - z), in the k order
+// 0, 4, 1, 5, 2, 6, 3, 7 that the activation chunks use: nibbles at bits
+// 0-3 of a half are OR-ed into fp16 1024 (ulp 1), nibbles at bits 4-7 into
+// fp16 64 (ulp 1/16), and 1024 + z / 64 + z are subtracted.  The scale is
+// applied later, to the group's float32 sums.
+struct QMinusZ {
+    uint32_t b1024, b64;   // bias constants in vector registers
+    half2v z1024, z64;
+    __device__ __forceinline__ void init() {
+        b1024 = 0x64006400u;
+        b64 = 0x54005400u;
+    }
+    __device__ __forceinline__ void set(uint32_t z) {
+        z1024 = as_h2(0x64006400u | z | (z << 16));
+        z64 = as_h2(0x54005400u | (z << 4) | (z << 20));
+    }
+    __device__ __forceinline__ half8 operator()(uint32_t w) const {
+        const uint32_t w8 = w >> 8;
+        const half2v p0 = as_h2(and_or(w, 0x000F000Fu, b1024)) - z1024;
+        const half2v p1 = as_h2(and_or(w, 0x00F000F0u, b64)) - z64;
+        const half2v p2 = as_h2(and_or(w8, 0x000F000Fu, b1024)) - z1024;
+        const half2v p3 = as_h2(and_or(w8, 0x00F000F0u, b64)) - z64;
+        return __builtin_bit_cast(half8, u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+    }
+};
+
 template <int NC, int PF, int kRB, int WK, bool DX>
 __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk) {
     constexpr int NCOL = 16 * NC;       // staged columns (N padded to 16 NC)
@@ -201,28 +227,46 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    Dequant dq[kRB];
+    QMinusZ qz[kRB];
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) dq[rb].init();
+    for (int rb = 0; rb < kRB; ++rb) qz[rb].init();
 
     // activation fragment of MFMA step t, block cb, local group s: chunk
     // (16 s + 4 kq + t, 16 cb + r16)
     const unsigned char* xl = DX ? xs + (4 * kq) * NCOL * 16 + (r16 >> 2) * NCOL * 2 + (r16 & 3) * 8
                                  : xs + ((4 * kq) * NCOL + r16) * 16;
 
-    // stage s of this wave: group g0 + gw0 + s, local index gw0 + s
-    auto stage = [&](int p, int s) {
-        const int gl = gw0 + s, g = g0 + gl;
+    // Each stage's four MFMA steps start from zero and give the group's
+    // float32 sums of (q - z) x; the group's scale multiplies them into the
+    // accumulators one stage later (so that multiply waits for nothing).
+    floatx4 part[kRB][NC];
+    float sprev[kRB];
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-            const int r = 16 * (kRB * wave_m + rb) + r16;
-            const uint32_t zw = zl[((g >> 3) - zw0) * ZP + r];
-            dq[rb].set((zw >> (4 * (g & 7))) & 0xFu, sl[gl * SP + r]);
-        }
+    for (int rb = 0; rb < kRB; ++rb) {
+        sprev[rb] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) part[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto retire = [&]() {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[rb][cb][j] = fmaf(sprev[rb], part[rb][cb][j], acc[rb][cb][j]);
+    };
+
+    // LDS operands of a stage (the activation fragments of all four steps,
+    // the zero word and the scale of each row block), read one stage ahead
+    // so that their latency hides behind the previous stage's work
+    half8 xn[4][NC];
+    uint32_t zn[kRB];
+    uint16_t sn[kRB];
+    auto fetch = [&](int s) {
+        const int gl = gw0 + (s < ngw ? s : ngw - 1), g = g0 + gl;
         const unsigned char* xg = xl + gl * 16 * NCOL * 16;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            half8 xf[NC];
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int cb = 0; cb < NC; ++cb) {
                 if constexpr (DX) {
@@ -234,18 +278,51 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
                         (__attribute__((address_space(3))) short4v*)(b));
                     const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) short4v*)(b + 4 * NCOL * 2));
-                    xf[cb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    xn[t][cb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 } else {
-                    xf[cb] = *reinterpret_cast<const half8*>(xg + (t * NCOL + 16 * cb) * 16);
+                    xn[t][cb] = *reinterpret_cast<const half8*>(xg + (t * NCOL + 16 * cb) * 16);
                 }
             }
 #pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            const int r = 16 * (kRB * wave_m + rb) + r16;
+            zn[rb] = zl[((g >> 3) - zw0) * ZP + r] >> (4 * (g & 7));
+            sn[rb] = sl[gl * SP + r];
+        }
+    };
+    fetch(0);
+
+    // stage s of this wave: group g0 + gw0 + s, local index gw0 + s
+    auto stage = [&](int p, int s) {
+        half8 xf[4][NC];
+        float scur[kRB];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) xf[t][cb] = xn[t][cb];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            qz[rb].set(zn[rb] & 0xFu);
+            scur[rb] = (float)__builtin_bit_cast(_Float16, sn[rb]);
+        }
+        fetch(s + 1);
+        floatx4 np[kRB][NC];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
             for (int rb = 0; rb < kRB; ++rb) {
-                const half8 wf = dq[rb](wr[p][rb][t]);
+                const half8 wf = qz[rb](wr[p][rb][t]);
 #pragma unroll
                 for (int cb = 0; cb < NC; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[cb], wf, acc[rb][cb], 0, 0, 0);
+                    np[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        xf[t][cb], wf, t == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : np[rb][cb], 0, 0, 0);
             }
+        retire();
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            sprev[rb] = scur[rb];
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) part[rb][cb] = np[rb][cb];
         }
     };
     // full rounds of PF groups: each slot is refilled with the group PF ahead
@@ -266,6 +343,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p)
         if (s0 + p < ngw) stage(p, s0 + p);
+    retire();
 
     // ---- waves along K meet in LDS (over the activation chunks, which
     // every wave has finished reading): wave_k > 0 parks its sums, wave_k 0
