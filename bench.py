@@ -105,7 +105,7 @@ def parse():
                     choices=["gemv_12288x4096", "gemv_4096x4096", "decode_linears", "small_n",
                              "large_n", "stack", "gemm_12288x4096_n4096", "copy_calib",
                              "quantize_12288x4096", "prologue", "attention", "tune_table", "decode_step",
-                             "read_floor"])
+                             "read_floor", "read_calib"])
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--gemm-warmup", type=int, default=1000, help="untimed N = 4096 calls first (about 0.4 s)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -362,6 +362,21 @@ def headline(args):
     print(json.dumps(line), flush=True)
 
 
+def read_calib():
+    """The streaming-read probe over one 512 MiB buffer, five launches: the
+    reference the rocprofv3 read counter (FETCH_SIZE) is scaled by, since it
+    reads exactly its buffer with 1 KB runs per load instruction, as the
+    weight streams do."""
+    import torch
+    from gemm_w4a16_group_amd import binding as B
+    nb = 512 << 20
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        B.stream_read(buf, waves=8, loads=4)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "read_calib", "launches": 5, "bytes_read_per_launch": nb}), flush=True)
+
+
 def copy_calib():
     """A plain fp16 copy kernel of known size (reads and writes 512 MiB each
     launch): the reference that rocprofv3 FETCH_SIZE / WRITE_SIZE are scaled
@@ -386,6 +401,9 @@ def extra(args):
     rows = []
     if args.workload == "copy_calib":
         copy_calib()
+        return
+    if args.workload == "read_calib":
+        read_calib()
         return
     if args.workload == "read_floor":
         # the streaming-read probe (one launch reads a buffer once) over
@@ -734,13 +752,20 @@ def trace_summary(path, kernel, last):
                       "files": files}))
 
 
+XCDS = 8   # accelerator complex dies of an MI355X
+
+
 def counter_summary(path, kernel):
     """Means per dispatch of the rocprofv3 --pmc counters recorded for
     ``kernel`` (csv files under ``path``), with the derived ratios they
-    allow: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x
-    GRBM_GUI_ACTIVE), VALU busy (SQ_ACTIVE_INST_VALU over 256 CUs x
-    GRBM_GUI_ACTIVE), mean waves resident per CU (SQ_WAVE_CYCLES /
-    SQ_BUSY_CYCLES), instruction mix per wave; no GPU."""
+    allow, over the per-XCD cycle count (GRBM_GUI_ACTIVE counts the eight
+    XCDs together, so one XCD's cycles are an eighth of it): MFMA busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs), VALU and LDS issue busy
+    (SQ_ACTIVE_INST_* over 256 CUs), TA / TD busy (summed over 256 CUs),
+    the clock those cycles imply over the kernel's traced duration when
+    given, mean waves resident per CU (SQ_WAVE_CYCLES / SQ_BUSY_CYCLES),
+    instruction mix per wave; no GPU.  Short kernels read high (the
+    counters run a little past the kernel)."""
     import collections
     import csv
     import glob
@@ -757,12 +782,13 @@ def counter_summary(path, kernel):
            "counters": {k: round(v, 1) for k, v in sorted(c.items())}}
     g = c.get("GRBM_GUI_ACTIVE")
     if g:
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-            out["mfma_busy"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * g), 4)
-        if "SQ_ACTIVE_INST_VALU" in c:
-            out["valu_busy"] = round(c["SQ_ACTIVE_INST_VALU"] / (256 * g), 4)
-        if "SQ_ACTIVE_INST_LDS" in c:
-            out["lds_busy"] = round(c["SQ_ACTIVE_INST_LDS"] / (256 * g), 4)
+        g = g / XCDS
+        out["xcd_cycles"] = round(g, 1)
+        for k, name, units in (("SQ_VALU_MFMA_BUSY_CYCLES", "mfma_busy", 1024),
+                               ("SQ_ACTIVE_INST_VALU", "valu_busy", 256), ("SQ_ACTIVE_INST_LDS", "lds_busy", 256),
+                               ("TA_TA_BUSY_sum", "ta_busy", 256), ("TD_TD_BUSY_sum", "td_busy", 256)):
+            if k in c:
+                out[name] = round(c[k] / (units * g), 4)
     if c.get("SQ_BUSY_CYCLES") and "SQ_WAVE_CYCLES" in c:
         out["waves_per_busy_cycle"] = round(c["SQ_WAVE_CYCLES"] / c["SQ_BUSY_CYCLES"], 3)
     if c.get("SQ_WAVES"):
@@ -773,8 +799,10 @@ def counter_summary(path, kernel):
 
 
 # (tag, kernel as w4a16_kernel_name prints it, M, K, N, bench.py arguments) of
-# the HBM-traffic records; "copy" is the calibration
+# the HBM-traffic records; "readcal" (the read probe over 512 MiB) calibrates
+# the read counters, "copy" (a torch copy of 512 MiB) the write counter
 TRAFFIC_RUNS = [
+    ("readcal", "stream_read_kernel<4>", 0, 0, 0, "--workload read_calib"),
     ("copy", "~elementwise_kernel", 0, 0, 0, "--workload copy_calib"),
     ("gemv", "skinny_kernel<1, 4>", 12288, 4096, 1, "--steps 400 --warmup 40 --no-gemm --no-cpu-baseline"),
     ("gemm", "tiled_kernel<512, 128, 8, 8, 2, 1>", 12288, 4096, 4096,
@@ -783,35 +811,41 @@ TRAFFIC_RUNS = [
 
 
 def traffic_commands(tag, args_):
-    return ["rocprofv3 --pmc %s -d /tmp/prof_%s_%s -o pmc --output-format csv -- python3 bench.py %s" % (c, tag, c, args_)
-            for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    return ["rocprofv3 --pmc %s -d /tmp/prof_%s_%s -o pmc --output-format csv -- python3 bench.py %s"
+            % (ctr, tag, name, args_) for ctr, name in (("FETCH_SIZE", "READ"), ("WRITE_SIZE", "WRITE"))]
 
 
 def write_traffic(path):
     """profiles/traffic_counters.{json,md} from the per-run counter summaries
-    <tag>_<FETCH_SIZE|WRITE_SIZE>.json under ``path`` (each the output of
+    <tag>_READ.json and <tag>_WRITE.json under ``path`` (each the output of
     --counter-summary for TRAFFIC_RUNS' kernel); no GPU."""
-    def mean(tag, ctr):
-        with open(os.path.join(path, "%s_%s.json" % (tag, ctr))) as fh:
-            d = json.loads(fh.read().strip().splitlines()[-1])
-        return d["counters"][ctr], d["dispatches"]
-    n_copy = 256 << 20
-    cf, _ = mean("copy", "FETCH_SIZE")
-    cw, _ = mean("copy", "WRITE_SIZE")
-    cal = {"kernel": "torch fp16 elementwise copy (torch.mul(src, 1, out=dst)), 256 Mi elements",
-           "bytes_read": 2 * n_copy, "bytes_written": 2 * n_copy, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
-           "fetch_factor": 2 * n_copy / (cf * 1024), "write_factor": 2 * n_copy / (cw * 1024),
-           "commands": traffic_commands("copy", TRAFFIC_RUNS[0][5])}
+    def counters(tag, part, kernel):
+        with open(os.path.join(path, "%s_%s.json" % (tag, part))) as fh:
+            for line in fh:
+                d = json.loads(line)
+                if d["kernel"] == kernel:
+                    return d["counters"], d["dispatches"]
+        raise KeyError("%s %s %s" % (tag, part, kernel))
+    nb = 512 << 20
+    rc, _ = counters("readcal", "READ", TRAFFIC_RUNS[0][1])
+    wc, _ = counters("copy", "WRITE", TRAFFIC_RUNS[1][1])
+    cal = {"read_kernel": "the streaming-read probe (stream_read_kernel<4>) over 512 MiB",
+           "write_kernel": "torch fp16 elementwise copy (torch.mul(src, 1, out=dst)), 256 Mi elements",
+           "bytes_read": nb, "bytes_written": nb, "fetch_kib": round(rc["FETCH_SIZE"], 1),
+           "write_kib": round(wc["WRITE_SIZE"], 1), "fetch_factor": nb / (rc["FETCH_SIZE"] * 1024),
+           "write_factor": nb / (wc["WRITE_SIZE"] * 1024),
+           "commands": traffic_commands("readcal", TRAFFIC_RUNS[0][5])[:1] + traffic_commands("copy", TRAFFIC_RUNS[1][5])[1:]}
     recs = {}
-    lines = ["HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE), one MI355X", "",
-             "Calibration: %s reads and writes %d B per launch; the counters read %.1f KiB fetched and %.1f KiB "
-             "written," % (cal["kernel"], cal["bytes_read"], cal["fetch_kib"], cal["write_kib"]),
-             "so fetch_factor = %.5f and write_factor = %.5f (applied to every figure below)."
-             % (cal["fetch_factor"], cal["write_factor"])]
+    lines = ["HBM traffic per launch from rocprofv3 counters, one MI355X", "",
+             "Calibration: %s reads %d B per launch; FETCH_SIZE reads %.1f KiB (fetch_factor %.5f)."
+             % (cal["read_kernel"], nb, cal["fetch_kib"], cal["fetch_factor"]),
+             "%s writes %d B; WRITE_SIZE reads %.1f KiB (write_factor %.5f)."
+             % (cal["write_kernel"], nb, cal["write_kib"], cal["write_factor"])]
     lines += ["  " + c for c in cal["commands"]] + [""]
-    for tag, kern, M, K, N, a in TRAFFIC_RUNS[1:]:
-        f, nf = mean(tag, "FETCH_SIZE")
-        w, _ = mean(tag, "WRITE_SIZE")
+    for tag, kern, M, K, N, a in TRAFFIC_RUNS[2:]:
+        r_, nf = counters(tag, "READ", kern)
+        w_, _ = counters(tag, "WRITE", kern)
+        f, w = r_["FETCH_SIZE"], w_["WRITE_SIZE"]
         b = f * 1024 * cal["fetch_factor"] + w * 1024 * cal["write_factor"]
         r = {"fetch_kib": round(f, 1), "write_kib": round(w, 1), "dispatches": nf,
              "sources_sha256": sources_sha(kern), "bytes_per_launch": int(round(b)),
@@ -822,11 +856,12 @@ def write_traffic(path):
         lines.append("  HBM bytes per launch %d = %.3f x the algorithmic %d"
                      % (r["bytes_per_launch"], b / r["algorithmic_bytes"], r["algorithmic_bytes"]))
         lines += ["  " + c for c in r["commands"]] + [""]
-    lines.append("Summaries: python3 bench.py --counter-summary /tmp/prof_<tag>_<counter> --kernel <kernel>;")
+    lines.append("Summaries: python3 bench.py --counter-summary /tmp/prof_<tag>_<READ|WRITE> --kernel <kernel> "
+                 "> <tag>_<READ|WRITE>.json;")
     lines.append("this file: python3 bench.py --write-traffic <directory of those summaries>.")
     out = {"note": "HBM bytes per launch = FETCH_SIZE KiB * 1024 * fetch_factor + WRITE_SIZE KiB * 1024 * "
-                   "write_factor; the factors make the counters read the copy kernel's known bytes. Counters were "
-                   "taken on the sources whose sha256 is stored; bench.py reports null traffic once they change.",
+                   "write_factor; the factors make the counters read the calibration kernels' known bytes. Counters "
+                   "were taken on the sources whose sha256 is stored; bench.py reports null traffic once they change.",
            "calibration": cal, "kernels": recs}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)

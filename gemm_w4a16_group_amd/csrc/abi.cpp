@@ -91,10 +91,11 @@ GemmArgs make_args(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_LAYOU
 
 SkinnyShape skinny_of(const w4a16_plan& p) { return SkinnyShape{p.ncol, p.rb, p.wm, p.wk, p.splitk}; }
 TiledShape tiled_of(const w4a16_plan& p) {
-    return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm, p.pf == 0 ? 1 : p.pf, p.xpf == 0 ? 1 : p.xpf};
+    return TiledShape{p.bm, p.bn, p.splitk, p.wm == 0 ? 4 : p.wm, p.pf == 0 ? 1 : p.pf, p.xpf == 0 ? 1 : p.xpf,
+                      p.wk == 0 ? 1 : p.wk};
 }
 NarrowShape narrow_of(const w4a16_plan& p) {
-    return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb, p.wk == 0 ? 1 : p.wk};
+    return NarrowShape{p.ncol, p.pf, p.splitk, p.rb == 0 ? 2 : p.rb, p.wk == 0 ? 1 : p.wk, p.wm == 0 ? 4 : p.wm};
 }
 
 int check_plan(const GemmArgs& a, const w4a16_plan& p);
@@ -132,8 +133,8 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     // ring of 8 groups per wave, one wave along K per row block, the
     // smallest split whose activations fit in LDS (each workgroup then holds
     // a CU's LDS, so about 192 workgroups stream best):
-    // - 16 staged columns: 64 rows per workgroup, 128 when 64-row tiles
-    //   outnumber the CUs (22016x4096 N = 8 / 16: 18.6 / 18.9 us);
+    // - 16 staged columns: 64 rows per workgroup, 128 (96 when those still
+    //   fit one per CU) when 64-row tiles outnumber the CUs;
     // - 32 staged columns: 128 rows when that still leaves at least 256
     //   workgroups' worth of 64-row tiles (12288x4096: 23.4 -> 17.4 us;
     //   4096x11008: 23.0 -> 17.8 us), else 64 rows and more splits up to
@@ -165,6 +166,20 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         if (use && p.ncol == 16) {
             p.rb = t64 > kCus ? 2 : 1;
             p.splitk = (int32_t)smin;
+            if (p.rb == 1) {
+                // more splits while every workgroup still has a CU of its own
+                // (4096x11008 N = 8 / 16: 13.6 -> 13.0 us)
+                while (t64 * (p.splitk + 1) <= kCus) {
+                    w4a16_plan q = p;
+                    q.splitk = p.splitk + 1;
+                    if (!fits(q)) break;
+                    p = q;
+                }
+            } else if (p.splitk == 1 && (M + 95) / 96 <= kCus) {
+                // 96-row tiles (three waves) where 128-row tiles leave CUs
+                // idle (22016x4096 N = 8 / 16: 17.4 -> 15.9 us)
+                p.wm = 3;
+            }
             use = fits(p);
         } else if (use) {
             if (t128 * smin > kCus) {
@@ -218,18 +233,38 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     }
     p.kernel = W4A16_KERNEL_TILED;
     p.wm = 4;
+    if (N < 1024) {
+        // Few columns: 128-row tiles, as many workgroups as CUs or a little
+        // fewer.  128-column tiles when they alone give 192 or more, with two
+        // K slices while that is one workgroup per CU (12288x4096 N = 192 /
+        // 256: 43.3 / 45.2 -> 40.2 / 41.4 us); else 64-column tiles, weights
+        // two stages ahead, split along K up to 256 workgroups while every
+        // split keeps 16 groups (4096x4096 N = 256 / 512: 44.6 / 46.4 ->
+        // 24.8 / 32.4 us; 4096x11008 N = 64 / 256: 41.0 / 64.9 -> 35.2 /
+        // 45.5 us).
+        const int64_t tm = (M + 127) / 128;
+        const int64_t t128 = tm * ((N + 127) / 128), t64 = tm * ((N + 63) / 64);
+        p.bm = 128;
+        p.splitk = 1;
+        if (t128 >= 192) {
+            p.bn = 128;
+            if (t128 <= kCus) p.wk = 2;
+        } else {
+            p.bn = 64;
+            p.pf = 2;
+            if (t64 <= kCounterSlots)
+                while (p.splitk < 4 && t64 * (p.splitk + 1) <= kCus && G / (p.splitk + 1) >= 16) ++p.splitk;
+        }
+        return p;
+    }
     // 256-row tiles from N = 1024 on when they still give 256 tiles
-    p.bm = (N >= 4096 || (N >= 1024 && ((M + 255) / 256) * ((N + 127) / 128) >= 256)) ? 256 : 128;
-    // 128-column tiles from N = 256 (12288x4096 N = 256: 47.3 -> 43.4 us)
-    p.bn = N >= 256 ? 128 : 64;
-    // 128 x 64 tiles load their weights two stages ahead (12288x4096 N = 64
-    // / 128: 37.2 / 37.1 -> 28.3 / 29.0 us)
-    if (p.bm == 128 && p.bn == 64) p.pf = 2;
-    // 512 x 128 tiles of eight waves (weights two stages ahead) from N = 1024
-    // when they give a CU no more rows than 256 x 128 tiles do: with one of
-    // them per CU against two of the others, the busiest CU then has the
-    // same work and the activation chunks are staged half as often
-    if (N >= 1024 && M >= 512) {
+    p.bm = (N >= 4096 || ((M + 255) / 256) * ((N + 127) / 128) >= 256) ? 256 : 128;
+    p.bn = 128;
+    // 512 x 128 tiles of eight waves (weights two stages ahead) when they
+    // give a CU no more rows than 256 x 128 tiles do: with one of them per
+    // CU against two of the others, the busiest CU then has the same work
+    // and the activation chunks are staged half as often
+    if (M >= 512) {
         const int64_t t256 = ((M + 255) / 256) * ((N + 127) / 128);
         const int64_t t512 = ((M + 511) / 512) * ((N + 127) / 128);
         if ((t512 + kCus - 1) / kCus * 512 <= (t256 + kCus - 1) / kCus * 256) {
@@ -240,12 +275,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     }
     const int64_t t = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
     int64_t splitk = 1;
-    if (t < 160 && t <= kCounterSlots) {
-        if (N <= 32)
-            splitk = t < 64 ? 4 : 2;
-        else if (N <= 128 || K >= 8192)   // 12288x4096 N = 64 (96 tiles): 28.3 -> 22.7 us
-            splitk = 2;
-    }
+    if (t < 160 && t <= kCounterSlots && K >= 8192) splitk = 2;
     while (splitk > G) splitk /= 2;
     p.splitk = (int32_t)splitk;
     return p;
@@ -422,17 +452,19 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
             for (int pf : {8, 16})
                 for (int rb : {1, 2})
                     for (int wk : {1, 2, 4})
-                        for (int splitk : {1, 2, 3, 4, 6, 8}) {
-                            if (ncol < N) continue;
-                            memset(&p, 0, sizeof(p));
-                            p.kernel = W4A16_KERNEL_NARROW;
-                            p.ncol = ncol;
-                            p.pf = pf;
-                            p.rb = rb;
-                            p.wk = wk;
-                            p.splitk = splitk;
-                            add(p);
-                        }
+                        for (int wm : {4, 3})
+                            for (int splitk : {1, 2, 3, 4, 6, 8}) {
+                                if (ncol < N || (wm == 3 && wk != 1)) continue;
+                                memset(&p, 0, sizeof(p));
+                                p.kernel = W4A16_KERNEL_NARROW;
+                                p.ncol = ncol;
+                                p.pf = pf;
+                                p.rb = rb;
+                                p.wk = wk;
+                                p.wm = wm;
+                                p.splitk = splitk;
+                                add(p);
+                            }
     }
     if (N >= 8) {
         const int pipes[][2] = {{0, 0}, {2, 0}, {2, 2}, {4, 2}, {4, 3}};   // (pf, xpf)
@@ -440,17 +472,19 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
             for (int bn : {64, 128, 256})
                 for (int wm : {4, 2, 8})
                     for (const auto& pp : pipes)
-                        for (int splitk : {1, 2, 3, 4}) {
-                            memset(&p, 0, sizeof(p));
-                            p.kernel = W4A16_KERNEL_TILED;
-                            p.bm = bm;
-                            p.bn = bn;
-                            p.wm = wm;
-                            p.pf = pp[0];
-                            p.xpf = pp[1];
-                            p.splitk = splitk;
-                            add(p);
-                        }
+                        for (int wk : {1, 2})
+                            for (int splitk : {1, 2, 3, 4}) {
+                                memset(&p, 0, sizeof(p));
+                                p.kernel = W4A16_KERNEL_TILED;
+                                p.bm = bm;
+                                p.bn = bn;
+                                p.wm = wm;
+                                p.wk = wk;
+                                p.pf = pp[0];
+                                p.xpf = pp[1];
+                                p.splitk = splitk;
+                                add(p);
+                            }
     }
     return out;
 }
@@ -911,12 +945,13 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     if (p.kernel == W4A16_KERNEL_SKINNY)
         snprintf(buf, len, "skinny_kernel<%d, %d>", p.ncol, skinny_pf(a, skinny_of(p)));
     else if (p.kernel == W4A16_KERNEL_NARROW)
-        snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d, %s>", p.ncol / 16, p.pf, narrow_of(p).rb, narrow_of(p).wk,
-                 narrow_direct_x(a) ? "true" : "false");
+        snprintf(buf, len, "narrow_kernel<%d, %d, %d, %d, %d, %s>", p.ncol / 16, p.pf, narrow_of(p).rb,
+                 narrow_of(p).wk, narrow_of(p).wm, narrow_direct_x(a) ? "true" : "false");
     else
     {
         const TiledShape t = tiled_of(p);
-        snprintf(buf, len, "tiled_kernel<%d, %d, %d, %d, %d, %d>", t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf);
+        snprintf(buf, len, "%s<%d, %d, %d, %d, %d, %d>", t.wk == 2 ? "tiled_k2_kernel" : "tiled_kernel", t.bm, t.bn,
+                 t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf);
     }
     return ok();
 }

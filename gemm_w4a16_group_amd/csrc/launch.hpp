@@ -55,14 +55,16 @@ struct TiledShape {
     int wm;    // waves along M: 4 (4 x 1), 2 (2 x 2) or 8 (8 x 1, bm = 512)
     int wpf;   // stages of weights loaded ahead: 1 or 2 (up to 4 with xpf > 1)
     int xpf;   // stages of activation chunks staged ahead: 1, or 2 or 3 (four-wave tiles up to 256 x 64)
+    int wk;    // K slices: 1, or 2 (four-wave 128 x 64 / 128 x 128 tiles, xpf = 1, wpf <= 2)
 };
 
 struct NarrowShape {
     int ncol;     // staged columns: 16, 32 or 64 (>= N)
     int pf;       // groups of weights in flight per wave: 8 or 16
     int splitk;
-    int rb;       // 16-row blocks per wave: 1 or 2 (64 or 128 rows per workgroup)
-    int wk;       // waves along K per row block: 1, 2 or 4 (256 wk threads)
+    int rb;       // 16-row blocks per wave: 1 or 2
+    int wk;       // waves along K per row block: 1, 2 or 4
+    int wm;       // waves along M: 4, or 3 with wk = 1 (16 wm rb rows, 64 wm wk threads per workgroup)
 };
 
 bool skinny_supported(const SkinnyShape& s);

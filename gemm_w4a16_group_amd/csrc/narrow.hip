@@ -3,24 +3,27 @@
 // item 1 (few tokens make B tall and thin), where the weight stream decides
 // the time and every weight byte must be read once, early and coalesced.
 //
-// A workgroup of four waves owns BM = 4 x 16 RB rows and a contiguous range
-// of groups along K (splitk workgroups share a row tile).  At the start it
-// copies the activations of its groups from L2 straight into LDS, where all
-// four waves read them; it never touches them in HBM again.  [K, N]
-// activations with N a multiple of 8 are copied from X itself, eight k rows
-// per octet stored in dequant order and read back with the transposing LDS
-// read (ds_read_b64_tr_b16), which hands each lane one column's k; any
-// other layout or N goes through the re-layout launch first (16-byte chunks:
-// eight k of one column in dequant order).
+// A workgroup of WM waves (four, or three: 48-row tiles put a 12288-row
+// matrix on 256 CUs, one tile each) owns BM = WM x 16 RB rows and a
+// contiguous range of groups along K (splitk workgroups share a row tile).
+// At the start it copies the activations of its groups from L2 straight
+// into LDS, where all its waves read them; it never touches them in HBM
+// again.  [K, N] activations with N a multiple of 8 are copied from X
+// itself, eight k rows per octet stored in dequant order and read back with
+// the transposing LDS read (ds_read_b64_tr_b16), which hands each lane one
+// column's k; any other layout or N goes through the re-layout launch first
+// (16-byte chunks: eight k of one column in dequant order).
 // Each wave streams the packed weights of its 16 RB rows through a ring of
 // PF register stages (one 128-k group per stage, 16 bytes per lane and
 // 16-row block), so PF groups of every wave are in flight while it works;
 // there is no barrier in the main loop.  Words are dequantized in registers
-// to fp16 (q - z) * s and meet the activations in v_mfma_f32_16x16x32_f16
-// with the activations as the A operand (16 columns as rows) and the weights
-// as B (16 weight rows as columns), so each lane ends with one weight row
-// and four consecutive output columns: one 8-byte store.  fp32 accumulation;
-// split-K partials are summed in order by the last workgroup of a tile.
+// to the exact fp16 codes q - z and meet the activations in
+// v_mfma_f32_16x16x32_f16 with the activations as the A operand (16
+// columns as rows) and the weights as B (16 weight rows as columns); each
+// group's fp32 sums are scaled by s into the accumulators, so each lane
+// ends with one weight row and four consecutive output columns: one 8-byte
+// store.  Split-K partials are summed in order by the last workgroup of a
+// tile.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -70,11 +73,12 @@ struct QMinusZ {
     }
 };
 
-template <int NC, int PF, int kRB, int WK, bool DX>
-__global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk) {
-    constexpr int NCOL = 16 * NC;       // staged columns (N padded to 16 NC)
-    constexpr int kNarrowBM = 64 * kRB; // rows per workgroup (16 kRB per wave)
-    constexpr int NT = 256 * WK;        // threads: 4 waves along M times WK along K
+template <int NC, int PF, int kRB, int WK, int WM, bool DX>
+__global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int splitk) {
+    constexpr int NCOL = 16 * NC;            // staged columns (N padded to 16 NC)
+    constexpr int kNarrowBM = 16 * WM * kRB; // rows per workgroup (16 kRB per wave)
+    constexpr int NT = 64 * WM * WK;         // threads: WM waves along M times WK along K
+    constexpr int NW = WM * WK;              // waves
     constexpr int WLOADS = kRB;         // weight loads per wave and stage
     static_assert(PF * WLOADS < 64, "vmcnt range");
     // dynamic LDS: the activation chunks, then the split-K flag (all of
@@ -86,7 +90,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_m = wave & 3, wave_k = wave >> 2;
+    const int wave_m = wave % WM, wave_k = wave / WM;
     const int r16 = lane & 15;   // weight row in a 16-row block / activation column in a 16-column block
     const int kq = lane >> 4;    // k-quarter of the 32-k MFMA step (words 4 kq .. 4 kq + 3 of a group)
 
@@ -101,12 +105,12 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
 
     // ---- activation chunks of groups [g0, g1), columns [0, NCOL): LDS chunk
     // (o, n) = X chunk (16 g0 + o, n) at (o NCOL + n) * 16.  Wave w issues
-    // instructions j = w, w + 4 WK, ...; instruction j fills chunks
+    // instructions j = w, w + NW, ...; instruction j fills chunks
     // [64 j, 64 j + 64).  Columns past N re-read column N - 1.
     if constexpr (!DX) {
         const i32x4 xres = raw_rsrc(a.xp + (int64_t)g0 * 16 * N * 8, (int64_t)ng * 16 * N * 16);
         const int nins = ng * 16 * NCOL / 64;
-        for (int j = wave; j < nins; j += 4 * WK) {
+        for (int j = wave; j < nins; j += NW) {
             const int c = 64 * j + lane;
             const int o = c / NCOL, n = c % NCOL;
             const int64_t nn = n < N ? n : N - 1;
@@ -121,7 +125,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         const i32x4 xres = raw_rsrc(a.x + (int64_t)g0 * 128 * N, (int64_t)ng * 128 * N * 2);
         const int nins = ng * 16 * NCOL / 64;
         const int n8 = (int)(N >> 3);
-        for (int j = wave; j < nins; j += 4 * WK) {
+        for (int j = wave; j < nins; j += NW) {
             const int c = 64 * j + lane;
             const int o = c / NCOL, w = c % NCOL;
             const int p = w / (NCOL / 8), cc = w % (NCOL / 8);
@@ -171,23 +175,26 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     const int spass = (tile_rows + srs - 1) / srs, zpass = (tile_rows + zrs - 1) / zrs;   // uniform
     const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(a.scales + row0 * G, (int64_t)tile_rows * G * 2);
     const __amdgpu_buffer_rsrc_t zres = buffer_rsrc(a.zpk + row0 * a.ZW, (int64_t)tile_rows * a.ZW * 4);
+    // Every one of the SMAX scale and ZMAX zero loads is issued (passes past
+    // spass / zpass reload the last pass): a load under a branch leaves a
+    // merge of loaded and unloaded values, and the compiler then widens the
+    // loaded one right after its load, waiting there for every load before
+    // it, the activation copies included, before a weight load is issued.
     uint32_t sv[SMAX], zv[ZMAX];
     {
         const int gc = sg < ng ? sg : ng - 1, wc = zg < nzw ? zg : nzw - 1;
 #pragma unroll
-        for (int j = 0; j < SMAX; ++j)
-            if (j < spass) {
-                int r = sr0 + srs * j;
-                r = r < tile_rows ? r : tile_rows - 1;
-                sv[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, (r * G + g0 + gc) * 2, 0, 0);
-            }
+        for (int j = 0; j < SMAX; ++j) {
+            int r = sr0 + srs * (j < spass ? j : spass - 1);
+            r = r < tile_rows ? r : tile_rows - 1;
+            sv[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, (r * G + g0 + gc) * 2, 0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < ZMAX; ++j)
-            if (j < zpass) {
-                int r = zr0 + zrs * j;
-                r = r < tile_rows ? r : tile_rows - 1;
-                zv[j] = __builtin_amdgcn_raw_buffer_load_b32(zres, (r * a.ZW + zw0 + wc) * 4, 0, 0);
-            }
+        for (int j = 0; j < ZMAX; ++j) {
+            int r = zr0 + zrs * (j < zpass ? j : zpass - 1);
+            r = r < tile_rows ? r : tile_rows - 1;
+            zv[j] = __builtin_amdgcn_raw_buffer_load_b32(zres, (r * a.ZW + zw0 + wc) * 4, 0, 0);
+        }
     }
 
     // ring of PF stages of packed words
@@ -356,7 +363,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
             for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
                 for (int cb = 0; cb < NC; ++cb)
-                    red[((((wave_k - 1) * 4 + wave_m) * kRB + rb) * NC + cb) * 64 + lane] = acc[rb][cb];
+                    red[((((wave_k - 1) * WM + wave_m) * kRB + rb) * NC + cb) * 64 + lane] = acc[rb][cb];
         }
         __syncthreads();
         if (wave_k == 0) {
@@ -365,7 +372,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
                 for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
                     for (int cb = 0; cb < NC; ++cb)
-                        acc[rb][cb] += red[((((k - 1) * 4 + wave_m) * kRB + rb) * NC + cb) * 64 + lane];
+                        acc[rb][cb] += red[((((k - 1) * WM + wave_m) * kRB + rb) * NC + cb) * 64 + lane];
         }
     }
 
@@ -405,7 +412,7 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     // ---- split-K: every split stores its fp32 partial tile; the last
     // workgroup of a row tile to arrive adds them in split order, its own
     // from its registers, and stores C.  A partial tile is kept in the
-    // register layout of the four waves that hold the sums
+    // register layout of the WM waves that hold the sums
     // ([wave][block][element][lane], 256 contiguous bytes per element, a
     // private slot per split and tile): every access is one coalesced store
     // or load with no mask, and a split's loads are all in flight at once.
@@ -417,9 +424,9 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
     constexpr int kAgent = 16;                  // cache policy sc1
     constexpr int SLOT = kRB * NC * 4 * 64;     // floats per wave and split
     const __amdgpu_buffer_rsrc_t pres =
-        buffer_rsrc(a.part, (int64_t)splitk * gridDim.x * 4 * SLOT * 4);
+        buffer_rsrc(a.part, (int64_t)splitk * gridDim.x * WM * SLOT * 4);
     auto slot_off = [&](int s, int rb, int cb) {   // uniform byte offset of a block
-        return (int)(((((int64_t)s * gridDim.x + blockIdx.x) * 4 + wave_m) * SLOT + (rb * NC + cb) * 4 * 64) * 4);
+        return (int)(((((int64_t)s * gridDim.x + blockIdx.x) * WM + wave_m) * SLOT + (rb * NC + cb) * 4 * 64) * 4);
     };
     const int lo = lane * 4;
     if (wave_k == 0) {
@@ -493,40 +500,45 @@ __global__ void __launch_bounds__(256 * WK) narrow_kernel(GemmArgs a, int splitk
         for (int cb = 0; cb < NC; ++cb) store_c(rb, cb, acc[rb][cb]);
 }
 
-template <int NC, int PF, int RB, int WK, bool DX>
+template <int NC, int PF, int RB, int WK, int WM, bool DX>
 hipError_t launch_nc(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
-    dim3 grid((unsigned)((a.M + 64 * RB - 1) / (64 * RB)), (unsigned)s.splitk);
+    constexpr int BM = 16 * WM * RB;
+    dim3 grid((unsigned)((a.M + BM - 1) / BM), (unsigned)s.splitk);
     const size_t lds = narrow_lds_bytes(a, s);
     // allow up to 160 KB of dynamic LDS, once per kernel; a refusal is kept
     // here (and cleared from the runtime's last error) and reported only to
     // a launch that needs more than the default 64 KB
     static const hipError_t lds_ok = [] {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB, WK, DX>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&narrow_kernel<NC, PF, RB, WK, WM, DX>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kNarrowMaxLds);
         if (e != hipSuccess) (void)hipGetLastError();
         return e;
     }();
     if (lds_ok != hipSuccess && lds > 65536) return lds_ok;
-    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB, WK, DX>), grid, dim3(256 * WK), lds, stream, a, s.splitk);
+    hipLaunchKernelGGL((narrow_kernel<NC, PF, RB, WK, WM, DX>), grid, dim3(64 * WM * WK), lds, stream, a, s.splitk);
     return hipGetLastError();
 }
 
-template <int NC, int RB, int WK>
+template <int NC, int RB, int WK, int WM>
 hipError_t launch_pf(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     const bool dx = narrow_direct_x(a);
     switch (s.pf) {
-        case 8: return dx ? launch_nc<NC, 8, RB, WK, true>(a, s, stream) : launch_nc<NC, 8, RB, WK, false>(a, s, stream);
-        case 16: return dx ? launch_nc<NC, 16, RB, WK, true>(a, s, stream) : launch_nc<NC, 16, RB, WK, false>(a, s, stream);
+        case 8: return dx ? launch_nc<NC, 8, RB, WK, WM, true>(a, s, stream)
+                          : launch_nc<NC, 8, RB, WK, WM, false>(a, s, stream);
+        case 16: return dx ? launch_nc<NC, 16, RB, WK, WM, true>(a, s, stream)
+                           : launch_nc<NC, 16, RB, WK, WM, false>(a, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+// three waves along M only with one wave along K
 template <int NC, int RB>
 hipError_t launch_wk(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
+    if (s.wm == 3) return s.wk == 1 ? launch_pf<NC, RB, 1, 3>(a, s, stream) : hipErrorInvalidValue;
     switch (s.wk) {
-        case 1: return launch_pf<NC, RB, 1>(a, s, stream);
-        case 2: return launch_pf<NC, RB, 2>(a, s, stream);
-        case 4: return launch_pf<NC, RB, 4>(a, s, stream);
+        case 1: return launch_pf<NC, RB, 1, 4>(a, s, stream);
+        case 2: return launch_pf<NC, RB, 2, 4>(a, s, stream);
+        case 4: return launch_pf<NC, RB, 4, 4>(a, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -540,9 +552,9 @@ hipError_t launch_rb(const GemmArgs& a, const NarrowShape& s, hipStream_t stream
 
 size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
     const int64_t ngmax = (a.G + s.splitk - 1) / s.splitk;
-    const int64_t bm = 64 * s.rb;
-    const size_t chunks = (size_t)ngmax * 16 * s.ncol * 16;                        // activation chunks
-    const size_t red = (size_t)(s.wk - 1) * 4 * s.rb * (s.ncol / 16) * 64 * 16;   // K-wave sums (reuse)
+    const int64_t bm = 16 * s.wm * s.rb;
+    const size_t chunks = (size_t)ngmax * 16 * s.ncol * 16;                           // activation chunks
+    const size_t red = (size_t)(s.wk - 1) * s.wm * s.rb * (s.ncol / 16) * 64 * 16;   // K-wave sums (reuse)
     return (chunks > red ? chunks : red)
            + (size_t)ngmax * (bm + 2) * 2            // scales ([group][row], rows padded by two halves)
            + (size_t)((ngmax + 15) / 8) * (bm + 1) * 4   // zero words (a range of ngmax groups spans at most this many)
@@ -553,14 +565,16 @@ bool narrow_direct_x(const GemmArgs& a) { return !a.tm && !a.xp_ready && !a.act 
 
 bool narrow_supported(const NarrowShape& s) {
     return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 8 || s.pf == 16) &&
-           (s.rb == 1 || s.rb == 2) && (s.wk == 1 || s.wk == 2 || s.wk == 4) && s.splitk >= 1;
+           (s.rb == 1 || s.rb == 2) && (s.wk == 1 || s.wk == 2 || s.wk == 4) &&
+           (s.wm == 4 || (s.wm == 3 && s.wk == 1)) && s.splitk >= 1;
 }
 
 const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
-    if (!narrow_supported(s)) return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2, wk 1, 2 or 4";
+    if (!narrow_supported(s))
+        return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2, wk 1, 2 or 4, wm 4 (or 3 with wk 1)";
     if (a.N > s.ncol) return "N exceeds the plan's columns";
     if ((int64_t)s.splitk * s.wk > a.G) return "splitk * wk exceeds the number of groups";
-    if ((a.G + s.splitk - 1) / s.splitk > 16 * (256 * s.wk / (64 * s.rb)))
+    if ((a.G + s.splitk - 1) / s.splitk > 16 * (4 * s.wk / s.rb))
         return "more than 16 * 4 wk / rb groups per workgroup; raise splitk";
     if (narrow_lds_bytes(a, s) > (size_t)kNarrowMaxLds)
         return "the workgroup's activation chunks exceed 160 KB of LDS; raise splitk";
@@ -572,10 +586,13 @@ const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
     return nullptr;
 }
 
-int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s) { return (a.M + 64 * s.rb - 1) / (64 * s.rb); }
+int64_t narrow_row_tiles(const GemmArgs& a, const NarrowShape& s) {
+    const int64_t bm = 16 * s.wm * s.rb;
+    return (a.M + bm - 1) / bm;
+}
 
 size_t narrow_partial_bytes(const GemmArgs& a, const NarrowShape& s) {
-    return s.splitk <= 1 ? 0 : (size_t)s.splitk * (size_t)narrow_row_tiles(a, s) * (64 * s.rb) * s.ncol * 4;
+    return s.splitk <= 1 ? 0 : (size_t)s.splitk * (size_t)narrow_row_tiles(a, s) * (16 * s.wm * s.rb) * s.ncol * 4;
 }
 
 hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {

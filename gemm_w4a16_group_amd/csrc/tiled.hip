@@ -14,7 +14,12 @@
 //
 // tiled_kernel: a workgroup of NWV waves (four, or eight for 512-row tiles)
 // owns a BM x BN tile of C and walks K one group (128 k) per stage.  The
-// waves form a WGM x (NWV / WGM) grid.  Each wave loads the packed weight
+// waves form a WGM x (NWV / WGM) grid.  tiled_k2_kernel doubles the
+// workgroup into two such grids along K: at stage p the first takes group
+// 2p, the second group 2p + 1 of the split's run, both behind the same
+// barrier, and the second's sums join the first's through LDS at the end,
+// so that few-column tiles (one workgroup per CU) keep two waves on every
+// SIMD with no dequantization done twice.  Each wave loads the packed weight
 // words of its rows straight into registers (32 bytes per lane per 32-row
 // block and stage, one or two stages ahead) and dequantizes them there, one
 // MFMA step ahead, to fp16 (q - z) * s: one fp16 rounding per weight, q - z
@@ -119,7 +124,9 @@ __host__ __device__ constexpr int tiled_vmcnt(int WPF, int XPF, int XL, int WL) 
     return XPF >= WPF ? (WPF - 1) * (XL + WL) : WL + (XPF - 1) * (XL + WL);
 }
 
-__host__ __device__ constexpr int tiled_lds_bytes(int BN, int XPF) { return (XPF + 1) * kStageRows * BN * 16; }
+__host__ __device__ constexpr int tiled_lds_bytes(int BN, int XPF, int WKS = 1) {
+    return (XPF + 1) * WKS * kStageRows * BN * 16;
+}
 
 // Prefetch distances built for a tile: (1, 1) and (2, 1) everywhere; deeper
 // pipelines for four waves along M and tiles of at most 256 x 64 outputs,
@@ -132,10 +139,14 @@ __host__ __device__ constexpr bool tiled_pipe_ok(int BM, int BN, int WGM, int NW
     return pair && NWV == 4 && WGM == 4 && BN <= 128 && BM * BN <= 256 * 64 && (XPF + WPF) * (xl + wl) < 64;
 }
 
-template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
-__global__ void __launch_bounds__(64 * NWV)
-__attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd(BM, BN, WGM, NWV))))
-tiled_kernel(GemmArgs a, int splitk) {
+// Two K slices are built for four-wave grids of tiles up to 128 x 128 with
+// one or two stages of weights and one of activations.
+__host__ __device__ constexpr bool tiled_k2_ok(int BM, int BN, int WGM, int NWV, int WPF, int XPF) {
+    return NWV == 4 && WGM == 4 && BM == 128 && BN <= 128 && XPF == 1 && WPF <= 2;
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS>
+__device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     constexpr int WGN = NWV / WGM;          // waves along N
     constexpr int WM = BM / WGM;            // rows per wave
     constexpr int WN = BN / WGN;            // columns per wave
@@ -147,10 +158,16 @@ tiled_kernel(GemmArgs a, int splitk) {
     constexpr int NXB = XPF + 1;                        // activation buffers
     constexpr int WLOADS = 4 * RBW;                     // weight, zero and scale loads per wave and stage
     constexpr int VMW = tiled_vmcnt(WPF, XPF, XLOADS, WLOADS);
+    constexpr int SLOT = RBW * CBW * 16 * 64;           // accumulator floats per wave
+    // MFMA steps the B fragments are read ahead: as many as 32 more
+    // registers allow with the wave's accumulators at 32 or 64 per lane
+    constexpr int BD = RBW * CBW <= 2 ? 4 : RBW * CBW <= 4 ? 2 : 1;
     static_assert(BN % 64 == 0 && XLOADS >= 1 && XLOADS % (BN / 64) == 0, "tile");
+    static_assert(WKS == 1 || WKS == 2, "waves along K");
+    static_assert((WKS - 1) * NWV * SLOT * 4 <= tiled_lds_bytes(BN, XPF, WKS), "K-slice sums fit the ring");
     static_assert(WPF >= 1 && WPF <= 4 && XPF >= 1 && XPF <= 3, "prefetch distances");
     static_assert(VMW < 64, "vmcnt");
-    // dynamic LDS: NXB activation buffers
+    // dynamic LDS: NXB x WKS activation buffers ([stage slot][K slice])
     extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
     __shared__ int flag;
 
@@ -158,7 +175,9 @@ tiled_kernel(GemmArgs a, int splitk) {
     const int G = a.G;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_k = wave_all / NWV;   // K slice
+    const int wave = wave_all - wave_k * NWV;
     const int wave_m = wave / WGN, wave_n = wave % WGN;
     const int l32 = lane & 31;     // A row / B column / C column inside a 32-block
     const int hh = lane >> 5;      // which half of the 16-k MFMA step
@@ -177,10 +196,13 @@ tiled_kernel(GemmArgs a, int splitk) {
     const int64_t row0 = tm * BM, col0 = tn * BN;
     const int64_t tile_id = tm * ntn + tn;
 
-    // stages are groups of 128 k
+    // groups [st0, st1) of 128 k; stage p (0 .. P - 1) takes group
+    // st0 + WKS p + wave_k in K slice wave_k
     const int sidx = blockIdx.y;
     const int st0 = (int)((int64_t)G * sidx / splitk);
     const int st1 = (int)((int64_t)G * (sidx + 1) / splitk);
+    const int P = (st1 - st0 + WKS - 1) / WKS;
+    auto group_of = [&](int p) { return st0 + WKS * p + wave_k; };
     const int64_t KW = K / 8;
 
     // ---- weights of this lane: row row0 + WM wave_m + 32 rb + l32, words
@@ -231,10 +253,10 @@ tiled_kernel(GemmArgs a, int splitk) {
             sS[set][rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
         }
     };
-    // stage st's chunks go to buffer (st - st0) % NXB
+    // stage p's chunks go to buffer p % NXB of the wave's K slice
     auto load_x = [&](int g, int slot) {
         const i32x4 xres = raw_rsrc(a.xp + (int64_t)g * kStageRows * N * 8, (int64_t)kStageRows * N * 16);
-        unsigned char* buf = xs + slot * XBYTES;
+        unsigned char* buf = xs + (slot * WKS + wave_k) * XBYTES;
 #pragma unroll
         for (int i = 0; i < XLOADS; ++i) {
             // XLOADS is a multiple of NCB, so the column base depends on i only
@@ -259,53 +281,57 @@ tiled_kernel(GemmArgs a, int splitk) {
     // column WN wave_n + 32 cb + l32 -> one base plus an immediate offset
     const int bbase = ((8 * hh) * BN + WN * wave_n + l32) * 16;
     const int last = st1 - 1;
+    auto clamp_g = [&](int g) { return g < st1 ? g : last; };
 
-    // One stage st (the i-th of this split, weights in register set `set`):
-    // prefetch the chunks of stage st + XPF into the buffer stage st - 1 used
-    // and the weights of stage st + WPF into the set stage st - 1 used (both
-    // clamped to the last stage, which then loads itself again into a buffer
-    // or set nobody reads any more), then 8 MFMA steps on stage st, then wait
-    // for what the next stage reads and meet.
-    auto stage = [&](int st, int set) {
-        const int rel = st - st0;
-        const int nx = st + XPF < st1 ? st + XPF : last;
-        const int nw = st + WPF < st1 ? st + WPF : last;
-        load_x(nx, (rel + XPF) % NXB);
+    // One stage p (weights in register set `set`): prefetch the chunks of
+    // stage p + XPF into the buffer stage p - 1 used and the weights of stage
+    // p + WPF into the set stage p - 1 used (groups past the run clamped to
+    // the last group, which then loads itself again into a buffer or set
+    // nobody reads any more), then 8 MFMA steps on stage p's group (none
+    // past the run: the second K slice of an odd run's last stage), then
+    // wait for what the next stage reads and meet.
+    auto stage = [&](int p, int set) {
+        const int g = group_of(p);
+        load_x(clamp_g(group_of(p + XPF)), (p + XPF) % NXB);
         __builtin_amdgcn_sched_barrier(0);
-        load_w(nw, (set + WPF) % NSET);
+        load_w(clamp_g(group_of(p + WPF)), (set + WPF) % NSET);
         // keep every load of the next stage at the top of this one
         __builtin_amdgcn_sched_barrier(0);
-        // scale and zero of this group
+        if (WKS == 1 || g < st1) {   // (the second slice of an odd run's last stage has no group)
+            // scale and zero of this group
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zS[set][rb] >> (4 * (st & 7))) & 0xFu, sS[set][rb]);
+            for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zS[set][rb] >> (4 * (g & 7))) & 0xFu, sS[set][rb]);
 
-        const unsigned char* xb = xs + (rel % NXB) * XBYTES + bbase;
-        // A operand of MFMA step t: word t of the lane's eight (k-octet
-        // 8 hh + t), dequantized one step ahead; B fragments likewise
-        half8 afrag[2][RBW], bfrag[2][CBW];
-        auto read_b = [&](int t, half8* bf) {
-#pragma unroll
-            for (int cb = 0; cb < CBW; ++cb)
-                bf[cb] = *reinterpret_cast<const half8*>(xb + (t * BN + cb * 32) * 16);
-        };
-        auto make_a = [&](int t, half8* af) {
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) af[rb] = dq[rb](wS[set][rb][t >> 2][t & 3]);
-        };
-        read_b(0, bfrag[0]);
-        make_a(0, afrag[0]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t < 7) {
-                read_b(t + 1, bfrag[(t + 1) & 1]);
-                make_a(t + 1, afrag[(t + 1) & 1]);
-            }
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
+            const unsigned char* xb = xs + ((p % NXB) * WKS + wave_k) * XBYTES + bbase;
+            // A operand of MFMA step t: word t of the lane's eight (k-octet
+            // 8 hh + t), dequantized one step ahead.  B fragments are read
+            // BD steps ahead: one step of MFMA work is shorter than an LDS
+            // read's latency, so reading one step ahead left every step
+            // waiting on LDS.
+            half8 afrag[2][RBW], bfrag[BD + 1][CBW];
+            auto read_b = [&](int t, half8* bf) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[t & 1][rb], bfrag[t & 1][cb],
-                                                                         acc[rb][cb], 0, 0, 0);
+                    bf[cb] = *reinterpret_cast<const half8*>(xb + (t * BN + cb * 32) * 16);
+            };
+            auto make_a = [&](int t, half8* af) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) af[rb] = dq[rb](wS[set][rb][t >> 2][t & 3]);
+            };
+#pragma unroll
+            for (int t = 0; t < BD; ++t) read_b(t, bfrag[t]);
+            make_a(0, afrag[0]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t + BD < 8) read_b(t + BD, bfrag[(t + BD) % (BD + 1)]);
+                if (t < 7) make_a(t + 1, afrag[(t + 1) & 1]);
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < CBW; ++cb)
+                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            afrag[t & 1][rb], bfrag[t % (BD + 1)][cb], acc[rb][cb], 0, 0, 0);
+            }
         }
         // the next stage's chunks have landed in LDS (and its weights in
         // registers) and every wave is done with this stage's buffer;
@@ -318,20 +344,19 @@ tiled_kernel(GemmArgs a, int splitk) {
     };
 
     // every split has at least one group (splitk <= G).  The prologue issues
-    // what the stages before st0 would have: for j = -D .. -1, the chunks of
-    // stage st0 + j + XPF and the weights of stage st0 + j + WPF (those at or
-    // after st0), so that the waits below count the same loads as in the loop
+    // what the stages before the first would have: for j = -D .. -1, the
+    // chunks of stage j + XPF and the weights of stage j + WPF (those at or
+    // after stage 0), so that the waits below count the same loads as in the
+    // loop
     constexpr int D = XPF > WPF ? XPF : WPF;
 #pragma unroll
     for (int j = -D; j < 0; ++j) {
         if (j + XPF >= 0) {
-            const int g = st0 + j + XPF;
-            load_x(g < st1 ? g : last, (j + XPF) % NXB);
+            load_x(clamp_g(group_of(j + XPF)), (j + XPF) % NXB);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (j + WPF >= 0) {
-            const int g = st0 + j + WPF;
-            load_w(g < st1 ? g : last, (j + WPF) % NSET);
+            load_w(clamp_g(group_of(j + WPF)), (j + WPF) % NSET);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -339,16 +364,47 @@ tiled_kernel(GemmArgs a, int splitk) {
     __syncthreads();
     // whole rounds of NSET stages, then the rest (so that every path back
     // to the loop head has the same loads in flight)
-    int st = st0;
-    for (; st + NSET <= st1; st += NSET) {
+    int p0 = 0;
+    for (; p0 + NSET <= P; p0 += NSET) {
 #pragma unroll
-        for (int j = 0; j < NSET; ++j) stage(st + j, j);
+        for (int j = 0; j < NSET; ++j) stage(p0 + j, j);
     }
 #pragma unroll
     for (int j = 0; j < NSET - 1; ++j)
-        if (st + j < st1) stage(st + j, j);
+        if (p0 + j < P) stage(p0 + j, j);
     // the last stages' own reloads may still be in flight
     __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- the second K slice's sums join the first's, in LDS over the
+    // activation ring: every wave is past its last read of it (each stage
+    // ends with a barrier), and after this barrier past its last reload
+    // into it (each has waited for its own loads above)
+    if constexpr (WKS > 1) {
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(xs);
+        if (wave_k == 1) {
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        red[(size_t)wave * SLOT + ((rb * CBW + cb) * 16 + e) * 64 + lane] = acc[rb][cb][e];
+        }
+        __syncthreads();
+        if (wave_k == 0) {
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[rb][cb][e] += red[(size_t)wave * SLOT + ((rb * CBW + cb) * 16 + e) * 64 + lane];
+        }
+    }
+    // from here on only the first slice's waves hold sums; the second's
+    // still meet at every barrier below
+    const bool holder = wave_k == 0;
 
     // ---- epilogue: lane holds rows (e / 4) * 8 + 4 hh + e % 4, column l32
     // (token-major output: the four consecutive rows e = 4 j .. 4 j + 3 of a
@@ -384,10 +440,12 @@ tiled_kernel(GemmArgs a, int splitk) {
         }
     };
     if (splitk == 1) {
+        if (holder) {
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
+            for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < CBW; ++cb) store_c(rb, cb, acc[rb][cb]);
+                for (int cb = 0; cb < CBW; ++cb) store_c(rb, cb, acc[rb][cb]);
+        }
         return;
     }
 
@@ -404,22 +462,22 @@ tiled_kernel(GemmArgs a, int splitk) {
     // semantics; the last arriver's thread acquires, and the barrier after
     // it orders the merge's loads after that.
     constexpr int kAgent = 16;                      // cache policy sc1
-    constexpr int SLOT = RBW * CBW * 16 * 64;       // floats per wave and split
     const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(a.part, (int64_t)splitk * T * NWV * SLOT * 4);
     auto slot_off = [&](int s, int rb, int cb) {     // uniform byte offset of a block
         return (int)(((((int64_t)s * T + tile_id) * NWV + wave) * SLOT + (rb * CBW + cb) * 16 * 64) * 4);
     };
     const int lo = lane * 4;
+    if (holder) {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+        for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < CBW; ++cb) {
-            const int so = slot_off(sidx, rb, cb);
+            for (int cb = 0; cb < CBW; ++cb) {
+                const int so = slot_off(sidx, rb, cb);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[rb][cb][e]), pres, lo + e * 256,
-                                                      so, kAgent);
-        }
+                for (int e = 0; e < 16; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[rb][cb][e]), pres, lo + e * 256, so, kAgent);
+            }
+    }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
@@ -433,7 +491,7 @@ tiled_kernel(GemmArgs a, int splitk) {
         flag = is_last;
     }
     __syncthreads();
-    if (!flag) return;
+    if (!flag || !holder) return;
     // the sum runs in split order, (p_0 + ... + p_(sidx-1)) + own +
     // p_(sidx+1) + ..., the order of a plain left-to-right sum whichever
     // split arrives last
@@ -460,22 +518,44 @@ tiled_kernel(GemmArgs a, int splitk) {
 }
 
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+__global__ void __launch_bounds__(64 * NWV)
+__attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd(BM, BN, WGM, NWV))))
+tiled_kernel(GemmArgs a, int splitk) {
+    tiled_body<BM, BN, WGM, NWV, WPF, XPF, 1>(a, splitk);
+}
+
+// two K slices of NWV waves each (two waves per SIMD for four-wave grids)
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+__global__ void __launch_bounds__(128 * NWV) __attribute__((amdgpu_waves_per_eu(2)))
+tiled_k2_kernel(GemmArgs a, int splitk) {
+    tiled_body<BM, BN, WGM, NWV, WPF, XPF, 2>(a, splitk);
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS>
 hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const dim3 grid((unsigned)tiles, (unsigned)t.splitk);
-    constexpr int lds = tiled_lds_bytes(BN, XPF);
+    constexpr int lds = tiled_lds_bytes(BN, XPF, WKS);
     if constexpr (lds > 65536) {
+        const void* fn;
+        if constexpr (WKS == 1)
+            fn = reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+        else
+            fn = reinterpret_cast<const void*>(&tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>);
         // dynamic LDS above 64 KB must be allowed per kernel, once
-        static const hipError_t ok = [] {
-            const hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        static const hipError_t ok = [fn] {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) (void)hipGetLastError();
             return e;
         }();
         if (ok != hipSuccess) return ok;
     }
-    hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(64 * NWV), lds, stream, a, t.splitk);
+    if constexpr (WKS == 1)
+        hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(64 * NWV), lds, stream, a,
+                           t.splitk);
+    else
+        hipLaunchKernelGGL((tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(128 * NWV), lds, stream, a,
+                           t.splitk);
     return hipGetLastError();
 }
 
@@ -484,8 +564,11 @@ hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream
 // pipelines for the tiles of four waves that the few-column calls use.
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
 hipError_t launch_if(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
-    if constexpr (tiled_pipe_ok(BM, BN, WGM, NWV, WPF, XPF))
-        return launch_one<BM, BN, WGM, NWV, WPF, XPF>(a, t, stream);
+    if constexpr (tiled_pipe_ok(BM, BN, WGM, NWV, WPF, XPF)) {
+        if constexpr (tiled_k2_ok(BM, BN, WGM, NWV, WPF, XPF))
+            if (t.wk == 2) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 2>(a, t, stream);
+        if (t.wk == 1) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 1>(a, t, stream);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -507,6 +590,7 @@ hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t strea
 
 bool tiled_supported(const TiledShape& t) {
     if (t.wm != 2 && t.wm != 4 && t.wm != 8) return false;
+    if (t.wk != 1 && !(t.wk == 2 && tiled_k2_ok(t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf))) return false;
     if (!tiled_pipe_ok(t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf)) return false;
     // a third weight register set spills with the 2 x 2 wave grid
     if (t.wpf == 2 && t.wm == 2) return false;

@@ -133,10 +133,14 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            activations staged ahead: 0 or 1 (one); deeper pipelines,
  *            (pf, xpf) in {(2, 2), (3, 2), (4, 2), (3, 3), (4, 3)}, for
  *            wm = 4 and tiles of at most 256 x 64 outputs with bn <= 128;
+ *            wk = K slices: 1 (0 means 1), or 2 for bm = 128, bn <= 128,
+ *            wm = 4, pf <= 2, xpf <= 1 (a second grid of waves takes every
+ *            other group; eight waves per workgroup);
  *            splitk as above; bm * K / 2 < 2^31 and N <= 2^23.
  *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
  *            weights in flight per wave (8 or 16); rb = 16-row blocks per
- *            wave (1 or 2: 64 or 128 rows per workgroup, 0 means 2); wk =
+ *            wave (1 or 2, 0 means 2); wm = waves along rows (4, or 3 with
+ *            wk = 1; 0 means 4), so 16 wm rb rows per workgroup; wk =
  *            waves along K per row block (1, 2 or 4; 0 means 1); splitk as
  *            above, with splitk * wk <= G, and large enough that a
  *            workgroup's activations, ceil(G / splitk) * 256 * ncol bytes

@@ -172,10 +172,39 @@ def test_tiled_pipeline_plan(case):
     assert np.array_equal(C.view(np.uint16), run(p, X, plan=base).view(np.uint16)), case
 
 
+TILED_K2 = [
+    # (M, K, N, bm, bn, splitk, pf): two K slices of four waves; runs of 1,
+    # 2, 3, 5 and 86 groups (odd runs leave the second slice's last stage
+    # empty), uneven splits, one group per split, ragged rows and columns
+    (1, 128, 70, 128, 64, 1, 1),
+    (130, 256, 64, 128, 64, 1, 2),
+    (200, 384, 100, 128, 64, 1, 2),
+    (257, 640, 129, 128, 128, 1, 1),
+    (129, 640, 64, 128, 64, 2, 2),
+    (300, 1152, 130, 128, 128, 3, 2),
+    (128, 1152, 64, 128, 64, 9, 1),
+    (150, 11008, 80, 128, 64, 1, 2),
+    (260, 11008, 256, 128, 128, 4, 1),
+]
+
+
+@pytest.mark.parametrize("case", TILED_K2, ids=lambda c: "M%d_K%d_N%d_bm%d_bn%d_s%d_pf%d" % c)
+def test_tiled_k2_plan(case):
+    M, K, N, bm, bn, splitk, pf = case
+    log("tiled k2 %s" % (case,))
+    p = prob(M, K)
+    X = X_for(K, N)
+    plan = B.Plan.make(kernel=B.KERNEL_TILED, bm=bm, bn=bn, splitk=splitk, wm=4, wk=2, pf=pf, xpf=1)
+    C = run(p, X, plan=plan)
+    C_ref, A_ref = p.reference(X)
+    assert_parity(C, C_ref, A_ref, str(case))
+
+
 NARROW = [
-    # (M, K, N, ncol, pf, splitk, rb, wk): 64- or 128-row tiles with ragged
-    # tails, every column width, columns past N, fewer groups than the ring,
-    # remainders of the ring, splits across workgroups and across waves
+    # (M, K, N, ncol, pf, splitk, rb, wk[, wm]): 64- or 128-row tiles (48 or
+    # 96 with three waves along M) with ragged tails, every column width,
+    # columns past N, fewer groups than the ring, remainders of the ring,
+    # splits across workgroups and across waves
     (1, 128, 1, 16, 8, 1, 2, 1),
     (100, 384, 9, 16, 8, 1, 1, 1),
     (129, 384, 16, 16, 16, 1, 2, 1),
@@ -198,16 +227,23 @@ NARROW = [
     (190, 1152, 9, 16, 8, 2, 2, 4),
     (129, 11008, 24, 32, 8, 6, 1, 2),
     (77, 384, 64, 64, 8, 1, 2, 2),
+    (100, 4096, 16, 16, 8, 1, 1, 1, 3),
+    (150, 1152, 9, 16, 16, 2, 1, 1, 3),
+    (97, 11008, 32, 32, 8, 6, 2, 1, 3),
+    (47, 640, 64, 64, 8, 1, 1, 1, 3),
+    (300, 4096, 24, 32, 8, 4, 1, 1, 3),
 ]
 
 
-@pytest.mark.parametrize("case", NARROW, ids=lambda c: "M%d_K%d_N%d_c%d_pf%d_s%d_rb%d_wk%d" % c)
+@pytest.mark.parametrize("case", NARROW, ids=lambda c: "M%d_K%d_N%d_c%d_pf%d_s%d_rb%d_wk%d" % c[:8]
+                         + ("_wm%d" % c[8] if len(c) > 8 else ""))
 def test_narrow_plan(case):
-    M, K, N, ncol, pf, splitk, rb, wk = case
+    M, K, N, ncol, pf, splitk, rb, wk = case[:8]
+    wm = case[8] if len(case) > 8 else 4
     log("narrow %s" % (case,))
     p = prob(M, K)
     X = X_for(K, N)
-    plan = B.Plan.make(kernel=B.KERNEL_NARROW, ncol=ncol, pf=pf, splitk=splitk, rb=rb, wk=wk)
+    plan = B.Plan.make(kernel=B.KERNEL_NARROW, ncol=ncol, pf=pf, splitk=splitk, rb=rb, wk=wk, wm=wm)
     C = run(p, X, plan=plan)
     C_ref, A_ref = p.reference(X)
     assert_parity(C, C_ref, A_ref, str(case))
@@ -245,7 +281,9 @@ def test_repeatable_bitwise():
                     (264, B.Plan.make(kernel=2, bm=128, bn=256, splitk=2)),
                     (100, B.Plan.make(kernel=2, bm=128, bn=64, splitk=3, pf=4, xpf=3)),
                     (30, B.Plan.make(kernel=3, ncol=32, pf=8, splitk=3, rb=2, wk=1)),
-                    (12, B.Plan.make(kernel=3, ncol=16, pf=8, splitk=1, rb=1, wk=4))]:
+                    (12, B.Plan.make(kernel=3, ncol=16, pf=8, splitk=1, rb=1, wk=4)),
+                    (20, B.Plan.make(kernel=3, ncol=32, pf=8, splitk=4, rb=1, wk=1, wm=3)),
+                    (90, B.Plan.make(kernel=2, bm=128, bn=64, wm=4, wk=2, pf=2, splitk=3))]:
         X = X_for(K, N, seed=3)
         a = run(p, X, plan=plan)
         b = run(p, X, plan=plan)

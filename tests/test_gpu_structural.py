@@ -70,6 +70,10 @@ EXPLICIT = [
     ("narrow_c64_rb2_wk2_relaid", _mk(kernel=NA, ncol=64, pf=8, rb=2, wk=2, splitk=4), 4096, 50, KN),
     ("narrow_c64_pf16_wk4_split8", _mk(kernel=NA, ncol=64, pf=16, rb=1, wk=4, splitk=8), 4096, 40, KN),
     ("narrow_c16_k11008", _mk(kernel=NA, ncol=16, pf=8, rb=1, wk=2, splitk=3), 11008, 16, KN),
+    ("narrow_c16_wm3_dx", _mk(kernel=NA, ncol=16, pf=8, rb=1, wk=1, wm=3, splitk=1), 4096, 16, KN),
+    ("narrow_c16_wm3_n8", _mk(kernel=NA, ncol=16, pf=8, rb=1, wk=1, wm=3, splitk=1), 4096, 8, KN),
+    ("narrow_c32_wm3_rb2_split6", _mk(kernel=NA, ncol=32, pf=8, rb=2, wk=1, wm=3, splitk=6), 11008, 32, KN),
+    ("narrow_c16_wm3_pf16_token", _mk(kernel=NA, ncol=16, pf=16, rb=1, wk=1, wm=3, splitk=2), 4096, 16, TOK),
     ("tiled_512x128_w8_pf2", _mk(kernel=TI, bm=512, bn=128, wm=8, pf=2, splitk=1), 4096, 136, KN),
     ("tiled_512x128_w8_split2", _mk(kernel=TI, bm=512, bn=128, wm=8, pf=2, splitk=2), 4096, 100, KN),
     ("tiled_128x128_w4", _mk(kernel=TI, bm=128, bn=128, wm=4, pf=1, splitk=1), 4096, 136, KN),
@@ -87,6 +91,10 @@ EXPLICIT = [
     ("tiled_256x64_p22_split3", _mk(kernel=TI, bm=256, bn=64, wm=4, pf=2, xpf=2, splitk=3), 4096, 72, KN),
     ("tiled_128x64_p43_k11008", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=3, splitk=3), 11008, 64, KN),
     ("tiled_128x64_p42_token", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=2, splitk=2), 4096, 64, TOK),
+    ("tiled_k2_128x64_split2", _mk(kernel=TI, bm=128, bn=64, wm=4, wk=2, pf=2, splitk=2), 4096, 64, KN),
+    ("tiled_k2_128x64_odd_k11008", _mk(kernel=TI, bm=128, bn=64, wm=4, wk=2, pf=2, splitk=1), 11008, 100, KN),
+    ("tiled_k2_128x128_split3", _mk(kernel=TI, bm=128, bn=128, wm=4, wk=2, pf=1, splitk=3), 4096, 136, KN),
+    ("tiled_k2_128x128_token", _mk(kernel=TI, bm=128, bn=128, wm=4, wk=2, pf=2, splitk=1), 4096, 200, TOK),
     ("skinny_c1_wk4", _mk(kernel=SK, ncol=1, rb=1, wm=1, wk=4, splitk=1), 4096, 1, KN),
     ("skinny_c16_split", _mk(kernel=SK, ncol=16, rb=1, wm=2, wk=4, splitk=4), 4096, 16, KN),
     ("skinny_c32_split8", _mk(kernel=SK, ncol=32, rb=1, wm=1, wk=2, splitk=8), 4096, 32, KN),
@@ -101,7 +109,7 @@ def _rows(plan):
     if plan.kernel == TI:
         tile = plan.bm
     elif plan.kernel == NA:
-        tile = 64 * plan.rb
+        tile = 16 * (plan.wm or 4) * (plan.rb or 2)
     else:
         tile = 16 * plan.rb * max(plan.wm, 1)
     return 2 * tile + tile // 2 + 5
