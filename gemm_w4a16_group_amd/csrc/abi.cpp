@@ -130,7 +130,9 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     const GemmArgs a = make_args(M, N, K, layout);
     // narrow kernel for 8 <= N <= 32 (N = 8 and 16 on a small [K, N] matrix
     // go to the skinny kernel: 4096x4096 8.1 / 8.7 against 9.2 / 9.2 us), a
-    // ring of 8 groups per wave, one wave along K per row block, the
+    // ring of 4 groups per wave (against 8: 12288x4096 N = 32 16.3 -> 15.2
+    // us, 4096x11008 N = 16 / 32 13.0 / 17.5 -> 12.3 / 15.6 us, 22016x4096
+    // N = 16 15.9 -> 15.2 us, the rest equal), one wave along K per row block, the
     // smallest split whose activations fit in LDS (each workgroup then holds
     // a CU's LDS, so about 192 workgroups stream best):
     // - 16 staged columns: 64 rows per workgroup, 128 (96 when those still
@@ -146,7 +148,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     if (N >= 8 && N <= 32 && !small_kn) {
         p.kernel = W4A16_KERNEL_NARROW;
         p.ncol = N <= 16 ? 16 : 32;
-        p.pf = 8;
+        p.pf = 4;
         p.wk = 1;
         auto fits = [&](const w4a16_plan& q) {
             const std::string saved = g_err;

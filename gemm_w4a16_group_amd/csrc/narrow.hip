@@ -523,6 +523,8 @@ template <int NC, int RB, int WK, int WM>
 hipError_t launch_pf(const GemmArgs& a, const NarrowShape& s, hipStream_t stream) {
     const bool dx = narrow_direct_x(a);
     switch (s.pf) {
+        case 4: return dx ? launch_nc<NC, 4, RB, WK, WM, true>(a, s, stream)
+                          : launch_nc<NC, 4, RB, WK, WM, false>(a, s, stream);
         case 8: return dx ? launch_nc<NC, 8, RB, WK, WM, true>(a, s, stream)
                           : launch_nc<NC, 8, RB, WK, WM, false>(a, s, stream);
         case 16: return dx ? launch_nc<NC, 16, RB, WK, WM, true>(a, s, stream)
@@ -564,14 +566,14 @@ size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s) {
 bool narrow_direct_x(const GemmArgs& a) { return !a.tm && !a.xp_ready && !a.act && a.N % 8 == 0; }
 
 bool narrow_supported(const NarrowShape& s) {
-    return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 8 || s.pf == 16) &&
+    return (s.ncol == 16 || s.ncol == 32 || s.ncol == 64) && (s.pf == 4 || s.pf == 8 || s.pf == 16) &&
            (s.rb == 1 || s.rb == 2) && (s.wk == 1 || s.wk == 2 || s.wk == 4) &&
            (s.wm == 4 || (s.wm == 3 && s.wk == 1)) && s.splitk >= 1;
 }
 
 const char* narrow_check(const GemmArgs& a, const NarrowShape& s) {
     if (!narrow_supported(s))
-        return "ncol must be 16, 32 or 64, the prefetch depth 8 or 16, rb 1 or 2, wk 1, 2 or 4, wm 4 (or 3 with wk 1)";
+        return "ncol must be 16, 32 or 64, the prefetch depth 4, 8 or 16, rb 1 or 2, wk 1, 2 or 4, wm 4 (or 3 with wk 1)";
     if (a.N > s.ncol) return "N exceeds the plan's columns";
     if ((int64_t)s.splitk * s.wk > a.G) return "splitk * wk exceeds the number of groups";
     if ((a.G + s.splitk - 1) / s.splitk > 16 * (4 * s.wk / s.rb))

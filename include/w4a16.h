@@ -138,7 +138,7 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            other group; eight waves per workgroup);
  *            splitk as above; bm * K / 2 < 2^31 and N <= 2^23.
  *   narrow : ncol = 16, 32 or 64 staged columns (>= N); pf = groups of
- *            weights in flight per wave (8 or 16); rb = 16-row blocks per
+ *            weights in flight per wave (4, 8 or 16); rb = 16-row blocks per
  *            wave (1 or 2, 0 means 2); wm = waves along rows (4, or 3 with
  *            wk = 1; 0 means 4), so 16 wm rb rows per workgroup; wk =
  *            waves along K per row block (1, 2 or 4; 0 means 1); splitk as

@@ -133,7 +133,7 @@ def test_plan_checks(lib):
     assert gk((1 << 24) - 128, bm=256, wm=4)[0] == WORKSPACE
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2) == WORKSPACE        # valid narrow plan
     assert gp(kernel=3, ncol=8, pf=8, splitk=1, rb=2) == UNSUPPORTED       # 16, 32 or 64 columns
-    assert gp(kernel=3, ncol=16, pf=4, splitk=1, rb=2) == UNSUPPORTED      # ring of 8 or 16
+    assert gp(kernel=3, ncol=16, pf=2, splitk=1, rb=2) == UNSUPPORTED      # ring of 4, 8 or 16
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=3) == UNSUPPORTED
     assert gp(kernel=3, ncol=16, pf=8, splitk=1, rb=2, wk=3) == UNSUPPORTED
     assert gp(kernel=3, ncol=16, pf=8, splitk=3, rb=2, wk=4) == UNSUPPORTED  # 12 > 8 groups
@@ -204,19 +204,19 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(300, 300, 1024, p) == "tiled_kernel<128, 256, 2, 4, 1, 1>"
     # narrow plans read [K, N] activations in place when N is a multiple of 8
     # (last template argument true) and re-laid by xpack_col_kernel otherwise
-    assert B.kernel_name(12288, 16, 4096) == "narrow_kernel<1, 8, 1, 1, 4, true>"
-    assert B.kernel_name(12288, 8, 4096) == "narrow_kernel<1, 8, 1, 1, 4, true>"
-    assert B.kernel_name(12288, 12, 4096) == "narrow_kernel<1, 8, 1, 1, 4, false>"
+    assert B.kernel_name(12288, 16, 4096) == "narrow_kernel<1, 4, 1, 1, 4, true>"
+    assert B.kernel_name(12288, 8, 4096) == "narrow_kernel<1, 4, 1, 1, 4, true>"
+    assert B.kernel_name(12288, 12, 4096) == "narrow_kernel<1, 4, 1, 1, 4, false>"
     # 32 staged columns: 128-row workgroups where 64-row tiles times the
     # smallest split reach 256, the tiled kernel where 128-row ones exceed it
-    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 8, 2, 1, 4, true>"
-    assert B.kernel_name(4096, 24, 11008) == "narrow_kernel<2, 8, 2, 1, 4, true>"
-    assert B.kernel_name(4096, 32, 4096) == "narrow_kernel<2, 8, 1, 1, 4, true>"
+    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 4, 2, 1, 4, true>"
+    assert B.kernel_name(4096, 24, 11008) == "narrow_kernel<2, 4, 2, 1, 4, true>"
+    assert B.kernel_name(4096, 32, 4096) == "narrow_kernel<2, 4, 1, 1, 4, true>"
     assert B.kernel_name(22016, 32, 4096) == "tiled_kernel<128, 64, 4, 4, 2, 1>"
     # 128-row workgroups when 64-row tiles outnumber the CUs; one wave along
     # K; the skinny kernel for N = 8 on a small matrix
-    assert B.kernel_name(22016, 16, 4096) == "narrow_kernel<1, 8, 2, 1, 3, true>"
-    assert B.kernel_name(4096, 8, 11008) == "narrow_kernel<1, 8, 1, 1, 4, true>"
+    assert B.kernel_name(22016, 16, 4096) == "narrow_kernel<1, 4, 2, 1, 3, true>"
+    assert B.kernel_name(4096, 8, 11008) == "narrow_kernel<1, 4, 1, 1, 4, true>"
     assert B.kernel_name(4096, 8, 4096) == "skinny_kernel<8, 4>"
     assert B.kernel_name(4096, 16, 4096) == "skinny_kernel<16, 4>"
     buf = ctypes.create_string_buffer(8)

@@ -232,6 +232,10 @@ NARROW = [
     (97, 11008, 32, 32, 8, 6, 2, 1, 3),
     (47, 640, 64, 64, 8, 1, 1, 1, 3),
     (300, 4096, 24, 32, 8, 4, 1, 1, 3),
+    (300, 4096, 16, 16, 4, 1, 1, 2),
+    (190, 1152, 9, 16, 4, 2, 2, 4),
+    (70, 640, 5, 16, 4, 1, 1, 1),
+    (129, 11008, 32, 32, 4, 6, 2, 2),
 ]
 
 
