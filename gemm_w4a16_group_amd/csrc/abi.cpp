@@ -137,12 +137,12 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     // a CU's LDS, so about 192 workgroups stream best):
     // - 16 staged columns: 64 rows per workgroup, 128 (96 when those still
     //   fit one per CU) when 64-row tiles outnumber the CUs;
-    // - 32 staged columns: 128 rows when that still leaves at least 256
-    //   workgroups' worth of 64-row tiles (12288x4096: 23.4 -> 17.4 us;
-    //   4096x11008: 23.0 -> 17.8 us), else 64 rows and more splits up to
-    //   192 workgroups (4096x4096: 11.3 -> 10.0 us); where even 128-row tiles
-    //   give more than 256 workgroups the tiled kernel is faster
-    //   (22016x4096: 39.4 -> 27.5 us).
+    // - 32 staged columns: 128 rows where 64-row tiles would give at least
+    //   one workgroup per CU, with more splits while the workgroups still
+    //   fit one per CU and 96-row tiles (three waves) where those do
+    //   (12288x4096: 13.9 -> 13.7 us; 4096x11008: 15.6 -> 15.0 us; 22016x4096,
+    //   in place of the tiled kernel: 27.5 -> 25.7 us), else 64 rows and
+    //   more splits up to one workgroup per CU (4096x4096: 9.7 -> 9.4 us).
     const bool small = M * K < ((int64_t)1 << 25);
     const bool small_kn = small && !a.tm && (N == 8 || N == 16);
     if (N >= 8 && N <= 32 && !small_kn) {
@@ -184,15 +184,24 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
             }
             use = fits(p);
         } else if (use) {
-            if (t128 * smin > kCus) {
-                use = false;   // the tiled kernel
-            } else if (t64 * smin >= kCus) {
+            if (t64 * smin >= kCus) {
                 p.rb = 2;
                 p.splitk = (int32_t)smin;
+                while (t128 * (p.splitk + 1) <= kCus) {
+                    w4a16_plan q = p;
+                    q.splitk = p.splitk + 1;
+                    if (!fits(q)) break;
+                    p = q;
+                }
+                if ((M + 95) / 96 * p.splitk <= kCus) {
+                    w4a16_plan q = p;
+                    q.wm = 3;
+                    if (fits(q)) p = q;
+                }
                 use = fits(p);
             } else {
                 p.splitk = (int32_t)smin;
-                while (t64 * p.splitk < 192) {
+                while (t64 * (p.splitk + 1) <= kCus) {
                     w4a16_plan q = p;
                     q.splitk = p.splitk + 1;
                     if (!fits(q)) break;
@@ -471,7 +480,7 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
     }
     if (N <= 64) {
         for (int ncol : {16, 32, 64})
-            for (int pf : {8, 16})
+            for (int pf : {4, 8, 16})
                 for (int rb : {1, 2})
                     for (int wk : {1, 2, 4})
                         for (int wm : {4, 3})

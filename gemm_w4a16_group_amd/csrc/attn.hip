@@ -249,15 +249,26 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     if (tid < D) __hip_atomic_store(part_base + tid, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == D) __hip_atomic_store(part_base + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == D + 1) __hip_atomic_store(part_base + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // stores complete, then one release arrival per workgroup; the last
-    // arriver acquires before the barrier that precedes the merge's loads
+    // Every thread waits until its partial stores (relaxed agent-scope
+    // atomics) have completed, the workgroup meets, and one thread adds one
+    // to the head's counter
+    // (relaxed, agent scope); the barrier after it puts the last arriver's
+    // loads after that add.  This ordering holds without an agent-scope
+    // release or acquire: the partials are written and read only with
+    // agent-coherent accesses (sc1, the instructions of agent-scope
+    // atomics), an sc1 store has reached agent coherence once the load
+    // counter shows it complete, and the barriers' fences keep the compiler
+    // from moving the stores after the add or the loads before it.  A
+    // release or acquire at agent scope would add a write-back (release) or
+    // an invalidation (acquire) of the whole L2 of the workgroup's XCD;
+    // the write-backs, one per workgroup, made plans with two to eight
+    // splits up to five times slower.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(nlive - 1);
         if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(a.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         last_flag = last;

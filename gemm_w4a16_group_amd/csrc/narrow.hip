@@ -416,11 +416,19 @@ __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int sp
     // ([wave][block][element][lane], 256 contiguous bytes per element, a
     // private slot per split and tile): every access is one coalesced store
     // or load with no mask, and a split's loads are all in flight at once.
-    // Partials are stored and loaded agent-coherently (cache policy sc1, as
-    // agent-scope atomics are).  Every thread waits for its stores to
-    // complete, the workgroup meets, and one thread arrives on the tile's
-    // counter with release semantics; the last arriver's thread acquires,
-    // and the barrier after it orders the merge's loads after that.
+    // Every thread waits until its partial stores have completed, the
+    // workgroup meets, and one thread adds one to the tile's counter
+    // (relaxed, agent scope); the barrier after it puts the last arriver's
+    // loads after that add.  This ordering holds without an agent-scope
+    // release or acquire: the partials are written and read only with
+    // agent-coherent accesses (sc1, the instructions of agent-scope
+    // atomics), an sc1 store has reached agent coherence once the load
+    // counter shows it complete, and the barriers' fences keep the compiler
+    // from moving the stores after the add or the loads before it.  A
+    // release or acquire at agent scope would add a write-back (release) or
+    // an invalidation (acquire) of the whole L2 of the workgroup's XCD;
+    // the write-backs, one per workgroup, made plans with two to eight
+    // splits up to five times slower.
     constexpr int kAgent = 16;                  // cache policy sc1
     constexpr int SLOT = kRB * NC * 4 * 64;     // floats per wave and split
     const __amdgpu_buffer_rsrc_t pres =
@@ -445,11 +453,10 @@ __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int sp
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELEASE,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
         if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         *flag = last;

@@ -631,20 +631,28 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     if (splitk == 1) return;
 
     // ---- 8. split-K: the last workgroup of a row tile sums the partials in
-    // order.  Partials are written and read with agent-scope accesses.  Every
-    // thread waits for its stores to complete, the workgroup meets, and one
-    // thread arrives on the tile's counter with release semantics; the last
-    // arriver's thread acquires, and the barrier after it orders the merge's
-    // loads after that acquire.
+    // order.  Partials are written and read with agent-scope relaxed atomics.
+    // Every thread waits until its partial stores have completed, the
+    // workgroup meets, and one thread adds one to the tile's counter
+    // (relaxed, agent scope); the barrier after it puts the last arriver's
+    // loads after that add.  This ordering holds without an agent-scope
+    // release or acquire: the partials are written and read only with
+    // agent-coherent accesses (sc1, the instructions of agent-scope
+    // atomics), an sc1 store has reached agent coherence once the load
+    // counter shows it complete, and the barriers' fences keep the compiler
+    // from moving the stores after the add or the loads before it.  A
+    // release or acquire at agent scope would add a write-back (release) or
+    // an invalidation (acquire) of the whole L2 of the workgroup's XCD;
+    // the write-backs, one per workgroup, made plans with two to eight
+    // splits up to five times slower.
     int* flag = reinterpret_cast<int*>(smem + P.flag_off);
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELEASE,
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == (unsigned)(splitk - 1);
         if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         *flag = last;

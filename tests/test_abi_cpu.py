@@ -208,11 +208,12 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 8, 4096) == "narrow_kernel<1, 4, 1, 1, 4, true>"
     assert B.kernel_name(12288, 12, 4096) == "narrow_kernel<1, 4, 1, 1, 4, false>"
     # 32 staged columns: 128-row workgroups where 64-row tiles times the
-    # smallest split reach 256, the tiled kernel where 128-row ones exceed it
-    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 4, 2, 1, 4, true>"
+    # smallest split reach 256 (96-row ones of three waves where those fit
+    # one per CU), 64-row ones otherwise
+    assert B.kernel_name(12288, 32, 4096) == "narrow_kernel<2, 4, 2, 1, 3, true>"
     assert B.kernel_name(4096, 24, 11008) == "narrow_kernel<2, 4, 2, 1, 4, true>"
     assert B.kernel_name(4096, 32, 4096) == "narrow_kernel<2, 4, 1, 1, 4, true>"
-    assert B.kernel_name(22016, 32, 4096) == "tiled_kernel<128, 64, 4, 4, 2, 1>"
+    assert B.kernel_name(22016, 32, 4096) == "narrow_kernel<2, 4, 2, 1, 4, true>"
     # 128-row workgroups when 64-row tiles outnumber the CUs; one wave along
     # K; the skinny kernel for N = 8 on a small matrix
     assert B.kernel_name(22016, 16, 4096) == "narrow_kernel<1, 4, 2, 1, 3, true>"
