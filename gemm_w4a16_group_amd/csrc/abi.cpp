@@ -280,6 +280,13 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         if (t128 >= 192) {
             p.bn = 128;
             if (t128 <= kCus) p.wk = 2;
+        } else if (t128 >= 96 && G >= 64 && t128 <= kCounterSlots) {
+            // long K: 128-column tiles split along K to fill the CUs
+            // (4096x11008 N = 384 / 512: 67.3 / 75.4 -> 61.2 / 67.8 us; at
+            // K = 4096 the 64-column tiles stay ahead)
+            p.bn = 128;
+            p.pf = 2;
+            p.splitk = (int32_t)(kCus / t128);
         } else {
             p.bn = 64;
             p.pf = 2;
