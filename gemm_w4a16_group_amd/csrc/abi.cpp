@@ -292,6 +292,16 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
             p.pf = 2;
             if (t64 <= kCounterSlots)
                 while (p.splitk < 4 && t64 * (p.splitk + 1) <= kCus && G / (p.splitk + 1) >= 16) ++p.splitk;
+            // 96-row tiles of three waves where 128-row ones leave a fifth
+            // of the CUs idle and these nearly fill them (12288x4096 N = 48
+            // / 64 / 128: 21.7 / 21.2 / 28.7 -> 20.3 / 20.3 / 27.6 us;
+            // 11008x4096 N = 64 / 128: 21.3 / 28.7 -> 20.7 / 27.5 us)
+            const int64_t t96 = ((M + 95) / 96) * ((N + 63) / 64);
+            if (t64 * p.splitk < 200 && t96 * p.splitk >= 224 && t96 * p.splitk <= kCus &&
+                (p.splitk == 1 || t96 <= kCounterSlots)) {
+                p.bm = 96;
+                p.wm = 3;
+            }
         }
         return p;
     }
@@ -523,6 +533,17 @@ std::vector<w4a16_plan> candidate_plans(const GemmArgs& a) {
                                 p.splitk = splitk;
                                 add(p);
                             }
+        for (int pf : {1, 2})   // 96 x 64 tiles of three waves
+            for (int splitk : {1, 2, 3, 4}) {
+                memset(&p, 0, sizeof(p));
+                p.kernel = W4A16_KERNEL_TILED;
+                p.bm = 96;
+                p.bn = 64;
+                p.wm = 3;
+                p.pf = pf;
+                p.splitk = splitk;
+                add(p);
+            }
     }
     return out;
 }
@@ -989,7 +1010,7 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     {
         const TiledShape t = tiled_of(p);
         snprintf(buf, len, "%s<%d, %d, %d, %d, %d, %d>", t.wk == 2 ? "tiled_k2_kernel" : "tiled_kernel", t.bm, t.bn,
-                 t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf);
+                 t.wm, t.wm == 8 ? 8 : t.wm == 3 ? 3 : 4, t.wpf, t.xpf);
     }
     return ok();
 }

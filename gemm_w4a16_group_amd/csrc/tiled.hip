@@ -12,8 +12,9 @@
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
 // reads them back conflict-free.
 //
-// tiled_kernel: a workgroup of NWV waves (four, or eight for 512-row tiles)
-// owns a BM x BN tile of C and walks K one group (128 k) per stage.  The
+// tiled_kernel: a workgroup of NWV waves (four, eight for 512-row tiles,
+// three for 96-row ones) owns a BM x BN tile of C and walks K one group
+// (128 k) per stage.  The
 // waves form a WGM x (NWV / WGM) grid.  tiled_k2_kernel doubles the
 // workgroup into two such grids along K: at stage p the first takes group
 // 2p, the second group 2p + 1 of the split's run, both behind the same
@@ -103,7 +104,9 @@ __global__ void __launch_bounds__(256) xpack_silu_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// NWV waves per workgroup (4 or 8) in a WGM x (NWV / WGM) grid.  Weights are
+// NWV waves per workgroup (4, 8, or 3 for 96 x 64 tiles, whose 16 activation
+// copies per stage fall six to a wave with the last two repeated) in a
+// WGM x (NWV / WGM) grid.  Weights are
 // loaded WPF stages ahead into WPF + 1 register sets; activation chunks XPF
 // stages ahead into a ring of XPF + 1 LDS buffers.  Every stage issues its
 // activation loads, then its weight loads, and ends by waiting for exactly
@@ -153,7 +156,8 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     constexpr int RBW = WM / 32;            // 32-row MFMA blocks per wave
     constexpr int CBW = WN / 32;            // 32-column MFMA blocks per wave
     constexpr int XBYTES = kStageRows * BN * 16;        // one stage of activation chunks
-    constexpr int XLOADS = kStageRows * BN / 64 / NWV;  // 1 KB buffer-to-LDS loads per wave and stage
+    constexpr int XTOT = kStageRows * BN / 64;          // 1 KB buffer-to-LDS loads per stage
+    constexpr int XLOADS = (XTOT + NWV - 1) / NWV;      // per wave (three waves: two copies repeat the last)
     constexpr int NSET = WPF + 1;                       // weight register sets
     constexpr int NXB = XPF + 1;                        // activation buffers
     constexpr int WLOADS = 4 * RBW;                     // weight, zero and scale loads per wave and stage
@@ -163,6 +167,7 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     // registers allow with the wave's accumulators at 32 or 64 per lane
     constexpr int BD = RBW * CBW <= 2 ? 4 : RBW * CBW <= 4 ? 2 : 1;
     static_assert(BN % 64 == 0 && XLOADS >= 1 && XLOADS % (BN / 64) == 0, "tile");
+    static_assert(XLOADS * NWV == XTOT || BN == 64, "uneven copies only with one column base");
     static_assert(WKS == 1 || WKS == 2, "waves along K");
     static_assert((WKS - 1) * NWV * SLOT * 4 <= tiled_lds_bytes(BN, XPF, WKS), "K-slice sums fit the ring");
     static_assert(WPF >= 1 && WPF <= 4 && XPF >= 1 && XPF <= 3, "prefetch distances");
@@ -260,7 +265,9 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
 #pragma unroll
         for (int i = 0; i < XLOADS; ++i) {
             // XLOADS is a multiple of NCB, so the column base depends on i only
-            const int chunk = 64 * (wave * XLOADS + i);
+            int idx = wave * XLOADS + i;
+            if constexpr (XLOADS * NWV != XTOT) idx = idx < XTOT ? idx : XTOT - 1;
+            const int chunk = 64 * idx;
             const int row = chunk / BN, cb = i % NCB;
             buffer_load_lds16(xres, buf + chunk * 16, xcoff[cb], row * xrow);
         }
@@ -596,6 +603,8 @@ hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t strea
 }  // namespace
 
 bool tiled_supported(const TiledShape& t) {
+    // three waves of 32 rows: 96 x 64 tiles, weights one or two stages ahead
+    if (t.wm == 3) return t.bm == 96 && t.bn == 64 && t.wk == 1 && (t.wpf == 1 || t.wpf == 2) && t.xpf == 1 && t.splitk >= 1;
     if (t.wm != 2 && t.wm != 4 && t.wm != 8) return false;
     if (t.wk != 1 && !(t.wk == 2 && tiled_k2_ok(t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf))) return false;
     if (!tiled_pipe_ok(t.bm, t.bn, t.wm, t.wm == 8 ? 8 : 4, t.wpf, t.xpf)) return false;
@@ -654,6 +663,10 @@ hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stre
     if (e != hipSuccess) return e;
     if (t.wm == 8) {
         if (t.bm == 512 && t.bn == 128) return launch_bmbn<512, 128, 8, 8>(a, t, stream);
+        return hipErrorInvalidValue;
+    }
+    if (t.wm == 3) {
+        if (t.bm == 96 && t.bn == 64) return launch_bmbn<96, 64, 3, 3>(a, t, stream);
         return hipErrorInvalidValue;
     }
     if (t.wm == 2) {

@@ -124,10 +124,12 @@ int w4a16_gemv(const uint32_t *q_packed, const void *scales,
  *            N > 4, 4 for N = 16, 2 for N = 32); plans beyond that, or whose
  *            staged activations exceed 160 KB of LDS, are rejected.
  *   tiled  : bm, bn = tile sizes (bm in {128, 256}, bn in {64, 128, 256},
- *            or bm = 512 with bn = 128 and wm = 8);
+ *            or bm = 512 with bn = 128 and wm = 8, or bm = 96 with
+ *            bn = 64 and wm = 3);
  *            wm = waves along rows: 4 (each wave owns bm/4 rows and all
- *            bn columns), 2 (2 x 2 waves, bn >= 128) or 8 (eight waves of
- *            64 rows, bm = 512); 0 means 4;
+ *            bn columns), 2 (2 x 2 waves, bn >= 128), 8 (eight waves of
+ *            64 rows, bm = 512) or 3 (three waves of 32 rows, bm = 96,
+ *            pf <= 2, xpf <= 1, wk = 1); 0 means 4;
  *            pf = stages (groups of 128 k) of weights a wave loads ahead:
  *            0 or 1 (one) or 2 (two; not with wm = 2); xpf = stages of
  *            activations staged ahead: 0 or 1 (one); deeper pipelines,

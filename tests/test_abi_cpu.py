@@ -111,6 +111,10 @@ def test_plan_checks(lib):
     assert gp(kernel=2, bm=128, bn=64, splitk=9) == UNSUPPORTED             # > 8 groups
     assert gp(kernel=2, bm=128, bn=64, splitk=1, wm=2) == UNSUPPORTED       # 2 x 2 needs bn >= 128
     assert gp(kernel=2, bm=128, bn=128, splitk=1, wm=3) == UNSUPPORTED
+    assert gp(kernel=2, bm=96, bn=64, splitk=1, wm=3, pf=2) == WORKSPACE      # three waves of 32 rows
+    assert gp(kernel=2, bm=96, bn=128, splitk=1, wm=3) == UNSUPPORTED       # 96 rows: 64 columns only
+    assert gp(kernel=2, bm=96, bn=64, splitk=1, wm=4) == UNSUPPORTED
+    assert gp(kernel=2, bm=96, bn=64, splitk=1, wm=3, pf=4, xpf=2) == UNSUPPORTED
     assert gp(kernel=2, bm=512, bn=128, splitk=1, wm=8) == WORKSPACE        # valid eight-wave plan
     assert gp(kernel=2, bm=512, bn=128, splitk=1, wm=8, pf=2) == WORKSPACE
     assert gp(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=2) == WORKSPACE
@@ -200,6 +204,10 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"
     assert B.kernel_name(12288, 2048, 4096) == "tiled_kernel<256, 128, 4, 4, 1, 1>"
     assert B.kernel_name(12288, 512, 4096) == "tiled_kernel<128, 128, 4, 4, 1, 1>"
+    # 96-row tiles of three waves where 128-row ones leave CUs idle
+    assert B.kernel_name(12288, 64, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
+    assert B.kernel_name(11008, 128, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
+    assert B.kernel_name(4096, 64, 11008) == "tiled_kernel<128, 64, 4, 4, 2, 1>"
     # long K below N = 1024: 128-column tiles split along K
     assert B.kernel_name(4096, 384, 11008) == "tiled_kernel<128, 128, 4, 4, 2, 1>"
     assert B.kernel_name(4096, 384, 4096) == "tiled_kernel<128, 64, 4, 4, 2, 1>"

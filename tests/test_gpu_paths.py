@@ -119,6 +119,12 @@ TILED_DEEP = [
     (257, 1152, 264, 128, 64, 3, 4, 2),
     (520, 896, 520, 256, 256, 1, 4, 2),
     (64, 11008, 65, 512, 128, 1, 8, 2),
+    # 96-row tiles of three waves: ragged M and N, uneven splits, K = 11008
+    (1, 128, 65, 96, 64, 1, 3, 1),
+    (97, 384, 100, 96, 64, 1, 3, 2),
+    (300, 1152, 64, 96, 64, 3, 3, 2),
+    (193, 11008, 48, 96, 64, 2, 3, 2),
+    (1000, 4096, 128, 96, 64, 2, 3, 1),
 ]
 
 

@@ -91,6 +91,9 @@ EXPLICIT = [
     ("tiled_256x64_p22_split3", _mk(kernel=TI, bm=256, bn=64, wm=4, pf=2, xpf=2, splitk=3), 4096, 72, KN),
     ("tiled_128x64_p43_k11008", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=3, splitk=3), 11008, 64, KN),
     ("tiled_128x64_p42_token", _mk(kernel=TI, bm=128, bn=64, wm=4, pf=4, xpf=2, splitk=2), 4096, 64, TOK),
+    ("tiled_96x64_w3_pf2_split2", _mk(kernel=TI, bm=96, bn=64, wm=3, pf=2, splitk=2), 4096, 64, KN),
+    ("tiled_96x64_w3_pf1_k11008", _mk(kernel=TI, bm=96, bn=64, wm=3, pf=1, splitk=3), 11008, 48, KN),
+    ("tiled_96x64_w3_token", _mk(kernel=TI, bm=96, bn=64, wm=3, pf=2, splitk=1), 4096, 72, TOK),
     ("tiled_k2_128x64_split2", _mk(kernel=TI, bm=128, bn=64, wm=4, wk=2, pf=2, splitk=2), 4096, 64, KN),
     ("tiled_k2_128x64_odd_k11008", _mk(kernel=TI, bm=128, bn=64, wm=4, wk=2, pf=2, splitk=1), 11008, 100, KN),
     ("tiled_k2_128x128_split3", _mk(kernel=TI, bm=128, bn=128, wm=4, wk=2, pf=1, splitk=3), 4096, 136, KN),
