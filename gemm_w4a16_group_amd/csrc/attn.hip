@@ -13,7 +13,7 @@
 // The step stores fp16(rope(k, p)) and fp16(v) at position p and attends
 // over keys 0 .. p.  D = 128.
 //
-// HBM-bound on the cache: 2 * 2 D bytes per key.  Grid (splits, H, B): a
+// HBM-bound on the cache: 2 * 2 D bytes per key.  Grid (H, B, splits): a
 // workgroup of four waves takes 4 * KPW consecutive keys of one head (flash-
 // decoding split along the keys, so that one sequence fills the chip); each
 // wave KPW keys in rounds of 8: lane (key slot lane / 8, channel block
@@ -28,7 +28,14 @@
 // arrival counter in the workspace, compared with the number of such
 // splits) merges them in split order, with all of the merge's loads in
 // flight at once; workgroups past p leave without taking part, so a graph
-// captured for a large max_len pays little for the unused part of it.
+// captured for a large max_len pays little for the unused part of it.  The
+// split is the slowest grid dimension: workgroups are dispatched in grid
+// order, so every sequence's early (live) splits go out before the late
+// ones that short sequences leave empty.  With the split fastest, those
+// empty workgroups sat between live ones holding CU slots while their one
+// load (the position) waited behind the live ones' cache stream: eight
+// 361-key sequences took 44.5 us with max_len = 2022 against 16.5 us with
+// max_len = 361.
 //
 // Angles: theta_i = theta_1^i from theta_1 = base^(-2/D) (double, from the
 // host), p * theta_i in double, reduced modulo 2 pi in double (two-part
@@ -63,7 +70,7 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     constexpr int R = KPW / 8;   // rounds of 8 keys per wave
     constexpr int D = kHeadDim;
     constexpr int NT = 64 * W;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int part = lane & 7, kslot = lane >> 3;
     const int H = a.H;
@@ -227,7 +234,7 @@ __global__ void __launch_bounds__(64 * W) decode_attn_kernel(AttnArgs a) {
     }
 
     uint16_t* outp = a.out + (int64_t)b * H * D + (int64_t)h * D;
-    const int splits = gridDim.x;
+    const int splits = gridDim.z;
     if (splits == 1) {
         // an invalid position leaves L = 0: the output is NaN
         if (tid < D) outp[tid] = (uint16_t)f32_to_h16_bits(O / L);
@@ -372,7 +379,7 @@ hipError_t launch_attn_w(const AttnArgs& a, int waves, const dim3& grid, hipStre
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, const AttnShape& sh, hipStream_t stream) {
-    const dim3 grid((unsigned)attn_splits(a, sh), (unsigned)a.H, (unsigned)a.B);
+    const dim3 grid((unsigned)a.H, (unsigned)a.B, (unsigned)attn_splits(a, sh));
     if (sh.kpw == 16 && sh.waves == 16) return launch_attn_t<16, 16>(a, grid, stream);
     switch (sh.kpw) {
         case 16: return launch_attn_w<16>(a, sh.waves, grid, stream);
