@@ -266,18 +266,18 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     p.wm = 4;
     if (N < 1024) {
         // Few columns: 128-row tiles, as many workgroups as CUs or a little
-        // fewer.  128-column tiles when they alone give 192 or more, with two
+        // fewer.  128-column tiles when they alone give 160 or more, with two
         // K slices while that is one workgroup per CU (12288x4096 N = 192 /
-        // 256: 43.3 / 45.2 -> 40.2 / 41.4 us); else 64-column tiles, weights
-        // two stages ahead, split along K up to 256 workgroups while every
-        // split keeps 16 groups (4096x4096 N = 256 / 512: 44.6 / 46.4 ->
-        // 24.8 / 32.4 us; 4096x11008 N = 64 / 256: 41.0 / 64.9 -> 35.2 /
-        // 45.5 us).
+        // 256: 43.3 / 45.2 -> 40.2 / 41.4 us; 22016x4096 N = 128, 172
+        // tiles: 50.0 -> 41.6 us); else 64-column tiles, weights two stages
+        // ahead, split along K up to 256 workgroups while every split keeps
+        // 8 groups (4096x4096 N = 128: 20.4 -> 17.2 us at four splits;
+        // 4096x11008 N = 64: 26.8 -> 21.6 us at eight).
         const int64_t tm = (M + 127) / 128;
         const int64_t t128 = tm * ((N + 127) / 128), t64 = tm * ((N + 63) / 64);
         p.bm = 128;
         p.splitk = 1;
-        if (t128 >= 192) {
+        if (t128 >= 160) {
             p.bn = 128;
             if (t128 <= kCus) p.wk = 2;
         } else if (t128 >= 96 && G >= 64 && t128 <= kCounterSlots) {
@@ -291,7 +291,7 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
             p.bn = 64;
             p.pf = 2;
             if (t64 <= kCounterSlots)
-                while (p.splitk < 4 && t64 * (p.splitk + 1) <= kCus && G / (p.splitk + 1) >= 16) ++p.splitk;
+                while (p.splitk < 8 && t64 * (p.splitk + 1) <= kCus && G / (p.splitk + 1) >= 8) ++p.splitk;
             // 96-row tiles of three waves where 128-row ones leave a fifth
             // of the CUs idle and these nearly fill them (12288x4096 N = 48
             // / 64 / 128: 21.7 / 21.2 / 28.7 -> 20.3 / 20.3 / 27.6 us;

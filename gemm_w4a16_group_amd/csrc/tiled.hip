@@ -25,6 +25,8 @@
 // block and stage, one or two stages ahead) and dequantizes them there, one
 // MFMA step ahead, to fp16 (q - z) * s: one fp16 rounding per weight, q - z
 // being exact before the scale is applied.  fp32 accumulation throughout.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -459,10 +461,11 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     // ---- split-K: every split stores its fp32 partial tile; the last
     // workgroup of a tile to arrive adds them in split order, its own from
     // its registers, and stores C.  A partial tile is kept in the waves'
-    // register layout ([wave][block][element][lane], 256 contiguous bytes
-    // per element and wave, a private slot per split and tile), so that
-    // every access is one coalesced store or load, no lane needs a mask, and
-    // a split's loads are all in flight at once.
+    // register layout ([wave][block][element quad][lane], 1 KB contiguous
+    // per quad and wave, a private slot per split and tile), so that every
+    // access is one coalesced 16-byte-per-lane store or load and no lane
+    // needs a mask (4-byte accesses, four times as many, made the merge
+    // of a 4-way split take 10 us).
     // Every thread waits until its partial stores have completed, the
     // workgroup meets, and one thread adds one to the tile's counter
     // (relaxed, agent scope); the barrier after it puts the last arriver's
@@ -481,7 +484,8 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     auto slot_off = [&](int s, int rb, int cb) {     // uniform byte offset of a block
         return (int)(((((int64_t)s * T + tile_id) * NWV + wave) * SLOT + (rb * CBW + cb) * 16 * 64) * 4);
     };
-    const int lo = lane * 4;
+    // within a block, elements 4 j .. 4 j + 3 of lane l at byte 1024 j + 16 l
+    const int lo = lane * 16;
     if (holder) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
@@ -489,8 +493,11 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
             for (int cb = 0; cb < CBW; ++cb) {
                 const int so = slot_off(sidx, rb, cb);
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(f32_bits(acc[rb][cb][e]), pres, lo + e * 256, so, kAgent);
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{f32_bits(acc[rb][cb][4 * j]), f32_bits(acc[rb][cb][4 * j + 1]),
+                              f32_bits(acc[rb][cb][4 * j + 2]), f32_bits(acc[rb][cb][4 * j + 3])},
+                        pres, lo + j * 1024, so, kAgent);
             }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
@@ -508,27 +515,75 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     if (!flag || !holder) return;
     // the sum runs in split order, (p_0 + ... + p_(sidx-1)) + own +
     // p_(sidx+1) + ..., the order of a plain left-to-right sum whichever
-    // split arrives last
+    // split arrives last.  The partials of KQ splits for BG blocks are
+    // loaded together before any is added (one round trip to memory per
+    // split and block, taken one after another, made the merge slow).
     auto load_part = [&](int s, int rb, int cb) {
         const int so = slot_off(s, rb, cb);
         floatx16 p;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            p[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pres, lo + e * 256, so, kAgent));
+        for (int j = 0; j < 4; ++j) {
+            // (the whole vector is reinterpreted: this compiler turns a
+            // bit_cast of one element of a loaded vector into a load of
+            // element 0 alone)
+            const floatx4 f =
+                __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(pres, lo + j * 1024, so, kAgent));
+            p[4 * j] = f[0];
+            p[4 * j + 1] = f[1];
+            p[4 * j + 2] = f[2];
+            p[4 * j + 3] = f[3];
+        }
         return p;
     };
+    constexpr int NB = RBW * CBW;                   // blocks per wave
+    // blocks merged together and the most splits loaded together: eight
+    // loads in flight for up to two blocks per wave, four for four; tiles
+    // with more blocks keep one at a time (their sums fill the registers)
+    constexpr int BG = NB <= 4 && NB % 2 == 0 ? 2 : 1;
+    constexpr int KQ = NB >= 8 ? 1 : NB >= 4 ? 2 : 4;
+    // the other splits, o = 0 .. splitk - 2, in order: split o, or o + 1
+    // from this split's own index on
+    const int n_other = splitk - 1;
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < CBW; ++cb) {
-            if (sidx > 0) {
-                floatx16 pre = load_part(0, rb, cb);
-                for (int s = 1; s < sidx; ++s) pre += load_part(s, rb, cb);
-                acc[rb][cb] = pre + acc[rb][cb];
+    for (int b0 = 0; b0 < NB; b0 += BG) {
+        floatx16 pre[BG];
+        auto add = [&](int s, int g, const floatx16& v) {
+            floatx16& ac = acc[(b0 + g) / CBW][(b0 + g) % CBW];
+            if (s < sidx) {
+                pre[g] = s == 0 ? v : pre[g] + v;
+                if (s == sidx - 1) ac = pre[g] + ac;
+            } else {
+                ac += v;
             }
-            for (int s = sidx + 1; s < splitk; ++s) acc[rb][cb] += load_part(s, rb, cb);
-            store_c(rb, cb, acc[rb][cb]);
+        };
+        // C consecutive other splits from o0 on: all loads, then the adds
+        auto piece = [&](auto count, int o0) {
+            constexpr int C = decltype(count)::value;
+            floatx16 buf[C][BG];
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const int s = o0 + i < sidx ? o0 + i : o0 + i + 1;
+#pragma unroll
+                for (int g = 0; g < BG; ++g) buf[i][g] = load_part(s, (b0 + g) / CBW, (b0 + g) % CBW);
+            }
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const int s = o0 + i < sidx ? o0 + i : o0 + i + 1;
+#pragma unroll
+                for (int g = 0; g < BG; ++g) add(s, g, buf[i][g]);
+            }
+        };
+        int o = 0;
+        if constexpr (KQ >= 4) {
+            for (; o + 4 <= n_other; o += 4) piece(std::integral_constant<int, 4>{}, o);
+            if (o + 3 == n_other) piece(std::integral_constant<int, 3>{}, o), o += 3;
         }
+        if constexpr (KQ >= 2)
+            for (; o + 2 <= n_other; o += 2) piece(std::integral_constant<int, 2>{}, o);
+        for (; o < n_other; ++o) piece(std::integral_constant<int, 1>{}, o);
+#pragma unroll
+        for (int g = 0; g < BG; ++g) store_c((b0 + g) / CBW, (b0 + g) % CBW, acc[(b0 + g) / CBW][(b0 + g) % CBW]);
+    }
 }
 
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>

@@ -171,6 +171,23 @@ def test_default_plans_are_valid(lib):
                 assert st == WORKSPACE, (M, N, K, p.as_dict(), lib.w4a16_last_error())
 
 
+def test_default_split_fills_the_cus(lib):
+    # 64-column tiles are split along K up to 256 workgroups while every
+    # split keeps 8 groups of 128 k
+    def plan(M, N, K):
+        p = B.Plan()
+        assert lib.w4a16_plan_default(M, N, K, 128, ctypes.byref(p)) == OK
+        return p
+    p = plan(4096, 64, 11008)           # 32 tiles, 86 groups
+    assert (p.kernel, p.bm, p.bn, p.splitk) == (2, 128, 64, 8)
+    p = plan(4096, 128, 4096)           # 64 tiles, 32 groups
+    assert (p.kernel, p.bm, p.bn, p.splitk) == (2, 128, 64, 4)
+    p = plan(2048, 128, 4096)           # 32 tiles: 8 groups per split stops it at 4
+    assert (p.kernel, p.bm, p.bn, p.splitk) == (2, 128, 64, 4)
+    p = plan(12288, 64, 4096)           # 96-row tiles, two splits
+    assert (p.kernel, p.bm, p.wm, p.splitk) == (2, 96, 3, 2)
+
+
 def test_gemv_checks(lib):
     assert lib.w4a16_gemv(Q, S, Z, X, C, 64, 256, 32, NULL) == UNSUPPORTED
     assert lib.w4a16_gemv(Q, S, Z, NULL, C, 64, 256, 128, NULL) == INVALID
@@ -208,6 +225,8 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 64, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(11008, 128, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(4096, 64, 11008) == "tiled_kernel<128, 64, 4, 4, 2, 1>"
+    # two K slices of 128 x 128 tiles from 160 tiles on (22016 rows, N = 128)
+    assert B.kernel_name(22016, 128, 4096) == "tiled_k2_kernel<128, 128, 4, 4, 1, 1>"
     # long K below N = 1024: 128-column tiles split along K
     assert B.kernel_name(4096, 384, 11008) == "tiled_kernel<128, 128, 4, 4, 2, 1>"
     assert B.kernel_name(4096, 384, 4096) == "tiled_kernel<128, 64, 4, 4, 2, 1>"
