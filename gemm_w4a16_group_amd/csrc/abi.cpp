@@ -1009,8 +1009,10 @@ int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size, const
     else
     {
         const TiledShape t = tiled_of(p);
-        snprintf(buf, len, "%s<%d, %d, %d, %d, %d, %d>", t.wk == 2 ? "tiled_k2_kernel" : "tiled_kernel", t.bm, t.bn,
-                 t.wm, t.wm == 8 ? 8 : t.wm == 3 ? 3 : 4, t.wpf, t.xpf);
+        const bool dx = tiled_direct_x(a, t);
+        snprintf(buf, len, "%s<%d, %d, %d, %d, %d, %d>",
+                 t.wk == 2 ? (dx ? "tiled_k2_dx_kernel" : "tiled_k2_kernel") : (dx ? "tiled_dx_kernel" : "tiled_kernel"),
+                 t.bm, t.bn, t.wm, t.wm == 8 ? 8 : t.wm == 3 ? 3 : 4, t.wpf, t.xpf);
     }
     return ok();
 }

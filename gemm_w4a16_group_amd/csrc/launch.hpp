@@ -93,6 +93,8 @@ size_t narrow_lds_bytes(const GemmArgs& a, const NarrowShape& s);
 // true when the narrow kernel stages the activations straight from x ([K, N],
 // N a multiple of 8), with no re-layout launch before it
 bool narrow_direct_x(const GemmArgs& a);
+// the tiled plan reads X [K, N] in place (no xpack_col launch)
+bool tiled_direct_x(const GemmArgs& a, const TiledShape& t);
 hipError_t launch_narrow(const GemmArgs& a, const NarrowShape& s, hipStream_t stream);
 
 // X [K, N] -> 16-byte chunks [K/8][N] in a.xp (the tiled and narrow kernels' B/A operand layout)

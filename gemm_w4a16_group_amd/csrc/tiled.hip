@@ -10,7 +10,11 @@
 // the chunks itself).  The chunks are exactly the B operand of
 // v_mfma_f32_32x32x16_f16, so the GEMM stages them into LDS with
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
-// reads them back conflict-free.
+// reads them back conflict-free.  The 64-column tiles of the few-column
+// calls (96 x 64, 128 x 64) read [K, N] activations in place instead when
+// N is a multiple of 8 (tiled_dx_kernel, tiled_k2_dx_kernel): each k-octet's
+// eight rows are copied into LDS in the dequant order and two transposing
+// LDS reads give a lane its B fragment, with no second launch.
 //
 // tiled_kernel: a workgroup of NWV waves (four, eight for 512-row tiles,
 // three for 96-row ones) owns a BM x BN tile of C and walks K one group
@@ -35,6 +39,8 @@ namespace w4a16 {
 namespace {
 
 constexpr int kStageRows = kGroup / 8;   // k-octets per stage
+
+typedef short short4v __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // X [K, N] -> chunks [K/8][N] of 16 bytes: one thread per chunk (ko, n),
@@ -150,7 +156,7 @@ __host__ __device__ constexpr bool tiled_k2_ok(int BM, int BN, int WGM, int NWV,
     return NWV == 4 && WGM == 4 && BM == 128 && BN <= 128 && XPF == 1 && WPF <= 2;
 }
 
-template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS>
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS, bool DX = false>
 __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     constexpr int WGN = NWV / WGM;          // waves along N
     constexpr int WM = BM / WGM;            // rows per wave
@@ -260,10 +266,44 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
             sS[set][rb] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rb], g * 2, 0);
         }
     };
+    // X read in place ([K, N] rows, N a multiple of 8; DX): the stage's
+    // octet o (k rows 8 o .. 8 o + 7 of the group) holds its eight rows of
+    // the tile's BN columns in dequant order (k offsets 0, 4, 1, 5, 2, 6, 3,
+    // 7), [row][column] halves, so that two transposing reads of four rows
+    // give a lane one column's eight k in the order the chunks hold them.
+    // Copy i of an octet fills its bytes [1024 i, 1024 i + 1024): lane l
+    // takes 16-byte piece q = 64 i + l, row q / (BN / 8), columns
+    // col0 + 8 (q % (BN / 8)) .. + 7 (pieces past N re-read the row's last).
+    constexpr int XPO = BN / 64;    // copies per octet
+    int dxoff[XPO];
+    if constexpr (DX) {
+        const int n8 = (int)(N >> 3);
+#pragma unroll
+        for (int i = 0; i < XPO; ++i) {
+            const int q = 64 * i + lane;
+            const int pr = q / (BN / 8), cc = q % (BN / 8);
+            const int r = (pr >> 1) + 4 * (pr & 1);
+            int c8 = (int)(col0 >> 3) + cc;
+            c8 = c8 < n8 ? c8 : n8 - 1;
+            dxoff[i] = (int)((r * N + 8 * (int64_t)c8) * 2);
+        }
+    }
     // stage p's chunks go to buffer p % NXB of the wave's K slice
     auto load_x = [&](int g, int slot) {
-        const i32x4 xres = raw_rsrc(a.xp + (int64_t)g * kStageRows * N * 8, (int64_t)kStageRows * N * 16);
         unsigned char* buf = xs + (slot * WKS + wave_k) * XBYTES;
+        if constexpr (DX) {
+            const i32x4 xres = raw_rsrc(a.x + (int64_t)g * 128 * N, (int64_t)128 * N * 2);
+#pragma unroll
+            for (int i = 0; i < XLOADS; ++i) {
+                int idx = wave * XLOADS + i;
+                if constexpr (XLOADS * NWV != XTOT) idx = idx < XTOT ? idx : XTOT - 1;
+                // copy idx: octet idx / XPO, part idx % XPO (XLOADS is a
+                // multiple of XPO, so the part depends on i only)
+                buffer_load_lds16(xres, buf + idx * 1024, dxoff[i % XPO], (idx / XPO) * 8 * (int)N * 2);
+            }
+            return;
+        }
+        const i32x4 xres = raw_rsrc(a.xp + (int64_t)g * kStageRows * N * 8, (int64_t)kStageRows * N * 16);
 #pragma unroll
         for (int i = 0; i < XLOADS; ++i) {
             // XLOADS is a multiple of NCB, so the column base depends on i only
@@ -289,6 +329,12 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     // B fragment of lane (l32, hh), block cb, MFMA step t: chunk row 8 hh + t,
     // column WN wave_n + 32 cb + l32 -> one base plus an immediate offset
     const int bbase = ((8 * hh) * BN + WN * wave_n + l32) * 16;
+    // DX: lanes 4 j .. 4 j + 3 of a 16-lane group read row 4 h + j of the
+    // octet, columns base + 4 (lane % 4) ..; the transpose hands lane i of
+    // the group column base + i of the four rows (the second 16 lanes of a
+    // half-wave take the block's columns 16 .. 31)
+    const int dxbase = ((8 * hh) * 8 * BN + ((lane & 15) >> 2) * BN + WN * wave_n + 16 * ((lane >> 4) & 1) +
+                        4 * (lane & 3)) * 2;
     const int last = st1 - 1;
     auto clamp_g = [&](int g) { return g < st1 ? g : last; };
 
@@ -311,7 +357,7 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) dq[rb].set((zS[set][rb] >> (4 * (g & 7))) & 0xFu, sS[set][rb]);
 
-            const unsigned char* xb = xs + ((p % NXB) * WKS + wave_k) * XBYTES + bbase;
+            const unsigned char* xb = xs + ((p % NXB) * WKS + wave_k) * XBYTES + (DX ? dxbase : bbase);
             // A operand of MFMA step t: word t of the lane's eight (k-octet
             // 8 hh + t), dequantized one step ahead.  B fragments are read
             // BD steps ahead: one step of MFMA work is shorter than an LDS
@@ -320,8 +366,18 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
             half8 afrag[2][RBW], bfrag[BD + 1][CBW];
             auto read_b = [&](int t, half8* bf) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; ++cb)
-                    bf[cb] = *reinterpret_cast<const half8*>(xb + (t * BN + cb * 32) * 16);
+                for (int cb = 0; cb < CBW; ++cb) {
+                    if constexpr (DX) {
+                        const unsigned char* b = xb + (t * 8 * BN + cb * 32) * 2;
+                        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) short4v*)(b));
+                        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) short4v*)(b + 4 * BN * 2));
+                        bf[cb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    } else {
+                        bf[cb] = *reinterpret_cast<const half8*>(xb + (t * BN + cb * 32) * 16);
+                    }
+                }
             };
             auto make_a = [&](int t, half8* af) {
 #pragma unroll
@@ -600,17 +656,47 @@ tiled_k2_kernel(GemmArgs a, int splitk) {
     tiled_body<BM, BN, WGM, NWV, WPF, XPF, 2>(a, splitk);
 }
 
-template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS>
+// The same two kernels reading X [K, N] in place (no xpack_col launch),
+// built for the 64-column tiles of the few-column calls: 96 x 64 of three
+// waves and 128 x 64 of four, one stage of activations ahead.  Each B
+// fragment then takes two transposing LDS reads instead of one; with two
+// column blocks per wave that costs less than the launch it saves
+// (12288x4096 N = 64: 20.3 -> 17.8 us; 4096x4096 N = 128 / 512: 18.1 /
+// 33.3 -> 15.0 / 27.3 us), with four (128 x 128 tiles) it cost more
+// (N = 512: 65.6 -> 75.4 us).
+__host__ __device__ constexpr bool tiled_dx_built(int BM, int BN, int WGM, int NWV, int WPF, int XPF) {
+    return XPF == 1 && WPF <= 2 && WGM == NWV && BN == 64 &&
+           ((BM == 96 && NWV == 3) || (BM == 128 && NWV == 4));
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+__global__ void __launch_bounds__(64 * NWV)
+__attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd(BM, BN, WGM, NWV))))
+tiled_dx_kernel(GemmArgs a, int splitk) {
+    tiled_body<BM, BN, WGM, NWV, WPF, XPF, 1, true>(a, splitk);
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
+__global__ void __launch_bounds__(128 * NWV) __attribute__((amdgpu_waves_per_eu(2)))
+tiled_k2_dx_kernel(GemmArgs a, int splitk) {
+    tiled_body<BM, BN, WGM, NWV, WPF, XPF, 2, true>(a, splitk);
+}
+
+template <int BM, int BN, int WGM, int NWV, int WPF, int XPF, int WKS, bool DX>
 hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const dim3 grid((unsigned)tiles, (unsigned)t.splitk);
     constexpr int lds = tiled_lds_bytes(BN, XPF, WKS);
+    const void* fn;
+    if constexpr (WKS == 1 && DX)
+        fn = reinterpret_cast<const void*>(&tiled_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+    else if constexpr (WKS == 1)
+        fn = reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+    else if constexpr (DX)
+        fn = reinterpret_cast<const void*>(&tiled_k2_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+    else
+        fn = reinterpret_cast<const void*>(&tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>);
     if constexpr (lds > 65536) {
-        const void* fn;
-        if constexpr (WKS == 1)
-            fn = reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>);
-        else
-            fn = reinterpret_cast<const void*>(&tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>);
         // dynamic LDS above 64 KB must be allowed per kernel, once
         static const hipError_t ok = [fn] {
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -619,12 +705,19 @@ hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream
         }();
         if (ok != hipSuccess) return ok;
     }
-    if constexpr (WKS == 1)
+    if constexpr (WKS == 1 && DX)
+        hipLaunchKernelGGL((tiled_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(64 * NWV), lds, stream, a,
+                           t.splitk);
+    else if constexpr (WKS == 1)
         hipLaunchKernelGGL((tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(64 * NWV), lds, stream, a,
                            t.splitk);
+    else if constexpr (DX)
+        hipLaunchKernelGGL((tiled_k2_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(128 * NWV), lds, stream,
+                           a, t.splitk);
     else
         hipLaunchKernelGGL((tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(128 * NWV), lds, stream, a,
                            t.splitk);
+    (void)fn;
     return hipGetLastError();
 }
 
@@ -632,25 +725,34 @@ hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream
 // two stages of weights and one of activations for every tile, deeper
 // pipelines for the tiles of four waves that the few-column calls use.
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
-hipError_t launch_if(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
+hipError_t launch_if(const GemmArgs& a, const TiledShape& t, bool dx, hipStream_t stream) {
     if constexpr (tiled_pipe_ok(BM, BN, WGM, NWV, WPF, XPF)) {
+        if constexpr (tiled_dx_built(BM, BN, WGM, NWV, WPF, XPF)) {
+            if (dx) {
+                if constexpr (tiled_k2_ok(BM, BN, WGM, NWV, WPF, XPF))
+                    if (t.wk == 2) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 2, true>(a, t, stream);
+                if (t.wk == 1) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 1, true>(a, t, stream);
+                return hipErrorInvalidValue;
+            }
+        }
+        if (dx) return hipErrorInvalidValue;
         if constexpr (tiled_k2_ok(BM, BN, WGM, NWV, WPF, XPF))
-            if (t.wk == 2) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 2>(a, t, stream);
-        if (t.wk == 1) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 1>(a, t, stream);
+            if (t.wk == 2) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 2, false>(a, t, stream);
+        if (t.wk == 1) return launch_one<BM, BN, WGM, NWV, WPF, XPF, 1, false>(a, t, stream);
     }
     return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WGM = 4, int NWV = 4>
-hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
+hipError_t launch_bmbn(const GemmArgs& a, const TiledShape& t, bool dx, hipStream_t stream) {
     switch (t.wpf * 10 + t.xpf) {
-        case 11: return launch_if<BM, BN, WGM, NWV, 1, 1>(a, t, stream);
-        case 21: return launch_if<BM, BN, WGM, NWV, 2, 1>(a, t, stream);
-        case 22: return launch_if<BM, BN, WGM, NWV, 2, 2>(a, t, stream);
-        case 32: return launch_if<BM, BN, WGM, NWV, 3, 2>(a, t, stream);
-        case 42: return launch_if<BM, BN, WGM, NWV, 4, 2>(a, t, stream);
-        case 33: return launch_if<BM, BN, WGM, NWV, 3, 3>(a, t, stream);
-        case 43: return launch_if<BM, BN, WGM, NWV, 4, 3>(a, t, stream);
+        case 11: return launch_if<BM, BN, WGM, NWV, 1, 1>(a, t, dx, stream);
+        case 21: return launch_if<BM, BN, WGM, NWV, 2, 1>(a, t, dx, stream);
+        case 22: return launch_if<BM, BN, WGM, NWV, 2, 2>(a, t, dx, stream);
+        case 32: return launch_if<BM, BN, WGM, NWV, 3, 2>(a, t, dx, stream);
+        case 42: return launch_if<BM, BN, WGM, NWV, 4, 2>(a, t, dx, stream);
+        case 33: return launch_if<BM, BN, WGM, NWV, 3, 3>(a, t, dx, stream);
+        case 43: return launch_if<BM, BN, WGM, NWV, 4, 3>(a, t, dx, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -713,30 +815,39 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+bool tiled_direct_x(const GemmArgs& a, const TiledShape& t) {
+    if (a.tm || a.xp_ready || a.act || a.N % 8 != 0 || a.N > 65536) return false;
+    if (t.xpf != 1 || t.wpf > 2) return false;
+    return t.bn == 64 && ((t.bm == 96 && t.wm == 3) || (t.bm == 128 && t.wm == 4));
+}
+
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {
-    hipError_t e = launch_xpack(a, stream);
-    if (e != hipSuccess) return e;
+    const bool dx = tiled_direct_x(a, t);
+    if (!dx) {
+        const hipError_t e = launch_xpack(a, stream);
+        if (e != hipSuccess) return e;
+    }
     if (t.wm == 8) {
-        if (t.bm == 512 && t.bn == 128) return launch_bmbn<512, 128, 8, 8>(a, t, stream);
+        if (t.bm == 512 && t.bn == 128) return launch_bmbn<512, 128, 8, 8>(a, t, dx, stream);
         return hipErrorInvalidValue;
     }
     if (t.wm == 3) {
-        if (t.bm == 96 && t.bn == 64) return launch_bmbn<96, 64, 3, 3>(a, t, stream);
+        if (t.bm == 96 && t.bn == 64) return launch_bmbn<96, 64, 3, 3>(a, t, dx, stream);
         return hipErrorInvalidValue;
     }
     if (t.wm == 2) {
-        if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256, 2>(a, t, stream);
-        if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128, 2>(a, t, stream);
-        if (t.bm == 128 && t.bn == 256) return launch_bmbn<128, 256, 2>(a, t, stream);
-        if (t.bm == 128 && t.bn == 128) return launch_bmbn<128, 128, 2>(a, t, stream);
+        if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256, 2>(a, t, dx, stream);
+        if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128, 2>(a, t, dx, stream);
+        if (t.bm == 128 && t.bn == 256) return launch_bmbn<128, 256, 2>(a, t, dx, stream);
+        if (t.bm == 128 && t.bn == 128) return launch_bmbn<128, 128, 2>(a, t, dx, stream);
         return hipErrorInvalidValue;
     }
-    if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256>(a, t, stream);
-    if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128>(a, t, stream);
-    if (t.bm == 256 && t.bn == 64) return launch_bmbn<256, 64>(a, t, stream);
-    if (t.bm == 128 && t.bn == 256) return launch_bmbn<128, 256>(a, t, stream);
-    if (t.bm == 128 && t.bn == 128) return launch_bmbn<128, 128>(a, t, stream);
-    if (t.bm == 128 && t.bn == 64) return launch_bmbn<128, 64>(a, t, stream);
+    if (t.bm == 256 && t.bn == 256) return launch_bmbn<256, 256>(a, t, dx, stream);
+    if (t.bm == 256 && t.bn == 128) return launch_bmbn<256, 128>(a, t, dx, stream);
+    if (t.bm == 256 && t.bn == 64) return launch_bmbn<256, 64>(a, t, dx, stream);
+    if (t.bm == 128 && t.bn == 256) return launch_bmbn<128, 256>(a, t, dx, stream);
+    if (t.bm == 128 && t.bn == 128) return launch_bmbn<128, 128>(a, t, dx, stream);
+    if (t.bm == 128 && t.bn == 64) return launch_bmbn<128, 64>(a, t, dx, stream);
     return hipErrorInvalidValue;
 }
 

@@ -72,6 +72,17 @@ PLANS = [
     (520, 640, 520, dict(kernel=2, bm=512, bn=128, splitk=1, wm=8, pf=2)),
     (129, 384, 130, dict(kernel=2, bm=512, bn=128, splitk=2, wm=8, pf=2)),   # M % 4 != 0
     (300, 512, 100, dict(kernel=2, bm=256, bn=128, splitk=1, wm=4, pf=2)),
+    # [K, N] read in place (N a multiple of 8) against the chunk layout:
+    # ragged column tiles, splits, both K-slice forms, the 86-group tail
+    (100, 384, 72, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4)),
+    (77, 384, 8, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4, pf=2)),
+    (300, 1152, 136, dict(kernel=2, bm=96, bn=64, splitk=2, wm=3, pf=2)),
+    (97, 1152, 64, dict(kernel=2, bm=96, bn=64, splitk=3, wm=3, pf=1)),
+    (129, 4096, 64, dict(kernel=2, bm=128, bn=64, splitk=4, wm=4, pf=2)),
+    (257, 1152, 96, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4, wk=2, pf=1)),
+    (130, 1152, 200, dict(kernel=2, bm=128, bn=64, splitk=2, wm=4, wk=2, pf=2)),
+    (520, 640, 248, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4, pf=2)),
+    (64, 11008, 64, dict(kernel=2, bm=128, bn=64, splitk=2, wm=4, pf=2)),
 ]
 
 
