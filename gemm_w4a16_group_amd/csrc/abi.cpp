@@ -223,12 +223,26 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         p.rb = 1;
         p.wk = 1;
         const int64_t t64 = (M + 63) / 64;
+        auto fits64 = [&](const w4a16_plan& q) {
+            const std::string saved = g_err;
+            const int st = check_plan(a, q);
+            g_err = saved;
+            return st == W4A16_OK;
+        };
         for (int64_t splitk = 1; splitk <= G && t64 * splitk <= kCus; ++splitk) {
             p.splitk = (int32_t)splitk;
-            const std::string saved = g_err;
-            const int st = check_plan(a, p);
-            g_err = saved;
-            if (st == W4A16_OK) return p;
+            if (fits64(p)) {
+                // more splits, up to six, while the workgroups still fit
+                // the CUs (2048x4096 / 1024x4096 N = 64: 12.9 / 12.7 ->
+                // 12.1 / 12.0 us at six)
+                while (p.splitk < 6 && t64 * (p.splitk + 1) <= kCus && G / (p.splitk + 1) >= 4) {
+                    w4a16_plan q = p;
+                    q.splitk = p.splitk + 1;
+                    if (!fits64(q)) break;
+                    p = q;
+                }
+                return p;
+            }
         }
         memset(&p, 0, sizeof(p));
     }
@@ -266,7 +280,9 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
     p.wm = 4;
     if (N < 1024) {
         // Few columns: 128-row tiles, as many workgroups as CUs or a little
-        // fewer.  128-column tiles when they alone give 160 or more, with two
+        // fewer.  128-column tiles when N > 64 and they alone give 160 or more
+        // (at N <= 64 half of each would be empty: 22016x4096 N = 64 38.2
+        // against 25.7 us with 96 x 64 tiles), with two
         // K slices while that is one workgroup per CU (12288x4096 N = 192 /
         // 256: 43.3 / 45.2 -> 40.2 / 41.4 us; 22016x4096 N = 128, 172
         // tiles: 50.0 -> 41.6 us); else 64-column tiles, weights two stages
@@ -277,10 +293,10 @@ w4a16_plan default_plan(int64_t M, int64_t N, int64_t K, int32_t layout = W4A16_
         const int64_t t128 = tm * ((N + 127) / 128), t64 = tm * ((N + 63) / 64);
         p.bm = 128;
         p.splitk = 1;
-        if (t128 >= 160) {
+        if (N > 64 && t128 >= 160) {
             p.bn = 128;
             if (t128 <= kCus) p.wk = 2;
-        } else if (t128 >= 96 && G >= 64 && t128 <= kCounterSlots) {
+        } else if (N > 64 && t128 >= 96 && G >= 64 && t128 <= kCounterSlots) {
             // long K: 128-column tiles split along K to fill the CUs
             // (4096x11008 N = 384 / 512: 67.3 / 75.4 -> 61.2 / 67.8 us; at
             // K = 4096 the 64-column tiles stay ahead)

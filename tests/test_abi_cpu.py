@@ -229,8 +229,11 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(12288, 60, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(11008, 128, 4096) == "tiled_dx_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(4096, 64, 11008) == "tiled_dx_kernel<128, 64, 4, 4, 2, 1>"
-    # two K slices of 128 x 128 tiles from 160 tiles on (22016 rows, N = 128)
+    # two K slices of 128 x 128 tiles from 160 tiles on (22016 rows, N = 128),
+    # never at N <= 64 (half of each tile would be empty)
     assert B.kernel_name(22016, 128, 4096) == "tiled_k2_kernel<128, 128, 4, 4, 1, 1>"
+    assert B.kernel_name(22016, 64, 4096) == "tiled_dx_kernel<96, 64, 3, 3, 2, 1>"
+    assert B.kernel_name(24576, 64, 4096) != "tiled_k2_kernel<128, 128, 4, 4, 1, 1>"
     # long K below N = 1024: 128-column tiles split along K
     assert B.kernel_name(4096, 384, 11008) == "tiled_kernel<128, 128, 4, 4, 2, 1>"
     assert B.kernel_name(4096, 384, 4096) == "tiled_dx_kernel<128, 64, 4, 4, 2, 1>"
