@@ -10,11 +10,12 @@
 // the chunks itself).  The chunks are exactly the B operand of
 // v_mfma_f32_32x32x16_f16, so the GEMM stages them into LDS with
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
-// reads them back conflict-free.  The 64-column tiles of the few-column
-// calls (96 x 64, 128 x 64) read [K, N] activations in place instead when
-// N is a multiple of 8 (tiled_dx_kernel, tiled_k2_dx_kernel): each k-octet's
-// eight rows are copied into LDS in the dequant order and two transposing
-// LDS reads give a lane its B fragment, with no second launch.
+// reads them back conflict-free.  The tiles of the few-column calls (96 x
+// 64, 128 x 64, 128 x 128) read [K, N] activations in place instead when N
+// is a multiple of 8 (tiled_dx_kernel, tiled_k2_dx_kernel): each k-octet's
+// eight rows are copied into LDS in the dequant order (16-byte pieces
+// permuted per row against bank conflicts) and two transposing LDS reads
+// give a lane its B fragment, with no second launch.
 //
 // tiled_kernel: a workgroup of NWV waves (four, eight for 512-row tiles,
 // three for 96-row ones) owns a BM x BN tile of C and walks K one group
@@ -269,19 +270,23 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     // X read in place ([K, N] rows, N a multiple of 8; DX): the stage's
     // octet o (k rows 8 o .. 8 o + 7 of the group) holds its eight rows of
     // the tile's BN columns in dequant order (k offsets 0, 4, 1, 5, 2, 6, 3,
-    // 7), [row][column] halves, so that two transposing reads of four rows
-    // give a lane one column's eight k in the order the chunks hold them.
+    // 7), so that two transposing reads of four rows give a lane one
+    // column's eight k in the order the chunks hold them.  Row p keeps its
+    // 16-byte pieces (8 columns each) in slots permuted by an XOR with
+    // 4 dx_swz(p), so that the four rows a transposing read takes fall on
+    // distinct banks (without it their starts coincide: BN x 2 bytes apart).
     // Copy i of an octet fills its bytes [1024 i, 1024 i + 1024): lane l
-    // takes 16-byte piece q = 64 i + l, row q / (BN / 8), columns
-    // col0 + 8 (q % (BN / 8)) .. + 7 (pieces past N re-read the row's last).
+    // fills slot q = 64 i + l, row q / (BN / 8), with the row's piece
+    // (q % (BN / 8)) ^ 4 dx_swz(row) (pieces past N re-read the row's last).
     constexpr int XPO = BN / 64;    // copies per octet
+    auto dx_swz = [](int p) { return BN == 64 ? (p >> 1) & 1 : p & 3; };
     int dxoff[XPO];
     if constexpr (DX) {
         const int n8 = (int)(N >> 3);
 #pragma unroll
         for (int i = 0; i < XPO; ++i) {
             const int q = 64 * i + lane;
-            const int pr = q / (BN / 8), cc = q % (BN / 8);
+            const int pr = q / (BN / 8), cc = (q % (BN / 8)) ^ (4 * dx_swz(pr));
             const int r = (pr >> 1) + 4 * (pr & 1);
             int c8 = (int)(col0 >> 3) + cc;
             c8 = c8 < n8 ? c8 : n8 - 1;
@@ -332,9 +337,17 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
     // DX: lanes 4 j .. 4 j + 3 of a 16-lane group read row 4 h + j of the
     // octet, columns base + 4 (lane % 4) ..; the transpose hands lane i of
     // the group column base + i of the four rows (the second 16 lanes of a
-    // half-wave take the block's columns 16 .. 31)
-    const int dxbase = ((8 * hh) * 8 * BN + ((lane & 15) >> 2) * BN + WN * wave_n + 16 * ((lane >> 4) & 1) +
-                        4 * (lane & 3)) * 2;
+    // half-wave take the block's columns 16 .. 31).  Rows j and 4 + j share
+    // their piece permutation, so one column offset per block serves both
+    // reads.
+    const int dxj = (lane & 15) >> 2;
+    const int dxbase = ((8 * hh) * 8 * BN + dxj * BN) * 2;
+    int dxcol[CBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; ++cb) {
+        const int col = WN * wave_n + 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        dxcol[cb] = (((col >> 3) ^ (4 * dx_swz(dxj))) * 8 + (col & 7)) * 2;
+    }
     const int last = st1 - 1;
     auto clamp_g = [&](int g) { return g < st1 ? g : last; };
 
@@ -368,7 +381,7 @@ __device__ __forceinline__ void tiled_body(const GemmArgs& a, int splitk) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; ++cb) {
                     if constexpr (DX) {
-                        const unsigned char* b = xb + (t * 8 * BN + cb * 32) * 2;
+                        const unsigned char* b = xb + dxcol[cb] + t * 8 * BN * 2;
                         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) short4v*)(b));
                         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -657,16 +670,16 @@ tiled_k2_kernel(GemmArgs a, int splitk) {
 }
 
 // The same two kernels reading X [K, N] in place (no xpack_col launch),
-// built for the 64-column tiles of the few-column calls: 96 x 64 of three
-// waves and 128 x 64 of four, one stage of activations ahead.  Each B
-// fragment then takes two transposing LDS reads instead of one; with two
-// column blocks per wave that costs less than the launch it saves
-// (12288x4096 N = 64: 20.3 -> 17.8 us; 4096x4096 N = 128 / 512: 18.1 /
-// 33.3 -> 15.0 / 27.3 us), with four (128 x 128 tiles) it cost more
-// (N = 512: 65.6 -> 75.4 us).
+// built for the tiles of the few-column calls: 96 x 64 of three waves,
+// 128 x 64 and 128 x 128 of four, one stage of activations ahead.  Each B
+// fragment then takes two transposing LDS reads instead of one, which
+// costs less than the launch it saves once the rows' pieces are permuted
+// against bank conflicts (12288x4096 N = 64 / 256: 20.3 / 41.9 -> 17.6 /
+// 37.6 us; without the permutation the 128 x 128 tiles lost: N = 512
+// 65.6 -> 75.4 us).
 __host__ __device__ constexpr bool tiled_dx_built(int BM, int BN, int WGM, int NWV, int WPF, int XPF) {
-    return XPF == 1 && WPF <= 2 && WGM == NWV && BN == 64 &&
-           ((BM == 96 && NWV == 3) || (BM == 128 && NWV == 4));
+    return XPF == 1 && WPF <= 2 && WGM == NWV &&
+           ((BM == 96 && NWV == 3 && BN == 64) || (BM == 128 && NWV == 4 && (BN == 64 || BN == 128)));
 }
 
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
@@ -818,7 +831,7 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
 bool tiled_direct_x(const GemmArgs& a, const TiledShape& t) {
     if (a.tm || a.xp_ready || a.act || a.N % 8 != 0 || a.N > 65536) return false;
     if (t.xpf != 1 || t.wpf > 2) return false;
-    return t.bn == 64 && ((t.bm == 96 && t.wm == 3) || (t.bm == 128 && t.wm == 4));
+    return (t.bn == 64 && t.bm == 96 && t.wm == 3) || (t.bm == 128 && (t.bn == 64 || t.bn == 128) && t.wm == 4);
 }
 
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {

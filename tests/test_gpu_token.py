@@ -83,6 +83,9 @@ PLANS = [
     (130, 1152, 200, dict(kernel=2, bm=128, bn=64, splitk=2, wm=4, wk=2, pf=2)),
     (520, 640, 248, dict(kernel=2, bm=128, bn=64, splitk=1, wm=4, pf=2)),
     (64, 11008, 64, dict(kernel=2, bm=128, bn=64, splitk=2, wm=4, pf=2)),
+    (257, 1152, 96, dict(kernel=2, bm=128, bn=128, splitk=1, wm=4, wk=2, pf=1)),
+    (520, 640, 248, dict(kernel=2, bm=128, bn=128, splitk=1, wm=4, pf=2)),
+    (300, 4096, 136, dict(kernel=2, bm=128, bn=128, splitk=3, wm=4, wk=2, pf=1)),
 ]
 
 
