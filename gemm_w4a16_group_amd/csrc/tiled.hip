@@ -10,9 +10,9 @@
 // the chunks itself).  The chunks are exactly the B operand of
 // v_mfma_f32_32x32x16_f16, so the GEMM stages them into LDS with
 // buffer-to-LDS loads (no registers, no shuffles, contiguous LDS writes) and
-// reads them back conflict-free.  The tiles of the few-column calls (96 x
-// 64, 128 x 64, 128 x 128) read [K, N] activations in place instead when N
-// is a multiple of 8 (tiled_dx_kernel, tiled_k2_dx_kernel): each k-octet's
+// reads them back conflict-free.  The default tiles (96 x 64, 128 x 64,
+// 128 x 128, 256 x 128, 512 x 128) read [K, N] activations in place instead
+// when N is a multiple of 8 (tiled_dx_kernel, tiled_k2_dx_kernel): each k-octet's
 // eight rows are copied into LDS in the dequant order (16-byte pieces
 // permuted per row against bank conflicts) and two transposing LDS reads
 // give a lane its B fragment, with no second launch.
@@ -670,16 +670,18 @@ tiled_k2_kernel(GemmArgs a, int splitk) {
 }
 
 // The same two kernels reading X [K, N] in place (no xpack_col launch),
-// built for the tiles of the few-column calls: 96 x 64 of three waves,
-// 128 x 64 and 128 x 128 of four, one stage of activations ahead.  Each B
-// fragment then takes two transposing LDS reads instead of one, which
-// costs less than the launch it saves once the rows' pieces are permuted
-// against bank conflicts (12288x4096 N = 64 / 256: 20.3 / 41.9 -> 17.6 /
-// 37.6 us; without the permutation the 128 x 128 tiles lost: N = 512
-// 65.6 -> 75.4 us).
+// built for the default tiles (waves along M only, one stage of
+// activations ahead): 96 x 64 of three waves, 128 x 64, 128 x 128 and
+// 256 x 128 of four, 512 x 128 of eight.  Each B fragment then takes two
+// transposing LDS reads instead of one, which costs less than the launch
+// and the 2 K N bytes of re-layout it saves once the rows' pieces are
+// permuted against bank conflicts (12288x4096 N = 64 / 256 / 4096: 20.3 /
+// 41.9 / 372.5 -> 17.6 / 37.6 / 364.8 us; without the permutation the
+// 128 x 128 tiles lost: N = 512 65.6 -> 75.4 us).
 __host__ __device__ constexpr bool tiled_dx_built(int BM, int BN, int WGM, int NWV, int WPF, int XPF) {
     return XPF == 1 && WPF <= 2 && WGM == NWV &&
-           ((BM == 96 && NWV == 3 && BN == 64) || (BM == 128 && NWV == 4 && (BN == 64 || BN == 128)));
+           ((BM == 96 && NWV == 3 && BN == 64) || (BM == 128 && NWV == 4 && (BN == 64 || BN == 128)) ||
+            (BM == 256 && NWV == 4 && BN == 128) || (BM == 512 && NWV == 8 && BN == 128));
 }
 
 template <int BM, int BN, int WGM, int NWV, int WPF, int XPF>
@@ -831,7 +833,8 @@ hipError_t launch_xpack(const GemmArgs& a, hipStream_t stream) {
 bool tiled_direct_x(const GemmArgs& a, const TiledShape& t) {
     if (a.tm || a.xp_ready || a.act || a.N % 8 != 0 || a.N > 65536) return false;
     if (t.xpf != 1 || t.wpf > 2) return false;
-    return (t.bn == 64 && t.bm == 96 && t.wm == 3) || (t.bm == 128 && (t.bn == 64 || t.bn == 128) && t.wm == 4);
+    return (t.bn == 64 && t.bm == 96 && t.wm == 3) || (t.bm == 128 && (t.bn == 64 || t.bn == 128) && t.wm == 4) ||
+           (t.bm == 256 && t.bn == 128 && t.wm == 4) || (t.bm == 512 && t.bn == 128 && t.wm == 8);
 }
 
 hipError_t launch_tiled(const GemmArgs& a, const TiledShape& t, hipStream_t stream) {

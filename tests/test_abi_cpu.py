@@ -217,16 +217,15 @@ def test_kernel_name_follows_the_plan(lib):
     assert B.kernel_name(4096, 1, 11008) == "skinny_kernel<1, 8>"
     # 512-row tiles where they load the 256 CUs as evenly as 256-row tiles
     # (768 = 3 x 256 tiles at N = 4096, 192 at N = 1024), not at N = 2048
-    assert B.kernel_name(12288, 4096, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"
-    assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"
-    assert B.kernel_name(12288, 2048, 4096) == "tiled_kernel<256, 128, 4, 4, 1, 1>"
+    assert B.kernel_name(12288, 4096, 4096) == "tiled_dx_kernel<512, 128, 8, 8, 2, 1>"
+    assert B.kernel_name(12288, 1024, 4096) == "tiled_dx_kernel<512, 128, 8, 8, 2, 1>"
+    assert B.kernel_name(12288, 2048, 4096) == "tiled_dx_kernel<256, 128, 4, 4, 1, 1>"
     assert B.kernel_name(12288, 512, 4096) == "tiled_dx_kernel<128, 128, 4, 4, 1, 1>"
     # 96-row tiles of three waves where 128-row ones leave CUs idle; the
     # few-column tiles read [K, N] activations in place (the _dx kernels)
     # when N is a multiple of 8, else through xpack_col_kernel
     assert B.kernel_name(12288, 64, 4096) == "tiled_dx_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(12288, 60, 4096) == "tiled_kernel<96, 64, 3, 3, 2, 1>"
-    assert B.kernel_name(12288, 1024, 4096) == "tiled_kernel<512, 128, 8, 8, 2, 1>"   # 512-row tiles keep xpack
     assert B.kernel_name(11008, 128, 4096) == "tiled_dx_kernel<96, 64, 3, 3, 2, 1>"
     assert B.kernel_name(4096, 64, 11008) == "tiled_dx_kernel<128, 64, 4, 4, 2, 1>"
     # two K slices of 128 x 128 tiles from 160 tiles on (22016 rows, N = 128),

@@ -86,6 +86,8 @@ PLANS = [
     (257, 1152, 96, dict(kernel=2, bm=128, bn=128, splitk=1, wm=4, wk=2, pf=1)),
     (520, 640, 248, dict(kernel=2, bm=128, bn=128, splitk=1, wm=4, pf=2)),
     (300, 4096, 136, dict(kernel=2, bm=128, bn=128, splitk=3, wm=4, wk=2, pf=1)),
+    (513, 1152, 1024, dict(kernel=2, bm=512, bn=128, splitk=1, wm=8, pf=2)),
+    (300, 640, 392, dict(kernel=2, bm=256, bn=128, splitk=2, wm=4, pf=1)),
 ]
 
 
