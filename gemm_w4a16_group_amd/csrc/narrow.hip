@@ -73,6 +73,20 @@ struct QMinusZ {
     }
 };
 
+// Piece permutation of an in-place activation octet with 64 staged columns
+// (16-byte pieces, eight per 128-byte row): the piece index is XORed with
+// a mask of its row p and of the parity g of the 16-lane group that reads
+// it (octet index / 4), so that the eight 32-byte segments a half-wave's
+// transposing read takes (two groups x four rows, rows 128 bytes apart)
+// cover 256 distinct bytes of banks.  An involution: the copy and the read
+// apply the same XOR.  4096x4096 N = 64 / 40: 13.2 -> 11.8 us; the same
+// idea for 16 and 32 columns (the two groups' octets start on the same
+// banks) was 1-2 % slower or level, so those keep the plain layout.
+template <int NCOL>
+__host__ __device__ constexpr int dx_piece_xor(int p, int g) {
+    return NCOL == 64 ? 4 * ((p >> 1) & 1) + 2 * g : 0;
+}
+
 template <int NC, int PF, int kRB, int WK, int WM, bool DX>
 __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int splitk) {
     constexpr int NCOL = 16 * NC;            // staged columns (N padded to 16 NC)
@@ -121,13 +135,18 @@ __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int sp
         // range holds its eight k rows of NCOL halves in dequant order
         // (k offsets 0, 4, 1, 5, 2, 6, 3, 7), so that two transposing reads
         // of four rows each give a lane one column's eight k in the order
-        // the weight words unpack to.  Chunks past N re-read the row's last.
+        // the weight words unpack to.  With 64 columns the octet's 16-byte
+        // pieces are permuted (dx_piece_xor) so that the two 16-lane groups
+        // of a half-wave, which read octets four apart, and the four rows
+        // each reads fall on distinct banks.  Chunks past N re-read the
+        // row's last.
         const i32x4 xres = raw_rsrc(a.x + (int64_t)g0 * 128 * N, (int64_t)ng * 128 * N * 2);
         const int nins = ng * 16 * NCOL / 64;
         const int n8 = (int)(N >> 3);
         for (int j = wave; j < nins; j += NW) {
             const int c = 64 * j + lane;
-            const int o = c / NCOL, w = c % NCOL;
+            const int o = c / NCOL;
+            const int w = (c % NCOL) ^ dx_piece_xor<NCOL>((c % NCOL) / (NCOL / 8), (o >> 2) & 1);
             const int p = w / (NCOL / 8), cc = w % (NCOL / 8);
             const int r = (p >> 1) + 4 * (p & 1);
             const int ccl = cc < n8 ? cc : n8 - 1;
@@ -240,7 +259,12 @@ __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int sp
 
     // activation fragment of MFMA step t, block cb, local group s: chunk
     // (16 s + 4 kq + t, 16 cb + r16)
-    const unsigned char* xl = DX ? xs + (4 * kq) * NCOL * 16 + (r16 >> 2) * NCOL * 2 + (r16 & 3) * 8
+    // DX: lane (r16, kq) reads row (r16 >> 2) (+ 4) of octet 4 kq + t, 8 bytes
+    // at column 16 cb + 4 (r16 & 3), at the position the piece permutation
+    // gives: with 64 columns the 32-byte column segment cb moves to cb ^ xcb
+    const int dxg = kq & 1, dxj = r16 >> 2;
+    const int xcb = NCOL == 64 ? 2 * ((dxj >> 1) & 1) + dxg : 0;
+    const unsigned char* xl = DX ? xs + (4 * kq) * NCOL * 16 + dxj * NCOL * 2 + (r16 & 3) * 8
                                  : xs + ((4 * kq) * NCOL + r16) * 16;
 
     // Each stage's four MFMA steps start from zero and give the group's
@@ -280,7 +304,7 @@ __global__ void __launch_bounds__(64 * WM * WK) narrow_kernel(GemmArgs a, int sp
                     // lanes 4 j .. 4 j + 3 of a 16-lane group read row 4 h + j of
                     // the octet (columns 16 cb + 4 (lane % 4) ..); the transpose
                     // hands lane i column 16 cb + i of the four rows
-                    const unsigned char* b = xg + t * NCOL * 16 + cb * 32;
+                    const unsigned char* b = xg + t * NCOL * 16 + (cb ^ xcb) * 32;
                     const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) short4v*)(b));
                     const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
