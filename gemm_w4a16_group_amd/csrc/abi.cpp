@@ -363,9 +363,12 @@ size_t partial_bytes(const GemmArgs& a, const w4a16_plan& p) {
 size_t chunks_offset(const GemmArgs& a, const w4a16_plan& p) {
     return (kCounterBytes + partial_bytes(a, p) + 255) & ~(size_t)255;
 }
+// (no chunk area where the plan reads x in place)
 size_t workspace_bytes_for(const GemmArgs& a, const w4a16_plan& p) {
-    if (p.kernel == W4A16_KERNEL_TILED || p.kernel == W4A16_KERNEL_NARROW)
-        return chunks_offset(a, p) + xpack_bytes(a);
+    if (p.kernel == W4A16_KERNEL_TILED)
+        return chunks_offset(a, p) + (tiled_direct_x(a, tiled_of(p)) ? 0 : xpack_bytes(a));
+    if (p.kernel == W4A16_KERNEL_NARROW)
+        return chunks_offset(a, p) + (narrow_direct_x(a) ? 0 : xpack_bytes(a));
     if (p.splitk <= 1) return 0;
     return kCounterBytes + partial_bytes(a, p);
 }
@@ -464,7 +467,9 @@ int run_gemm(const uint32_t* qpk, const void* scales, const uint32_t* zpk, const
             return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps a data buffer");
         a.counters = static_cast<uint32_t*>(workspace);
         a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-        if (p.kernel == W4A16_KERNEL_TILED || p.kernel == W4A16_KERNEL_NARROW)
+        // the chunk area, where the plan has one (workspace_bytes_for)
+        if (need > chunks_offset(a, p) &&
+            (p.kernel == W4A16_KERNEL_TILED || p.kernel == W4A16_KERNEL_NARROW))
             a.xp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + chunks_offset(a, p));
     }
     a.qpk = qpk;

@@ -200,8 +200,9 @@ size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
  * workspace: device memory of at least w4a16_gemm_workspace_size() bytes,
  * 16-byte aligned, or NULL when that size is 0.  Its first 64 KB hold one
  * arrival counter per output tile (split plans allow at most 16384 tiles);
- * fp32 partial sums follow, then (tiled kernel) x rewritten as 16-byte
- * chunks of eight k of one column.  Before its first use the caller must fill at
+ * fp32 partial sums follow, then (tiled and narrow kernels, only where they
+ * do not read x in place: token-major x, or N not a multiple of 8) x
+ * rewritten as 16-byte chunks of eight k of one column.  Before its first use the caller must fill at
  * least the first 64 KB with zeros; every call leaves the counters at zero
  * again, so one zero-fill serves all later calls of any shape.  Calls that
  * share a workspace must not run concurrently (one workspace per stream).

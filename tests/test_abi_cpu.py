@@ -161,7 +161,8 @@ def test_default_plans_are_valid(lib):
             needs = p.kernel in (2, 3) or p.splitk > 1
             assert (ws == 0) == (not needs), (M, N, K, p.as_dict())
             if p.kernel in (2, 3):
-                assert ws >= 65536 + K * N * 2
+                # x is read in place for N a multiple of 8 (no chunk area)
+                assert ws >= 65536 + (K * N * 2 if N % 8 else 0)
             # a valid plan passes every check: with fake pointers the call
             # then fails only on the workspace (if any), never on the plan
             far = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]

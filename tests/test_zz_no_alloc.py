@@ -16,11 +16,13 @@ from gpu_util import GUARD, Problem, assert_parity, dev, guarded_out, guards_int
 pytestmark = pytest.mark.gpu
 
 # (M, K, N) pairs: the first call, then a smaller one (split-K narrow,
-# tiled with activation chunks, skinny with and without a workspace)
+# tiled reading x in place and through activation chunks (N not a multiple
+# of 8), skinny with and without a workspace)
 PAIRS = [
     ((12288, 4096, 32), (4096, 4096, 16)),
     ((12288, 4096, 64), (4096, 11008, 8)),
     ((12288, 4096, 128), (1000, 4096, 40)),
+    ((12288, 4096, 100), (4096, 4096, 60)),
     ((12288, 4096, 1), (200, 1152, 1)),
     ((22016, 4096, 4), (4096, 11008, 2)),
 ]
@@ -50,7 +52,9 @@ def test_noalloc_matches_gemm_twice(first, second):
 
 
 def test_noalloc_refuses_oversize():
-    M, K, N = 12288, 4096, 4096
+    # N not a multiple of 8: the tiled plan needs the 2 K N bytes of
+    # activation chunks, above the scratch
+    M, K, N = 12288, 4096, 4095
     need = B.workspace_size(M, N, K)
     cap = int(B.lib().w4a16_gemm_noalloc_max_bytes())
     assert cap == 16 << 20 and need > cap
