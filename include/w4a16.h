@@ -458,7 +458,8 @@ int w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
  * up and clears its counters with a kernel on `stream`.  No call allocates
  * or frees memory.  A shape whose default plan needs more scratch than that
  * (w4a16_gemm_workspace_size above the maximum, e.g. the tiled kernel's
- * K x N activation chunks beyond 16 MiB) fails with W4A16_ERR_WORKSPACE
+ * K x N activation chunks beyond 16 MiB, needed only when N is not a
+ * multiple of 8) fails with W4A16_ERR_WORKSPACE
  * and writes nothing.  All calls on one GPU share the array: calls that may
  * run at the same time on that GPU (unordered streams) race and must not be
  * issued.  Other arguments, requirements and errors as w4a16_gemm.
