@@ -702,16 +702,16 @@ hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const dim3 grid((unsigned)tiles, (unsigned)t.splitk);
     constexpr int lds = tiled_lds_bytes(BN, XPF, WKS);
-    const void* fn;
-    if constexpr (WKS == 1 && DX)
-        fn = reinterpret_cast<const void*>(&tiled_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
-    else if constexpr (WKS == 1)
-        fn = reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>);
-    else if constexpr (DX)
-        fn = reinterpret_cast<const void*>(&tiled_k2_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
-    else
-        fn = reinterpret_cast<const void*>(&tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>);
     if constexpr (lds > 65536) {
+        const void* fn;
+        if constexpr (WKS == 1 && DX)
+            fn = reinterpret_cast<const void*>(&tiled_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+        else if constexpr (WKS == 1)
+            fn = reinterpret_cast<const void*>(&tiled_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+        else if constexpr (DX)
+            fn = reinterpret_cast<const void*>(&tiled_k2_dx_kernel<BM, BN, WGM, NWV, WPF, XPF>);
+        else
+            fn = reinterpret_cast<const void*>(&tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>);
         // dynamic LDS above 64 KB must be allowed per kernel, once
         static const hipError_t ok = [fn] {
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -732,7 +732,6 @@ hipError_t launch_one(const GemmArgs& a, const TiledShape& t, hipStream_t stream
     else
         hipLaunchKernelGGL((tiled_k2_kernel<BM, BN, WGM, NWV, WPF, XPF>), grid, dim3(128 * NWV), lds, stream, a,
                            t.splitk);
-    (void)fn;
     return hipGetLastError();
 }
 
