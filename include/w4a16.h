@@ -172,12 +172,14 @@ int w4a16_plan_default(int64_t M, int64_t N, int64_t K, int32_t group_size,
                        w4a16_plan *plan);
 
 /* Name of the main kernel a plan (NULL: the default plan) launches for this
- * shape, as profilers print it without namespaces, e.g. "skinny_kernel<1, 4>",
- * "narrow_kernel<1, 8, 1, 1, true>" or "tiled_kernel<512, 128, 8, 8, 2>"
- * (tiled plans also launch xpack_col_kernel first, and so do narrow plans
- * whose name ends in "false": N not a multiple of 8; narrow plans ending in
- * "true" read x in place).  Writes at most len bytes including the
- * terminating 0 into buf.
+ * shape with x [K, N], as profilers print it without namespaces, e.g.
+ * "skinny_kernel<1, 4>", "narrow_kernel<1, 4, 1, 1, 4, true>" or
+ * "tiled_dx_kernel<512, 128, 8, 8, 2, 1>".  Kernels that read x in place
+ * (narrow plans ending in "true", tiled_dx_kernel and tiled_k2_dx_kernel:
+ * N a multiple of 8) are the call's only launch; the others (narrow plans
+ * ending in "false", tiled_kernel and tiled_k2_kernel) follow
+ * xpack_col_kernel, which rewrites x into 16-byte chunks.  Writes at most
+ * len bytes including the terminating 0 into buf.
  * Returns a status; launches nothing. */
 int w4a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size,
                       const w4a16_plan *plan, char *buf, size_t len);
