@@ -35,8 +35,8 @@
 // Prologues (token-major activations, N <= 8), each its own kernel name so
 // that the plain kernel's code is untouched: skinny_silu_kernel stages
 // silu(gate) * up of a gate/up output; skinny_norm_kernel stages
-// rmsnorm(x + res) * gamma, reducing the sums of squares over the workgroup
-// while the weights are in flight.
+// (x + res) * gamma and applies the RMS factor of each token to its sums in
+// the epilogue, where the workgroup's sums of squares have met.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -380,10 +380,18 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3b. normalizing prologue, while the weights are in flight: h =
-    // fp16(x + res) per block (written out by the first row tile), the
-    // squares of h summed per column over the wave's blocks, then over the
-    // waves along K in LDS (the workgroup covers all of K), and the staged
-    // activations become fp16(h * rsqrt(mean h^2 + eps) * gamma)
+    // fp16(x + res) per block (written out by the first row tile) and the
+    // squares of h summed per column over the wave's blocks.  The factor
+    // rsqrt(mean h^2 + eps) is one scalar per column, so it moves out of the
+    // sum: the wave stages fp16(h * gamma * 2^e) and the epilogue multiplies
+    // the column's sum by 2^-e (exact) and by the factor, once the sums of
+    // squares of the waves along K have met behind the epilogue's barrier.
+    // No wave waits for another before its main loop.  The power of two e
+    // (per wave and column) brings the staged values of the wave's blocks
+    // to unit mean square, so that their fp16 rounding is relative, as that
+    // of the normalized activations is.
+    float nscale[XStage<NT>::T8];   // 2^-e per column
+    float nssq[XStage<NT>::T8];     // the wave's sums of squares, every lane
     if constexpr (NORM) {
         constexpr int T8 = XStage<NT>::T8;
         float ssq[T8];
@@ -416,19 +424,19 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
             }
         }
         float* nsum = reinterpret_cast<float*>(smem + P.norm_off);
+        int ex[T8];
 #pragma unroll
         for (int t = 0; t < T8; ++t) {
 #pragma unroll
             for (int m = 32; m >= 1; m >>= 1) ssq[t] += __shfl_xor(ssq[t], m);
             if (lane == 0) nsum[wave * 8 + t] = ssq[t];
-        }
-        __syncthreads();
-        float rs[T8];
-#pragma unroll
-        for (int t = 0; t < T8; ++t) {
-            float tot = 0.f;
-            for (int k = 0; k < P.wk; ++k) tot += nsum[(k * P.wm + wave_m) * 8 + t];
-            rs[t] = 1.0f / sqrtf(tot / (float)a.K + a.eps);
+            nssq[t] = ssq[t];
+            // mean square of the wave's values in [2^(E-1), 2^E): e = -floor(E / 2)
+            const float ms = ssq[t] / (float)(ng > 0 ? ng * kGroup : 1);
+            int e = ms > 0.f ? -(__builtin_amdgcn_frexp_expf(ms) >> 1) : 0;
+            e = e < 60 ? (e > -60 ? e : -60) : 60;
+            ex[t] = e;
+            nscale[t] = __builtin_ldexpf(1.0f, -e);
         }
 #pragma unroll
         for (int j = 0; j < F; ++j) {
@@ -440,8 +448,9 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const half2v hh = as_h2(hw[i]), gg = as_h2(gw[i]);
-                    const _Float16 lo = (_Float16)((float)hh[0] * rs[t] * (float)gg[0]);
-                    const _Float16 hi = (_Float16)((float)hh[1] * rs[t] * (float)gg[1]);
+                    // h * gamma is exact in float32; the power of two too
+                    const _Float16 lo = (_Float16)__builtin_ldexpf((float)hh[0] * (float)gg[0], ex[t]);
+                    const _Float16 hi = (_Float16)__builtin_ldexpf((float)hh[1] * (float)gg[1], ex[t]);
                     yw[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
                 }
@@ -571,6 +580,17 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
 
     // ---- 6. sum the wk waves of a row block through LDS
     const int wm = P.wm, wk = P.wk, splitk = P.splitk;
+    if constexpr (NORM) {
+        // undo the wave's power of two (exact) before the waves meet
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) {
+                int t = tb * 16 + kb * 4 + r;
+                t = t < NT ? t : NT - 1;
+                acc[tb][r] *= nscale[t < XStage<NT>::T8 ? t : 0];
+            }
+    }
     if (wk > 1) {
         __syncthreads();   // every wave is done with its staged data
         float* red = reinterpret_cast<float*>(smem);
@@ -600,6 +620,31 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, const SkinnyParam
     // ---- 7. epilogue: lane holds columns 16 tb + 4 kb + r of row row0 + li
     const int N = NT;
     const int64_t row = row0 + li;
+    if constexpr (NORM) {
+        // the normalization factor of each column, from the sums of squares
+        // of the waves along K in K order (after the barriers above; a wave
+        // alone along K has its own)
+        constexpr int T8 = XStage<NT>::T8;
+        const float* nsum = reinterpret_cast<const float*>(smem + P.norm_off);
+        float rs[T8];
+#pragma unroll
+        for (int t = 0; t < T8; ++t) {
+            float tot = nssq[t];
+            if (wk > 1) {
+                tot = 0.f;
+                for (int k = 0; k < wk; ++k) tot += nsum[(k * wm + wave_m) * 8 + t];
+            }
+            rs[t] = 1.0f / sqrtf(tot / (float)a.K + a.eps);
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) {
+                int t = tb * 16 + kb * 4 + r;
+                t = t < NT ? t : NT - 1;
+                acc[tb][r] *= rs[t < T8 ? t : 0];
+            }
+    }
     if (wave_k == 0 && row < M) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {

@@ -313,13 +313,16 @@ int w4a16_add_rmsnorm(const void *x, const void *residual, const void *gamma,
  *   h = fp16(x + residual);  c[n, m] = sum_k Wdeq[m, k] * y[n, k]
  * with y as in w4a16_add_rmsnorm and c fp16 [N, M].  y never reaches the
  * caller: with a skinny plan (N <= 8) of one split along K and h not the
- * residual itself, the skinny kernel normalizes while it stages its
- * activations (one launch; the sums of squares are reduced over the
- * workgroup while the weights are in flight); otherwise y is written into
- * the workspace, in the activation layout the plan's kernel reads (the
- * tiled and narrow kernels then skip their own rewrite of the
- * activations), and the call makes two launches.  The two forms may differ
- * in the last bit of y (summation order).  plan: NULL for the token-major
+ * residual itself, the skinny kernel stages fp16(h * gamma * 2^e) (e a
+ * power of two per wave and token that brings the staged values to unit
+ * mean square) and multiplies each token's sums by 2^-e and by the RMS
+ * factor rsqrt(mean h^2 + eps) in its epilogue, after the workgroup's sums
+ * of squares have met (one launch, no wait before the main loop);
+ * otherwise y is written into the workspace, in the activation layout the
+ * plan's kernel reads (the tiled and narrow kernels then skip their own
+ * rewrite of the activations), and the call makes two launches.  The two
+ * forms differ by one fp16 rounding of the activations (fp16(h gamma 2^e)
+ * against fp16(y)), within the product's tolerance.  plan: NULL for the token-major
  * default plan
  * (w4a16_plan_default_ex with W4A16_LAYOUT_TOKEN).  workspace: at least
  * w4a16_gemm_add_rmsnorm_workspace_size() bytes, with the rules of

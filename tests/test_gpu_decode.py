@@ -94,13 +94,16 @@ def test_decode_layer_matches_its_steps_bitwise():
     xa, ra = dev(x), dev(r)
     ws = torch.zeros(B.decode_layer_workspace_size(Bn, H, D, I, S, S), dtype=torch.uint8, device="cuda")
     B.decode_layer(la, pos, ra, xa, ws)
-    # the same steps one by one through the public calls
+    # the same steps one by one through the public calls, with the stream
+    # routed as the entry point routes it (residual -> second buffer ->
+    # residual, so that no normalizing call writes the buffer it reads)
     lb = clone_layer(layer)
     xb, rb = dev(x), dev(r)
-    qkv, _ = B.gemm_add_rmsnorm(*lb["qkv"], xb, rb, lb["attn_norm"], 1e-6, h=rb)
+    hb = torch.empty_like(rb)
+    qkv, _ = B.gemm_add_rmsnorm(*lb["qkv"], xb, rb, lb["attn_norm"], 1e-6, h=hb)
     att = B.decode_attention(qkv, lb["k_cache"], lb["v_cache"], pos)
     B.gemm(*lb["o"], att, out=xb, layout=B.LAYOUT_TOKEN)
-    gu, _ = B.gemm_add_rmsnorm(*lb["gate_up"], xb, rb, lb["mlp_norm"], 1e-6, h=rb)
+    gu, _ = B.gemm_add_rmsnorm(*lb["gate_up"], xb, hb, lb["mlp_norm"], 1e-6, h=rb)
     act = B.silu_mul(gu)
     B.gemm(*lb["down"], act, out=xb, layout=B.LAYOUT_TOKEN)
     torch.cuda.synchronize()
