@@ -130,6 +130,36 @@ def test_gemm_add_rmsnorm_in_place():
         assert_parity(C, C_ref, A_ref, "in place N=%d" % N)
 
 
+@pytest.mark.parametrize("case", [(-20, 1, 1, 8), (-12, 1, 2, 8), (-12, 4, 2, 8), (10, 1, 1, 8), (10, 3, 2, 4),
+                                  (0, 2, 1, 16)],
+                         ids=lambda c: "scale2^%d_N%d_wm%d_wk%d" % c)
+def test_gemm_add_rmsnorm_scaled_stream(case):
+    """The one-launch prologue stages fp16(h gamma 2^e), e a power of two per
+    wave and token: a residual stream of small (2^-12) or large (2^10)
+    magnitude (2^-20: fp16 subnormal inputs) still meets the GEMM rule on
+    the oracle's normalized rows.
+    eps = 0, where the normalization is scale-invariant; the skinny plan of
+    one split (the one-launch form) forced, with waves along M and K."""
+    ex, N, wm, wk = case
+    M, K = 300, 4096
+    log("gemm_add_rmsnorm scaled %s" % (case,))
+    p = prob(M, K)
+    x, r, g = inputs.hidden_states(N, K, wid=550 + N)
+    x = (x.astype(np.float64) * 2.0 ** ex).astype(np.float16)
+    r = (r.astype(np.float64) * 2.0 ** ex).astype(np.float16)
+    h16, y_ref = norm_ref(x, r, g, 0.0)
+    plan = B.Plan.make(kernel=1, ncol=N, rb=1, wm=wm, wk=wk, splitk=1)
+    cb, c = guarded_out(N, M)
+    hb, h = guarded_out(N, K)
+    B.gemm_add_rmsnorm(p.qpk, p.s_d, p.zpk, dev(x), dev(r), dev(g), 0.0, h=h, out=c, plan=plan)
+    torch.cuda.synchronize()
+    assert guards_intact(cb, N, M) and guards_intact(hb, N, K), "write outside an output"
+    assert np.array_equal(h.cpu().numpy().view(np.uint16), h16.view(np.uint16)), "h differs"
+    C = np.ascontiguousarray(c.cpu().numpy().T)
+    C_ref, A_ref = ora.reference(p.qpk_ref, p.s, p.zpk_ref, y_ref.T)
+    assert_parity(C, C_ref, A_ref, str(case))
+
+
 @pytest.mark.parametrize("shape", [(12288, 4096, 1), (12288, 4096, 16), (22016, 4096, 1), (22016, 4096, 128)],
                          ids=lambda s: "M%d_K%d_N%d" % s)
 def test_gemm_add_rmsnorm_full_size(shape):
